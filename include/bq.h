@@ -1,0 +1,169 @@
+/*
+ * bq.h -- C ABI of libbq: 1-bit (Q1_0) and ternary (Q2_0) quantized
+ * matrix-vector products on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (bankML "gpu/ -- the video-card component", section
+ * "kernels.rs -- the Q1_0 kernels"): a weight matrix stored as blocks of
+ * packed sign bits or ternary codes with one f16 scale per block, times an
+ * activation vector quantized to int8 with one f32 scale per block of qa
+ * values, gives one f32 dot product per output row.  Every output element is
+ * produced in one fixed order:
+ *
+ *   for each weight block b (Q1_0: 128 weights = 4 sub-blocks of 32;
+ *                            Q2_0:  64 weights = 2 sub-blocks of 32):
+ *     for each lane L in 0..7 and sub-block j:
+ *       s   = exact int32 sum over weights 32j+4L .. 32j+4L+3 of w * q
+ *             (Q1_0: w = +1 / -1, and -1 times -128 gives -128 as in an int8
+ *              negation; Q2_0: w = code - 1)
+ *       ab  = d1(j) * s        (first sub-block)
+ *       ab  = fma(d1(j), s, ab) (later sub-blocks)
+ *     acc[L] = fma(d0(b), ab, acc[L])        (acc starts at +0)
+ *   y = ((acc0+acc4) + (acc2+acc6)) + ((acc1+acc5) + (acc3+acc7))
+ *
+ * with d0 the block's f16 scale widened exactly and d1(j) the activation
+ * scale that covers the first value of sub-block j; every step is one
+ * binary32 operation rounded to nearest-even (no flush of subnormals).  The
+ * results do not depend on the grid, on how rows are split, or on which call
+ * (matvec or sweep) computes them.
+ *
+ * Conventions for every entry point:
+ *   - Return BQ_OK (0) on success or a BQ_E* code; the text of the last
+ *     error of the calling thread, naming the call and the argument, is
+ *     returned by bq_last_error().  No exception crosses this boundary, no
+ *     call aborts, and there is no CPU fallback: a call that cannot run on
+ *     the GPU fails.
+ *   - Arguments are validated before anything is launched.  A GPU fault
+ *     inside a kernel is reported by the caller's next synchronisation of
+ *     the stream, not by the launching call.
+ *   - "device" pointers are HIP device allocations (for example the
+ *     data_ptr() of a torch tensor on a ROCm device); "host" pointers are
+ *     ordinary process memory.  The caller allocates and owns every buffer;
+ *     the library keeps no pointer after a call returns, except that a sweep
+ *     plan keeps the pointers it was created with until it is destroyed.
+ *   - GPU work is enqueued on the given stream (a hipStream_t, NULL = the
+ *     null stream) and runs asynchronously; calls are reentrant and are
+ *     ordered only by their streams.
+ */
+#ifndef BQ_H
+#define BQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQ_ABI_VERSION 1
+
+/* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
+ * then 16 payload bytes).
+ *   BQ_Q1_0: 128 weights; weight k is bit (k & 7) of payload byte (k >> 3);
+ *            bit 1 means +1, bit 0 means -1.
+ *   BQ_Q2_0: 64 weights; weight k is bits 2(k&3)..2(k&3)+1 of payload byte
+ *            (k >> 2); code c means weight c - 1 (codes 0, 1, 2 are -1, 0, +1;
+ *            code 3 decodes as +2 on both the CPU and the GPU). */
+#define BQ_Q1_0 1
+#define BQ_Q2_0 2
+
+/* Return codes. */
+#define BQ_OK 0
+#define BQ_EARG 1   /* null pointer, bad shape, unsupported qa / ncols / format */
+#define BQ_EALIGN 2 /* a pointer or a leading dimension is not aligned as required */
+#define BQ_EHIP 3   /* the HIP runtime reported an error (its text is kept) */
+#define BQ_ENOMEM 4 /* a plan could not allocate its device table */
+
+typedef void *bq_stream; /* hipStream_t */
+
+/* A packed weight matrix as laid out by bq_pack (device pointers). */
+typedef struct bq_weights {
+    int32_t fmt;            /* BQ_Q1_0 or BQ_Q2_0 */
+    int32_t reserved;       /* must be 0 */
+    int64_t rows;           /* M >= 1 */
+    int64_t cols;           /* K >= 1, a multiple of the block length (128 or 64) */
+    const void *bits;       /* device, 16-byte aligned: payload plane from bq_pack */
+    const uint16_t *scales; /* device, 16-byte aligned: scale plane from bq_pack */
+} bq_weights;
+
+/* ncols quantized activation vectors (device pointers), as written by
+ * bq_quantize_act_q8: column c is q[c*ld_q .. c*ld_q + n) with scales
+ * d[c*ld_d .. c*ld_d + n/qa). */
+typedef struct bq_act {
+    const int8_t *q; /* device, 16-byte aligned */
+    const float *d;  /* device, 4-byte aligned */
+    int64_t n;       /* values per column; must equal the weights' cols */
+    int32_t qa;      /* values per scale: 32, 64 or 128 (n % qa == 0) */
+    int32_t ncols;   /* number of activation columns, 1..16 */
+    int64_t ld_q;    /* int8 elements between columns, >= n, multiple of 16 */
+    int64_t ld_d;    /* floats between columns, >= n / qa */
+} bq_act;
+
+/* One product of a sweep: y = W x for one activation vector. */
+typedef struct bq_gemv {
+    bq_weights w;
+    bq_act a; /* a.ncols must be 1 */
+    float *y; /* device, 4-byte aligned: w.rows floats */
+} bq_gemv;
+
+typedef struct bq_sweep bq_sweep; /* opaque plan */
+
+/* BQ_ABI_VERSION of the loaded library. */
+int bq_abi_version(void);
+
+/* Text of the calling thread's last error ("" if none).  Valid until the
+ * thread's next failing call. */
+const char *bq_last_error(void);
+
+/* Sizes in bytes of the two device planes that hold a packed rows x cols
+ * matrix of format fmt.  Host only; touches no GPU. */
+int bq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols, size_t *bits_bytes, size_t *scale_bytes);
+
+/* Repack canonical blocks into the device layout (bankML "gpu/", section
+ * "kernels.rs": weights are repacked once, numbers unchanged, only
+ * re-ordered).  Host only: canon (host) holds rows x (cols / block length)
+ * canonical 18-byte blocks, row-major; bits_out and scales_out (host) must
+ * hold the sizes bq_packed_bytes reports.  The caller copies both planes to
+ * the device once.  Padding is written as zeros. */
+int bq_pack(int32_t fmt, const uint8_t *canon, int64_t rows, int64_t cols, void *bits_out,
+            uint16_t *scales_out);
+
+/* Inverse of bq_pack (host only): recovers the canonical blocks. */
+int bq_unpack(int32_t fmt, const void *bits, const uint16_t *scales, int64_t rows, int64_t cols,
+              uint8_t *canon_out);
+
+/* Quantize n floats x (device, 16-byte aligned) in blocks of qa values:
+ * d = amax / 127 (f32, correctly rounded), q = x / d (correctly rounded)
+ * rounded half away from zero into [-127, 127]; an all-zero block gives
+ * d = 0 and q = 0.  q (device, 4-byte aligned) receives n int8 values and d
+ * (device, 4-byte aligned) n / qa floats.  qa is 32, 64 or 128; n % qa == 0.
+ * Non-finite inputs are outside the contract.  Asynchronous on s. */
+int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s);
+
+/* y (device, 4-byte aligned, a.ncols * w->rows floats; column c at
+ * y + c * rows) = W times each activation column, in the order given at the
+ * top of this file.  w->fmt must be BQ_Q1_0 (resp. BQ_Q2_0 for the second
+ * call); a->n must equal w->cols.  Allocates nothing.  Asynchronous on s. */
+int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
+int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
+
+/* A plan for many independent products run by ONE kernel launch (the 253
+ * products of one decode token: bankML "par.rs -- the persistent thread pool
+ * and row scheduler", section "Summary").  All entries must share one format
+ * and one qa, with ncols == 1.  Validates every entry, balances the work
+ * over the GPU and copies a descriptor table to the device (the plan's only
+ * allocation, freed by bq_sweep_destroy).  Must be called with the device of
+ * the pointers current.  *plan receives the plan, or NULL on failure. */
+int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan);
+
+/* Enqueue the whole plan on s as one kernel launch.  Each entry's y equals
+ * what bq_q1_0_matvec / bq_q2_0_matvec would write for it. */
+int bq_token_sweep(const bq_sweep *plan, bq_stream s);
+
+/* Release a plan (NULL is allowed).  Synchronises the device first. */
+void bq_sweep_destroy(bq_sweep *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQ_H */

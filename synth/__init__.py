@@ -83,19 +83,30 @@ def pack_codes(codes: np.ndarray) -> np.ndarray:
     return (c[:, 0] | (c[:, 1] << 2) | (c[:, 2] << 4) | (c[:, 3] << 6)).astype(np.uint8)
 
 
-def q2_0_blocks(rows: int, cols: int, seed: int, *stream: int, sigma: float = 0.02,
-                max_code: int = 2) -> np.ndarray:
-    """Canonical Q2_0 weights: uint8 [rows, cols/64, 18]; codes uniform over 0..max_code."""
+def _code_bytes() -> np.ndarray:
+    """The 81 payload bytes whose four 2-bit codes all lie in {0, 1, 2}."""
+    c = np.array([(i % 3, i // 3 % 3, i // 9 % 3, i // 27) for i in range(81)], dtype=np.uint8)
+    return pack_codes(c.ravel())
+
+
+def q2_0_blocks(rows: int, cols: int, seed: int, *stream: int, sigma: float = 0.02) -> np.ndarray:
+    """Canonical Q2_0 weights: uint8 [rows, cols/64, 18].  Each payload byte's
+    four codes are drawn together: a uniform 16-bit draw u picks combination
+    (81 * u) >> 16 of the 81, so each code is 0, 1 or 2 with probability 1/3
+    (to within 81/65536 relative)."""
     if cols % 64:
         raise ValueError("Q2_0 needs cols % 64 == 0")
     nb = cols // 64
     g = rng(seed, 2, *stream)
     sc = scales_f16(g, rows * nb, sigma)
-    payload = np.empty(rows * nb * 16, dtype=np.uint8)
-    step = 1 << 22  # codes drawn in slices to bound host memory
-    for s in range(0, rows * nb * 16, step):
-        e = min(s + step, rows * nb * 16)
-        payload[s:e] = pack_codes(g.integers(0, max_code + 1, size=(e - s) * 4, dtype=np.uint8))
+    table = _code_bytes()
+    total = rows * nb * 16
+    payload = np.empty(total, dtype=np.uint8)
+    step = 1 << 24  # drawn in slices to bound host memory
+    for s in range(0, total, step):
+        e = min(s + step, total)
+        u = g.integers(0, 65536, size=e - s, dtype=np.uint32)
+        payload[s:e] = table[(u * 81) >> 16]
     return _assemble(sc, payload, rows, nb)
 
 

@@ -1,0 +1,233 @@
+"""Python binding of libbq (include/bq.h): 1-bit (Q1_0) and ternary (Q2_0)
+quantized matrix-vector products on MI355X.
+
+The functions keep the C names and only marshal arguments: torch tensors on a
+ROCm device become device pointers, numpy arrays become host pointers, and a
+nonzero return code becomes a ``BQError`` carrying ``bq_last_error()``.  Every
+step of the computation runs in the HIP kernels of ``libbq.so``; importing
+this package fails if the library has not been built
+(``python -m ternary_quantized_gemv_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbq.so")
+
+BQ_Q1_0 = 1
+BQ_Q2_0 = 2
+BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
+BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
+BLOCK_BYTES = 18
+
+EXPORTS = (
+    "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
+    "bq_quantize_act_q8", "bq_q1_0_matvec", "bq_q2_0_matvec",
+    "bq_sweep_create", "bq_token_sweep", "bq_sweep_destroy",
+)
+
+
+class BQError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[bq error {code}] {msg}")
+        self.code = code
+
+
+class bq_weights(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("bits", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class bq_act(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("qa", ctypes.c_int32), ("ncols", ctypes.c_int32), ("ld_q", ctypes.c_int64),
+                ("ld_d", ctypes.c_int64)]
+
+
+class bq_gemv(ctypes.Structure):
+    _fields_ = [("w", bq_weights), ("a", bq_act), ("y", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ternary_quantized_gemv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.bq_abi_version.restype = ctypes.c_int
+    lib.bq_abi_version.argtypes = []
+    lib.bq_last_error.restype = ctypes.c_char_p
+    lib.bq_last_error.argtypes = []
+    lib.bq_packed_bytes.restype = ctypes.c_int
+    lib.bq_packed_bytes.argtypes = [i32, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.bq_pack.restype = ctypes.c_int
+    lib.bq_pack.argtypes = [i32, vp, i64, i64, vp, vp]
+    lib.bq_unpack.restype = ctypes.c_int
+    lib.bq_unpack.argtypes = [i32, vp, vp, i64, i64, vp]
+    lib.bq_quantize_act_q8.restype = ctypes.c_int
+    lib.bq_quantize_act_q8.argtypes = [vp, i64, i32, vp, vp, vp]
+    for f in (lib.bq_q1_0_matvec, lib.bq_q2_0_matvec):
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(bq_weights), ctypes.POINTER(bq_act), vp, vp]
+    lib.bq_sweep_create.restype = ctypes.c_int
+    lib.bq_sweep_create.argtypes = [ctypes.POINTER(bq_gemv), i32, ctypes.POINTER(vp)]
+    lib.bq_token_sweep.restype = ctypes.c_int
+    lib.bq_token_sweep.argtypes = [vp, vp]
+    lib.bq_sweep_destroy.restype = None
+    lib.bq_sweep_destroy.argtypes = [vp]
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int):
+    if rc != BQ_OK:
+        raise BQError(rc, lib.bq_last_error().decode())
+
+
+def _dev(t, what: str) -> int:
+    """Device pointer of a torch tensor on a GPU (refuses host tensors)."""
+    if t is None:
+        return 0
+    if not getattr(t, "is_cuda", False):
+        raise BQError(BQ_EARG, f"{what} must be a tensor on a ROCm device")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ----------------------------------------------------------------- host calls
+def bq_abi_version() -> int:
+    return lib.bq_abi_version()
+
+
+def bq_last_error() -> str:
+    return lib.bq_last_error().decode()
+
+
+def bq_packed_bytes(fmt: int, rows: int, cols: int) -> tuple[int, int]:
+    b, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.bq_packed_bytes(fmt, rows, cols, ctypes.byref(b), ctypes.byref(s)))
+    return b.value, s.value
+
+
+def bq_pack(fmt: int, canon: np.ndarray, rows: int, cols: int) -> tuple[np.ndarray, np.ndarray]:
+    """Canonical blocks (uint8, rows x cols/QK x 18) -> (payload plane uint8, scale plane uint16)."""
+    canon = np.ascontiguousarray(canon, dtype=np.uint8)
+    if canon.size != rows * (cols // BLOCK_LEN.get(fmt, 1)) * BLOCK_BYTES:
+        raise BQError(BQ_EARG, "bq_pack: canonical array has the wrong size")
+    nb, ns = bq_packed_bytes(fmt, rows, cols)
+    bits = np.empty(nb, dtype=np.uint8)
+    scales = np.empty(ns // 2, dtype=np.uint16)
+    _check(lib.bq_pack(fmt, canon.ctypes.data, rows, cols, bits.ctypes.data, scales.ctypes.data))
+    return bits, scales
+
+
+def bq_unpack(fmt: int, bits: np.ndarray, scales: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    nb, ns = bq_packed_bytes(fmt, rows, cols)
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if bits.nbytes != nb or scales.nbytes != ns:
+        raise BQError(BQ_EARG, "bq_unpack: plane sizes do not match")
+    out = np.empty((rows, cols // BLOCK_LEN[fmt], BLOCK_BYTES), dtype=np.uint8)
+    _check(lib.bq_unpack(fmt, bits.ctypes.data, scales.ctypes.data, rows, cols, out.ctypes.data))
+    return out
+
+
+# ------------------------------------------------------------------ GPU calls
+def bq_quantize_act_q8(x, qa: int, q, d, stream=None) -> None:
+    """x: float32 device tensor (n); q: int8 device tensor (n); d: float32 device tensor (n/qa)."""
+    n = x.numel()
+    _check(lib.bq_quantize_act_q8(_dev(x, "x"), n, qa, _dev(q, "q"), _dev(d, "d"), _stream(stream)))
+
+
+class Weights:
+    """A packed matrix resident on the GPU (the two planes of bq_pack)."""
+
+    def __init__(self, fmt: int, rows: int, cols: int, bits, scales):
+        self.fmt, self.rows, self.cols = fmt, rows, cols
+        self.bits, self.scales = bits, scales
+
+    @classmethod
+    def upload(cls, fmt: int, canon: np.ndarray, rows: int, cols: int, device="cuda"):
+        import torch
+        bits, scales = bq_pack(fmt, canon, rows, cols)
+        return cls(fmt, rows, cols, torch.from_numpy(bits).to(device),
+                   torch.from_numpy(scales.view(np.int16)).to(device))
+
+    def c(self) -> bq_weights:
+        return bq_weights(self.fmt, 0, self.rows, self.cols, _dev(self.bits, "weights.bits"),
+                          _dev(self.scales, "weights.scales"))
+
+
+class Act:
+    """ncols quantized activation columns on the GPU: q int8 [ncols, ld_q], d f32 [ncols, ld_d]."""
+
+    def __init__(self, q, d, n: int, qa: int, ncols: int = 1):
+        self.q, self.d, self.n, self.qa, self.ncols = q, d, n, qa, ncols
+
+    def c(self) -> bq_act:
+        ld_q = self.q.stride(0) if self.q.dim() == 2 else self.n
+        ld_d = self.d.stride(0) if self.d.dim() == 2 else self.n // self.qa
+        return bq_act(_dev(self.q, "act.q"), _dev(self.d, "act.d"), self.n, self.qa, self.ncols, ld_q, ld_d)
+
+
+def _matvec(fn, w: Weights, a: Act, y, stream):
+    wc, ac = w.c(), a.c()
+    _check(fn(ctypes.byref(wc), ctypes.byref(ac), _dev(y, "y"), _stream(stream)))
+
+
+def bq_q1_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
+    _matvec(lib.bq_q1_0_matvec, w, a, y, stream)
+
+
+def bq_q2_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
+    _matvec(lib.bq_q2_0_matvec, w, a, y, stream)
+
+
+class Sweep:
+    """A bq_sweep plan; keeps the tensors it points at alive until destroyed."""
+
+    def __init__(self, handle: int, keep):
+        self.handle = handle
+        self._keep = keep
+
+    def destroy(self):
+        if self.handle:
+            lib.bq_sweep_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def bq_sweep_create(entries) -> Sweep:
+    """entries: [(Weights, Act, y tensor)]."""
+    arr = (bq_gemv * len(entries))()
+    for i, (w, a, y) in enumerate(entries):
+        arr[i].w = w.c()
+        arr[i].a = a.c()
+        arr[i].y = _dev(y, "y")
+    h = ctypes.c_void_p()
+    _check(lib.bq_sweep_create(arr, len(entries), ctypes.byref(h)))
+    return Sweep(h.value, list(entries))
+
+
+def bq_token_sweep(plan: Sweep, stream=None) -> None:
+    _check(lib.bq_token_sweep(plan.handle, _stream(stream)))
+
+
+def bq_sweep_destroy(plan: Sweep) -> None:
+    plan.destroy()

@@ -1,0 +1,634 @@
+// bq_kernels.hip -- gfx950 kernels of libbq and the GPU entry points of the
+// C ABI (include/bq.h).
+//
+// The product computed for every output row is the dot-product order of
+// bankML's GPU page ("gpu/ -- the video-card component", section "kernels.rs
+// -- the Q1_0 kernels"): per block, eight lanes of exact integer sums over
+// four consecutive weights of each 32-weight sub-block; ab = d1*s on the
+// first sub-block, ab = fma(d1, s, ab) on the others; acc = fma(d0, ab, acc);
+// then the tree ((a0+a4)+(a2+a6)) + ((a1+a5)+(a3+a7)).  Everything is built
+// with -ffp-contract=off and every fused step is an explicit fma, so the
+// compiler neither fuses nor splits what that order prescribes.
+//
+// How the work maps onto CDNA4
+// ----------------------------
+// * One wavefront owns 64 rows (lane i = row 64t+i) and carries all eight
+//   lane accumulators of its row in registers.  Rows never split across
+//   threads, so the result does not depend on the grid.
+// * The weights stream from HBM once: per block each lane issues one 16-byte
+//   load of its row's payload, and the layout (bq_layout.h) makes the 64
+//   loads of a wavefront one contiguous KiB.  Loads run kPrefetch blocks
+//   ahead of the arithmetic.
+// * The activation never meets the weights as bytes.  For each group of
+//   weights that shares one 4-bit nibble of packed weights (Q1_0: 4 signs;
+//   Q2_0: 2 codes) the workgroup first tabulates, in LDS, the partial sum for
+//   all 16 nibble values (exact small integers held as floats; for Q1_0's
+//   first sub-block the table already holds the rounded product d1*s, which
+//   is the same single rounding the order prescribes).  The inner loop is
+//   then: byte-select the nibble (SDWA), one LDS read, one fma.  All 64
+//   lanes of a wavefront read the same 16-entry table, so reads never
+//   conflict on LDS banks.
+// * A table covers a chunk of 32 blocks (64 KiB); longer rows walk several
+//   chunks, rebuilding the table between barriers while the accumulators
+//   stay in registers.
+// * The sweep runs all products of a decode token in one launch: one
+//   workgroup per work item (up to 8 tiles of one matrix), ordered from the
+//   most to the least work so the hardware's in-order dispatch balances the
+//   GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/bq.h"
+#include "bq_layout.h"
+
+namespace bq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunkBlocks = 32;                                     // blocks per LDS table
+constexpr int kSlotsPerBlock = 32;                                   // nibbles per block
+constexpr int kSlotFloats = 16;                                      // entries per nibble table
+constexpr int kTableFloats = kChunkBlocks * kSlotsPerBlock * kSlotFloats;  // 64 KiB
+constexpr int kScaleFloats = kChunkBlocks * 4;                       // d1 per sub-block
+constexpr int kWaves = 8;                                            // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kPrefetch = 4;                                         // blocks loaded ahead
+
+struct GemvDesc {
+    const u32x4 *bits;    // payload plane
+    const u32x4 *scales;  // scale plane: 8 f16 per lane per 16 bytes
+    const int8_t *q;      // activation quants of this product
+    const float *d;       // activation scales
+    float *y;             // output
+    int32_t rows;
+    int32_t nb;  // blocks per row
+    int32_t ng;  // scale groups (of 8 blocks) per row
+    int32_t pad;
+};
+
+struct WorkItem {
+    int32_t gemv;
+    int32_t tile0;
+    int32_t ntiles;
+    int32_t pad;
+};
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// --------------------------------------------------------------- tables
+// Q1_0: slot t of a chunk covers chunk values 4t..4t+3 (block t/32, sub-block
+// (t/8)%4, lane t%8).  Entry n: s = sum_i (bit i of n ? q_i : -q_i), where the
+// negation of -128 stays -128; on sub-block 0 the entry is d1*s instead.
+template <int QA>
+__device__ void build_table_q1(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
+{
+    const int nslots = nbc * kSlotsPerBlock;
+    for (int t = threadIdx.x; t < nslots; t += blockDim.x) {
+        const uint32_t w4 = *reinterpret_cast<const uint32_t *>(q + k0 + 4 * t);
+        int p1[4], p0[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int v = (int8_t)(w4 >> (8 * i));
+            p1[i] = v;
+            p0[i] = v == -128 ? -128 : -v;
+        }
+        int lo[4], hi[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            lo[x] = ((x & 1) ? p1[0] : p0[0]) + ((x & 2) ? p1[1] : p0[1]);
+            hi[x] = ((x & 1) ? p1[2] : p0[2]) + ((x & 2) ? p1[3] : p0[3]);
+        }
+        const bool first = ((t >> 3) & 3) == 0;
+        const float d1 = d[(k0 + 4 * t) / QA];
+        f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float s = (float)(lo[e] + hi[h]);
+                v[e] = first ? d1 * s : s;
+            }
+            dst[h] = v;
+        }
+    }
+    for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x)
+        D1[i] = d[(k0 + 32 * i) / QA];
+}
+
+// Q2_0: slot t of a chunk covers chunk values 2t and 2t+1 (the low or high
+// nibble of payload byte t/2 of its block).  Entry n = (a, b) codes:
+// (a-1)*q_2t + (b-1)*q_2t+1.
+template <int QA>
+__device__ void build_table_q2(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
+{
+    const int nslots = nbc * kSlotsPerBlock;
+    for (int t = threadIdx.x; t < nslots; t += blockDim.x) {
+        const uint32_t w2 = *reinterpret_cast<const uint16_t *>(q + k0 + 2 * t);
+        const int qa0 = (int8_t)(w2 & 0xFF), qa1 = (int8_t)(w2 >> 8);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
+            dst[h] = v;
+        }
+    }
+    // d1 per (block, sub-block): D1[4b + j], j = 0, 1.
+    for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x) {
+        const int b = i >> 2, j = i & 3;
+        D1[i] = j < 2 ? d[(k0 + 64 * b + 32 * j) / QA] : 0.0f;
+    }
+}
+
+// LDS read of entry (byte offset idx4 = nibble*4) of the table at slot `slot`.
+__device__ __forceinline__ float tab(const float *T, int slot, uint32_t idx4)
+{
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(T) + slot * (kSlotFloats * 4) + idx4);
+}
+
+// Byte m of w masked to bits 2..5: the byte offset of a nibble's table entry.
+// The compiler selects bytes 0, 2 and 3 with SDWA on its own; byte 1 is
+// spelled out so that it also costs a single instruction.
+__device__ __forceinline__ uint32_t nib4(uint32_t w, int m)
+{
+    if (m == 1) {
+        uint32_t r;
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+            : "=v"(r)
+            : "v"(w), "v"(0x3Cu));
+        return r;
+    }
+    return (w >> (8 * m)) & 0x3Cu;
+}
+
+typedef const u32x4 __attribute__((address_space(1))) *gptr;
+
+__device__ __forceinline__ u32x4 gload(const u32x4 *p)
+{
+    return __builtin_nontemporal_load((gptr)(p));
+}
+
+// ------------------------------------------------------------ block math
+// The eight lane chains of one block of the calling lane's row.  `b` is the
+// block's index inside the table chunk; v its four payload words; d0 its
+// widened scale.
+template <int FMT>
+__device__ __forceinline__ void block_math(const float *__restrict__ T, const float *__restrict__ D1, int b,
+                                           u32x4 v, float d0, float acc[8])
+{
+    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1 + 4 * b);
+    float ab[8];
+    if (FMT == BQ_Q1_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t wa = v[j];
+            const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+#pragma unroll
+            for (int L = 0; L < 8; ++L) {
+                const uint32_t idx = nib4((L & 1) ? wb : wa, L >> 1);
+                const float t = tab(T, b * kSlotsPerBlock + j * 8 + L, idx);
+                ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t wa = v[m];
+            const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+            const int j = m >> 1;
+#pragma unroll
+            for (int beta = 0; beta < 4; ++beta) {
+                const int L = 4 * (m & 1) + beta;
+                const int slot = b * kSlotsPerBlock + m * 8 + 2 * beta;
+                const float s = tab(T, slot, nib4(wa, beta)) + tab(T, slot + 1, nib4(wb, beta));
+                ab[L] = j == 0 ? d1[0] * s : __builtin_fmaf(d1[1], s, ab[L]);
+            }
+        }
+    }
+#pragma unroll
+    for (int L = 0; L < 8; ++L) {
+        acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
+        asm volatile("" : "+v"(acc[L]));  // keep each block's chain inside its own code
+    }
+}
+
+__device__ __forceinline__ float scale_of(u32x4 sc, int b)
+{
+    const uint32_t sw = sc[(b & 7) >> 1];
+    return f16_bits_to_f32((b & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+}
+
+// Payload words of the first kPrefetch blocks of a full chunk, plus its first
+// two scale groups; issued before the table build so their latency overlaps it.
+struct Prefetch {
+    u32x4 buf[kPrefetch];
+    u32x4 sc0, sc1;
+};
+
+__device__ __forceinline__ void prefetch_chunk(Prefetch &pf, const u32x4 *wp, const u32x4 *sp)
+{
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i)
+        pf.buf[i] = gload(wp + i * kTileRows);
+    pf.sc0 = gload(sp);
+    pf.sc1 = gload(sp + kTileRows);
+}
+
+// A full chunk of 32 blocks: loads run kPrefetch blocks ahead; every index is
+// a compile-time constant, so each table read carries its slot as an
+// immediate LDS offset.
+template <int FMT>
+__device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, const float *__restrict__ D1,
+                                               const u32x4 *wp, const u32x4 *sp, Prefetch &pf, float acc[8])
+{
+    u32x4 sc = pf.sc0, sc_next = pf.sc1;
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+        if ((b & 7) == 0 && b > 0) {
+            sc = sc_next;
+            if (b / 8 + 1 < kChunkBlocks / 8)
+                sc_next = gload(sp + (b / 8 + 1) * kTileRows);
+        }
+        const u32x4 v = pf.buf[b % kPrefetch];
+        if (b + kPrefetch < kChunkBlocks)
+            pf.buf[b % kPrefetch] = gload(wp + (b + kPrefetch) * kTileRows);
+        block_math<FMT>(T, D1, b, v, scale_of(sc, b), acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// A partial chunk (rows whose length is not a multiple of 32 blocks): plain
+// loop, no prefetch.
+template <int FMT>
+__device__ void run_tail_chunk(const float *__restrict__ T, const float *__restrict__ D1, const u32x4 *wp,
+                               const u32x4 *sp, int nbc, float acc[8])
+{
+    for (int b = 0; b < nbc; ++b) {
+        const u32x4 v = gload(wp + b * kTileRows);
+        const u32x4 sc = gload(sp + (b / 8) * kTileRows);
+        block_math<FMT>(T, D1, b, v, scale_of(sc, b), acc);
+    }
+}
+
+// Rows [64*tile0, 64*(tile0+ntiles)) of one product; the calling workgroup
+// has kWaves wavefronts, wavefront w taking tile tile0 + w.
+template <int FMT, int QA>
+__device__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool active = wave < ntiles;
+    const int tile = tile0 + wave;
+    const int per_chunk = FMT == BQ_Q1_0 ? 128 * kChunkBlocks : 64 * kChunkBlocks;
+    const u32x4 *wp = g.bits + ((int64_t)tile * g.nb) * kTileRows + lane;
+    const u32x4 *sp = g.scales + ((int64_t)tile * g.ng) * kTileRows + lane;
+    float acc[8];
+#pragma unroll
+    for (int L = 0; L < 8; ++L)
+        acc[L] = 0.0f;
+    for (int cb = 0; cb < g.nb; cb += kChunkBlocks) {
+        const int nbc = min(kChunkBlocks, g.nb - cb);
+        const u32x4 *wc = wp + (int64_t)cb * kTileRows;
+        const u32x4 *sc = sp + (int64_t)(cb / 8) * kTileRows;
+        Prefetch pf;
+        if (active && nbc == kChunkBlocks)
+            prefetch_chunk(pf, wc, sc);
+        __syncthreads();  // every wavefront is done with the previous table
+        if (FMT == BQ_Q1_0)
+            build_table_q1<QA>(T, D1, g.q, g.d, (cb / kChunkBlocks) * per_chunk, nbc);
+        else
+            build_table_q2<QA>(T, D1, g.q, g.d, (cb / kChunkBlocks) * per_chunk, nbc);
+        __syncthreads();
+        if (active) {
+            if (nbc == kChunkBlocks)
+                run_full_chunk<FMT>(T, D1, wc, sc, pf, acc);
+            else
+                run_tail_chunk<FMT>(T, D1, wc, sc, nbc, acc);
+        }
+    }
+    if (active) {
+        const int row = tile * kTileRows + lane;
+        const float y = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
+        if (row < g.rows)
+            g.y[row] = y;
+    }
+}
+
+template <int FMT, int QA>
+__global__ __launch_bounds__(kThreads) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int tiles)
+{
+    __shared__ float T[kTableFloats];
+    __shared__ float D1[kScaleFloats];
+    const int c = blockIdx.y;  // activation column
+    g.q += c * ld_q;
+    g.d += c * ld_d;
+    g.y += (int64_t)c * g.rows;
+    const int tile0 = blockIdx.x * kWaves;
+    run_item<FMT, QA>(g, tile0, min(kWaves, tiles - tile0), T, D1);
+}
+
+template <int FMT, int QA>
+__global__ __launch_bounds__(kThreads) void sweep_kernel(const GemvDesc *__restrict__ descs,
+                                                         const WorkItem *__restrict__ items)
+{
+    __shared__ float T[kTableFloats];
+    __shared__ float D1[kScaleFloats];
+    const WorkItem it = items[blockIdx.x];
+    const GemvDesc g = descs[it.gemv];
+    run_item<FMT, QA>(g, it.tile0, it.ntiles, T, D1);
+}
+
+// ------------------------------------------------------------ quantizer
+// Each thread quantizes 4 consecutive values; QA/4 threads share a block and
+// combine their |x| maxima with butterfly shuffles (max is exact in any order).
+template <int QA>
+__global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ x, int64_t n4, int8_t *__restrict__ q,
+                                                       float *__restrict__ d)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < n4)
+        v = reinterpret_cast<const f32x4 *>(x)[i];
+    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int off = 1; off < QA / 4; off <<= 1)
+        m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (i >= n4)
+        return;
+    const float db = m / 127.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int qv = 0;
+        if (db != 0.0f) {
+            float r = __builtin_roundf(v[e] / db);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            qv = (int)r;
+        }
+        packed |= (uint32_t)(qv & 0xFF) << (8 * e);
+    }
+    reinterpret_cast<uint32_t *>(q)[i] = packed;
+    if ((i & (QA / 4 - 1)) == 0)
+        d[i / (QA / 4)] = db;
+}
+
+// ------------------------------------------------------------ validation
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static int hip_check(const char *fn, hipError_t e)
+{
+    if (e != hipSuccess)
+        return set_error(BQ_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    return BQ_OK;
+}
+
+static int check_weights(const char *fn, const bq_weights *w, int fmt)
+{
+    if (!w)
+        return set_error(BQ_EARG, "%s: null weights", fn);
+    if (w->fmt != fmt)
+        return set_error(BQ_EARG, "%s: weights format %d, expected %d", fn, (int)w->fmt, fmt);
+    if (w->reserved != 0)
+        return set_error(BQ_EARG, "%s: weights.reserved must be 0", fn);
+    if (w->rows < 1 || w->rows >= (int64_t(1) << 31) || w->cols < 1 || w->cols >= (int64_t(1) << 31))
+        return set_error(BQ_EARG, "%s: rows %lld / cols %lld out of range", fn, (long long)w->rows,
+                         (long long)w->cols);
+    if (w->cols % block_len(fmt))
+        return set_error(BQ_EARG, "%s: cols %lld not a multiple of %d", fn, (long long)w->cols, block_len(fmt));
+    if (!w->bits || !w->scales)
+        return set_error(BQ_EARG, "%s: null weight plane", fn);
+    if (!aligned(w->bits, 16) || !aligned(w->scales, 16))
+        return set_error(BQ_EALIGN, "%s: weight planes must be 16-byte aligned", fn);
+    return BQ_OK;
+}
+
+static int check_act(const char *fn, const bq_act *a, int64_t cols, int max_cols)
+{
+    if (!a)
+        return set_error(BQ_EARG, "%s: null activation", fn);
+    if (a->n != cols)
+        return set_error(BQ_EARG, "%s: activation length %lld != weight cols %lld", fn, (long long)a->n,
+                         (long long)cols);
+    if (a->qa != 32 && a->qa != 64 && a->qa != 128)
+        return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)a->qa);
+    if (a->n % a->qa)
+        return set_error(BQ_EARG, "%s: n %lld not a multiple of qa %d", fn, (long long)a->n, (int)a->qa);
+    if (a->ncols < 1 || a->ncols > max_cols)
+        return set_error(BQ_EARG, "%s: ncols %d not in [1, %d]", fn, (int)a->ncols, max_cols);
+    if (!a->q || !a->d)
+        return set_error(BQ_EARG, "%s: null activation pointer", fn);
+    if (a->ncols > 1 && (a->ld_q < a->n || a->ld_d < a->n / a->qa))
+        return set_error(BQ_EARG, "%s: leading dimensions too small", fn);
+    if (!aligned(a->q, 16) || (a->ncols > 1 && a->ld_q % 16) || !aligned(a->d, 4))
+        return set_error(BQ_EALIGN, "%s: q must be 16-byte aligned (ld_q a multiple of 16), d 4-byte aligned", fn);
+    return BQ_OK;
+}
+
+static GemvDesc make_desc(const bq_weights *w, const bq_act *a, float *y)
+{
+    GemvDesc g;
+    memset(&g, 0, sizeof g);
+    const int64_t nb = w->cols / block_len(w->fmt);
+    g.bits = static_cast<const u32x4 *>(w->bits);
+    g.scales = reinterpret_cast<const u32x4 *>(w->scales);
+    g.q = a->q;
+    g.d = a->d;
+    g.y = y;
+    g.rows = (int32_t)w->rows;
+    g.nb = (int32_t)nb;
+    g.ng = (int32_t)groups_of(nb);
+    return g;
+}
+
+template <int FMT>
+static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, float *y, bq_stream s)
+{
+    int rc = check_weights(fn, w, FMT);
+    if (!rc)
+        rc = check_act(fn, a, w->cols, 16);
+    if (rc)
+        return rc;
+    if (!y)
+        return set_error(BQ_EARG, "%s: null y", fn);
+    if (!aligned(y, 4))
+        return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", fn);
+    const GemvDesc g = make_desc(w, a, y);
+    const int tiles = (int)tiles_of(w->rows);
+    const dim3 grid((tiles + kWaves - 1) / kWaves, a->ncols);
+    hipStream_t st = static_cast<hipStream_t>(s);
+    switch (a->qa) {
+    case 32: hipLaunchKernelGGL((matvec_kernel<FMT, 32>), grid, dim3(kThreads), 0, st, g, a->ld_q, a->ld_d, tiles); break;
+    case 64: hipLaunchKernelGGL((matvec_kernel<FMT, 64>), grid, dim3(kThreads), 0, st, g, a->ld_q, a->ld_d, tiles); break;
+    default: hipLaunchKernelGGL((matvec_kernel<FMT, 128>), grid, dim3(kThreads), 0, st, g, a->ld_q, a->ld_d, tiles); break;
+    }
+    return hip_check(fn, hipGetLastError());
+}
+
+}  // namespace bq
+
+using namespace bq;
+
+struct bq_sweep {
+    int fmt;
+    int qa;
+    int nitems;
+    int count;
+    void *dev;  // descriptors, then work items
+    const GemvDesc *descs;
+    const WorkItem *items;
+};
+
+BQ_EXPORT int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s)
+{
+    const char *fn = "bq_quantize_act_q8";
+    if (qa != 32 && qa != 64 && qa != 128)
+        return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)qa);
+    if (n < 0 || n % qa)
+        return set_error(BQ_EARG, "%s: n %lld is not a non-negative multiple of qa %d", fn, (long long)n, (int)qa);
+    if (!x || !q || !d)
+        return set_error(BQ_EARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4))
+        return set_error(BQ_EALIGN, "%s: x must be 16-byte aligned, q and d 4-byte aligned", fn);
+    if (n == 0)
+        return BQ_OK;
+    const int64_t n4 = n / 4;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    hipStream_t st = static_cast<hipStream_t>(s);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((quantize_kernel<32>), grid, dim3(256), 0, st, x, n4, q, d); break;
+    case 64: hipLaunchKernelGGL((quantize_kernel<64>), grid, dim3(256), 0, st, x, n4, q, d); break;
+    default: hipLaunchKernelGGL((quantize_kernel<128>), grid, dim3(256), 0, st, x, n4, q, d); break;
+    }
+    return hip_check(fn, hipGetLastError());
+}
+
+BQ_EXPORT int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
+{
+    return launch_matvec<BQ_Q1_0>("bq_q1_0_matvec", w, a, y, s);
+}
+
+BQ_EXPORT int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
+{
+    return launch_matvec<BQ_Q2_0>("bq_q2_0_matvec", w, a, y, s);
+}
+
+BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan)
+{
+    const char *fn = "bq_sweep_create";
+    if (!plan)
+        return set_error(BQ_EARG, "%s: null plan pointer", fn);
+    *plan = nullptr;
+    if (!list || count < 1)
+        return set_error(BQ_EARG, "%s: empty list", fn);
+    const int fmt = list[0].w.fmt, qa = list[0].a.qa;
+    std::vector<GemvDesc> descs((size_t)count);
+    std::vector<WorkItem> items;
+    std::vector<int64_t> cost;
+    for (int i = 0; i < count; ++i) {
+        const bq_gemv &e = list[i];
+        char where[96];
+        snprintf(where, sizeof where, "%s: entry %d", fn, i);
+        if (e.w.fmt != fmt || e.a.qa != qa)
+            return set_error(BQ_EARG, "%s: every entry must share the format and qa of entry 0", where);
+        int rc = check_weights(where, &e.w, fmt);
+        if (!rc)
+            rc = check_act(where, &e.a, e.w.cols, 1);
+        if (rc)
+            return rc;
+        if (!e.y)
+            return set_error(BQ_EARG, "%s: null y", where);
+        if (!aligned(e.y, 4))
+            return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
+        descs[(size_t)i] = make_desc(&e.w, &e.a, e.y);
+        const int tiles = (int)tiles_of(e.w.rows);
+        for (int t = 0; t < tiles; t += kWaves) {
+            WorkItem it;
+            it.gemv = i;
+            it.tile0 = t;
+            it.ntiles = std::min(kWaves, tiles - t);
+            it.pad = 0;
+            items.push_back(it);
+        }
+    }
+    // Most work first: the hardware dispatches workgroups in order, so the
+    // short items fill the tail.
+    std::vector<size_t> order(items.size());
+    for (size_t i = 0; i < order.size(); ++i)
+        order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+        const int64_t ca = (int64_t)items[a].ntiles * descs[(size_t)items[a].gemv].nb;
+        const int64_t cb = (int64_t)items[b].ntiles * descs[(size_t)items[b].gemv].nb;
+        return ca > cb;
+    });
+    std::vector<WorkItem> sorted(items.size());
+    for (size_t i = 0; i < order.size(); ++i)
+        sorted[i] = items[order[i]];
+
+    const size_t dbytes = descs.size() * sizeof(GemvDesc);
+    const size_t ibytes = sorted.size() * sizeof(WorkItem);
+    void *dev = nullptr;
+    if (hipMalloc(&dev, dbytes + ibytes) != hipSuccess)
+        return set_error(BQ_ENOMEM, "%s: hipMalloc of %zu bytes failed", fn, dbytes + ibytes);
+    hipError_t e = hipMemcpy(dev, descs.data(), dbytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(static_cast<char *>(dev) + dbytes, sorted.data(), ibytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(dev);
+        return set_error(BQ_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    }
+    bq_sweep *p = new (std::nothrow) bq_sweep;
+    if (!p) {
+        (void)hipFree(dev);
+        return set_error(BQ_ENOMEM, "%s: out of host memory", fn);
+    }
+    p->fmt = fmt;
+    p->qa = qa;
+    p->count = count;
+    p->nitems = (int)sorted.size();
+    p->dev = dev;
+    p->descs = static_cast<const GemvDesc *>(dev);
+    p->items = reinterpret_cast<const WorkItem *>(static_cast<char *>(dev) + dbytes);
+    *plan = p;
+    return BQ_OK;
+}
+
+BQ_EXPORT int bq_token_sweep(const bq_sweep *plan, bq_stream s)
+{
+    const char *fn = "bq_token_sweep";
+    if (!plan)
+        return set_error(BQ_EARG, "%s: null plan", fn);
+    hipStream_t st = static_cast<hipStream_t>(s);
+    const dim3 grid((unsigned)plan->nitems);
+#define BQ_SWEEP(F, Q) hipLaunchKernelGGL((sweep_kernel<F, Q>), grid, dim3(kThreads), 0, st, plan->descs, plan->items)
+    if (plan->fmt == BQ_Q1_0) {
+        if (plan->qa == 32) BQ_SWEEP(BQ_Q1_0, 32);
+        else if (plan->qa == 64) BQ_SWEEP(BQ_Q1_0, 64);
+        else BQ_SWEEP(BQ_Q1_0, 128);
+    } else {
+        if (plan->qa == 32) BQ_SWEEP(BQ_Q2_0, 32);
+        else if (plan->qa == 64) BQ_SWEEP(BQ_Q2_0, 64);
+        else BQ_SWEEP(BQ_Q2_0, 128);
+    }
+#undef BQ_SWEEP
+    return hip_check(fn, hipGetLastError());
+}
+
+BQ_EXPORT void bq_sweep_destroy(bq_sweep *plan)
+{
+    if (!plan)
+        return;
+    (void)hipDeviceSynchronize();
+    (void)hipFree(plan->dev);
+    delete plan;
+}

@@ -1,0 +1,80 @@
+"""Staging helpers for the GPU tests: move seeded inputs to the device, run the
+HIP path through the C ABI binding, bring results back as numpy."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import synth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def dev(a: np.ndarray):
+    return torch().from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def bqmod():
+    import ternary_quantized_gemv_amd as bq
+    return bq
+
+
+def stage_act(q: np.ndarray, d: np.ndarray, qa: int):
+    """q int8 [ncols, n], d float32 [ncols, n/qa] -> bq.Act on the device."""
+    bq = bqmod()
+    q = np.atleast_2d(q)
+    d = np.atleast_2d(d)
+    ncols, n = q.shape
+    return bq.Act(dev(q), dev(d), n, qa, ncols)
+
+
+def quantize_gpu(x: np.ndarray, qa: int):
+    t, bq = torch(), bqmod()
+    xd = dev(x.astype(np.float32))
+    q = t.empty(x.size, dtype=t.int8, device="cuda")
+    d = t.empty(x.size // qa, dtype=t.float32, device="cuda")
+    bq.bq_quantize_act_q8(xd, qa, q, d)
+    t.cuda.synchronize()
+    return q.cpu().numpy(), d.cpu().numpy()
+
+
+def matvec_gpu(fmt: int, canon: np.ndarray, rows: int, cols: int, q: np.ndarray, d: np.ndarray, qa: int):
+    t, bq = torch(), bqmod()
+    w = bq.Weights.upload(fmt, canon, rows, cols)
+    a = stage_act(q, d, qa)
+    y = t.full((a.ncols * rows,), float("nan"), dtype=t.float32, device="cuda")
+    (bq.bq_q1_0_matvec if fmt == 1 else bq.bq_q2_0_matvec)(w, a, y)
+    t.cuda.synchronize()
+    return y.cpu().numpy().reshape(a.ncols, rows)
+
+
+class SweepWorkload:
+    """Seeded products (the 253 of one decode token, or any list of shapes)
+    staged on the GPU, one float32 N(0, 1) activation vector per product."""
+
+    def __init__(self, fmt: int, shapes, seed: int, qa: int = 128):
+        from ternary_quantized_gemv_amd.staging import StagedSweep
+        shapes = list(shapes)
+        canon = [synth.blocks(fmt, r, c, seed, i) for i, (_, r, c) in enumerate(shapes)]
+        x = [synth.activation(c, seed, 1000 + i) for i, (_, _, c) in enumerate(shapes)]
+        self.s = StagedSweep(fmt, canon, shapes, x, qa)
+        s = self.s
+        self.fmt, self.shapes, self.qa = fmt, shapes, qa
+        self.canon, self.weights, self.entries = s.canon, s.weights, s.entries
+        self.koff, self.yoff, self.x = s.koff, s.yoff, s.x
+        self.q, self.d, self.y = s.q, s.d, s.y
+        self.rows_total = s.rows_total
+
+    def run(self, stream=None):
+        self.s.run(stream)
+
+    def close(self):
+        self.s.close()

@@ -1,0 +1,134 @@
+"""Host-side checks of libbq that need no GPU: the library loads, exports every
+symbol the header declares, packs and unpacks losslessly, lays blocks out as
+documented, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import ternary_quantized_gemv_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "bq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    names = header_functions()
+    assert set(names) == set(bq.EXPORTS), names
+    lib = ctypes.CDLL(bq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert bq.bq_abi_version() == 1
+
+
+@pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
+@pytest.mark.parametrize("rows,nb", [(1, 1), (63, 3), (64, 8), (65, 9), (200, 33)])
+def test_pack_roundtrip(fmt, rows, nb):
+    cols = nb * bq.BLOCK_LEN[fmt]
+    w = synth.blocks(fmt, rows, cols, 3, rows, nb)
+    bits, scales = bq.bq_pack(fmt, w, rows, cols)
+    nbits, nsc = bq.bq_packed_bytes(fmt, rows, cols)
+    tiles = -(-rows // 64)
+    assert bits.nbytes == nbits == tiles * 64 * nb * 16
+    assert scales.nbytes == nsc == tiles * 64 * (-(-nb // 8)) * 16
+    assert np.array_equal(bq.bq_unpack(fmt, bits, scales, rows, cols), w)
+
+
+def test_pack_layout():
+    """Payload word j of (row r, block b) sits at [tile][b][lane][j], rotated
+    left by 2; the scale at [tile][b/8][lane][b%8]; padding is zero."""
+    rows, nb = 70, 10
+    w = synth.q1_0_blocks(rows, nb * 128, 4)
+    bits, scales = bq.bq_pack(1, w, rows, nb * 128)
+    words = bits.view("<u4").reshape(2, nb, 64, 4)
+    sc = scales.reshape(2, 2, 64, 8)
+    for r in (0, 5, 63, 64, 69):
+        t, lane = divmod(r, 64)
+        for b in (0, 7, 8, 9):
+            canon = w[r, b, 2:].copy().view("<u4")
+            rot = ((canon.astype(np.uint64) << 2) | (canon.astype(np.uint64) >> 30)) & 0xFFFFFFFF
+            assert np.array_equal(words[t, b, lane], rot.astype(np.uint32))
+            assert int(sc[t, b // 8, lane, b % 8]) == int(w[r, b, 0]) | (int(w[r, b, 1]) << 8)
+    assert not words[1, :, 6:].any() and not sc[1, :, 6:].any()  # padded rows
+    assert not sc[:, 1, :, 2:].any()  # padded blocks 10..15
+
+
+@pytest.mark.parametrize("call,args,code", [
+    ("bq_packed_bytes", (3, 4, 128), bq.BQ_EARG),
+    ("bq_packed_bytes", (1, 0, 128), bq.BQ_EARG),
+    ("bq_packed_bytes", (1, 4, 100), bq.BQ_EARG),
+    ("bq_packed_bytes", (2, 4, 96), bq.BQ_EARG),
+])
+def test_host_argument_errors(call, args, code):
+    with pytest.raises(bq.BQError) as e:
+        getattr(bq, call)(*args)
+    assert e.value.code == code and call in str(e.value)
+
+
+def _c(fn, *args):
+    return fn(*args)
+
+
+def test_gpu_entry_points_validate_before_launch():
+    """Bad arguments are refused on the host, so these calls touch no GPU."""
+    lib = bq.lib
+    x = ctypes.c_void_p(0x1000)
+    assert lib.bq_quantize_act_q8(x, 256, 33, x, x, None) == bq.BQ_EARG
+    assert "qa" in bq.bq_last_error()
+    assert lib.bq_quantize_act_q8(x, 100, 32, x, x, None) == bq.BQ_EARG
+    assert lib.bq_quantize_act_q8(None, 256, 32, x, x, None) == bq.BQ_EARG
+    assert lib.bq_quantize_act_q8(ctypes.c_void_p(0x1004), 256, 32, x, x, None) == bq.BQ_EALIGN
+    assert lib.bq_quantize_act_q8(x, 0, 32, x, x, None) == bq.BQ_OK  # empty input: nothing to do
+
+    w = bq.bq_weights(1, 0, 64, 256, 0x1000, 0x2000)
+    a = bq.bq_act(0x3000, 0x4000, 256, 128, 1, 256, 2)
+    ok = lambda: (ctypes.byref(w), ctypes.byref(a))
+    assert lib.bq_q2_0_matvec(*ok(), 0x5000, None) == bq.BQ_EARG  # Q1_0 weights to the Q2_0 call
+    assert "format" in bq.bq_last_error()
+    assert lib.bq_q1_0_matvec(None, ctypes.byref(a), 0x5000, None) == bq.BQ_EARG
+    assert lib.bq_q1_0_matvec(*ok(), None, None) == bq.BQ_EARG
+    for field, val, code in [("cols", 200, bq.BQ_EARG), ("rows", 0, bq.BQ_EARG), ("bits", 0x1008, bq.BQ_EALIGN),
+                             ("reserved", 1, bq.BQ_EARG)]:
+        old = getattr(w, field)
+        setattr(w, field, val)
+        assert lib.bq_q1_0_matvec(*ok(), 0x5000, None) == code, field
+        setattr(w, field, old)
+    for field, val, code in [("n", 128, bq.BQ_EARG), ("qa", 16, bq.BQ_EARG), ("ncols", 0, bq.BQ_EARG),
+                             ("ncols", 17, bq.BQ_EARG), ("q", 0x3004, bq.BQ_EALIGN), ("d", 0x4002, bq.BQ_EALIGN)]:
+        old = getattr(a, field)
+        setattr(a, field, val)
+        assert lib.bq_q1_0_matvec(*ok(), 0x5000, None) == code, field
+        setattr(a, field, old)
+    assert lib.bq_q1_0_matvec(*ok(), 0x5002, None) == bq.BQ_EALIGN
+
+    plan = ctypes.c_void_p()
+    assert lib.bq_sweep_create(None, 0, ctypes.byref(plan)) == bq.BQ_EARG and not plan.value
+    arr = (bq.bq_gemv * 2)()
+    arr[0].w, arr[0].a, arr[0].y = w, a, 0x5000
+    arr[1].w, arr[1].a, arr[1].y = w, a, 0x6000
+    arr[1].a.qa = 32
+    assert lib.bq_sweep_create(arr, 2, ctypes.byref(plan)) == bq.BQ_EARG
+    assert "entry 1" in bq.bq_last_error()
+    arr[1].a.qa = 128
+    arr[1].a.ncols = 2
+    assert lib.bq_sweep_create(arr, 2, ctypes.byref(plan)) == bq.BQ_EARG
+    assert lib.bq_token_sweep(None, None) == bq.BQ_EARG
+    lib.bq_sweep_destroy(None)
+
+
+def test_host_tensors_are_refused():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(256)
+    with pytest.raises(bq.BQError):
+        bq.bq_quantize_act_q8(x, 128, torch.zeros(256, dtype=torch.int8), torch.zeros(2))

@@ -1,0 +1,218 @@
+"""The HIP path (through the C ABI) against the CPU oracle, element by element.
+
+The bar is bit-exact equality for every output element: the order of every
+rounding is fixed (bankML "gpu/ -- the video-card component", section
+"kernels.rs -- the Q1_0 kernels"), so exactly one result is correct.  The
+scaled error max|gpu - oracle| / max|oracle| is reported beside it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import SweepWorkload, log, matvec_gpu, quantize_gpu, torch
+from pins import load_witnesses, same_bits
+
+pytestmark = pytest.mark.gpu
+
+Q1, Q2 = 1, 2
+QK = {Q1: 128, Q2: 64}
+THREADS = 16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import ternary_quantized_gemv_amd  # noqa: F401  (fails loudly if libbq.so is missing)
+    yield
+
+
+def assert_parity(y_gpu, y_ref, what):
+    y_gpu = np.asarray(y_gpu, np.float32)
+    y_ref = np.asarray(y_ref, np.float32)
+    assert y_gpu.shape == y_ref.shape
+    bad = np.flatnonzero(y_gpu.view(np.uint32) != y_ref.view(np.uint32))
+    scale = float(np.max(np.abs(y_ref))) or 1.0
+    err = float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref))) / scale if y_ref.size else 0.0
+    log(f"{what}: {y_ref.size} outputs, {bad.size} differ, scaled error {err:.3g}")
+    assert bad.size == 0, (what, bad[:8], y_gpu.ravel()[bad[:4]], y_ref.ravel()[bad[:4]])
+
+
+# --------------------------------------------------------------- witnesses
+@pytest.mark.parametrize("w", load_witnesses(), ids=lambda w: w["name"])
+def test_witness_gpu(w):
+    log("witness", w["name"])
+    y = matvec_gpu(w["fmt"], w["blocks"], 1, w["cols"], w["q"], w["d"], w["qa"])
+    assert same_bits(y[0, 0], w["expected"]), (float(y[0, 0]), float(w["expected"]))
+
+
+# ---------------------------------------------------------------- quantizer
+@pytest.mark.parametrize("qa", [32, 64, 128])
+@pytest.mark.parametrize("regime", ["normal", "layer", "special"])
+def test_quantizer_parity(qa, regime):
+    log("quantizer", qa, regime)
+    n = 12288 + 384
+    if regime == "normal":
+        x = synth.activation(n, 21, qa)
+    elif regime == "layer":
+        x = synth.layer_shaped(Q1, 1, n, 22, qa)[1]
+    else:
+        x = synth.activation(n, 23, qa)
+        x[:qa] = 0.0                                     # an all-zero block
+        x[qa:2 * qa] = 0.0
+        x[qa:qa + 6] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5]  # d = 1: exact ties
+        x[2 * qa:2 * qa + 3] = [5207.0, 20.5, -20.5]       # d = 41: x/d = 1/2 exactly
+        x[3 * qa] = 1e-30                                  # tiny scale
+        x[4 * qa:5 * qa] = -3.0                            # constant block
+    q_ref, d_ref, clamped = oracle.quantize_q8(x, qa)
+    assert clamped == 0
+    q, d = quantize_gpu(x, qa)
+    assert np.array_equal(q, q_ref)
+    assert same_bits(d, d_ref)
+
+
+# ------------------------------------------------------- small-shape matvec
+SHAPES = [(1, 1), (64, 4), (100, 33), (513, 8), (1000, 64), (130, 70)]  # (rows, blocks per row)
+
+
+def _cases():
+    out = []
+    for fmt in (Q1, Q2):
+        for rows, nb in SHAPES:
+            cols = nb * QK[fmt]
+            for qa in (32, 64, 128):
+                if cols % qa:
+                    continue
+                for regime in ("quant", "raw", "layer"):
+                    out.append((fmt, rows, cols, qa, regime))
+    return out
+
+
+def _inputs(fmt, rows, cols, qa, regime, seed):
+    if regime == "layer":
+        w, x = synth.layer_shaped(fmt, rows, cols, seed)
+        q, d, _ = oracle.quantize_q8(x, qa)
+    elif regime == "raw":
+        w = synth.blocks(fmt, rows, cols, seed)
+        q, d = synth.raw_q8(cols, qa, seed)
+    else:
+        w = synth.blocks(fmt, rows, cols, seed)
+        q, d, _ = oracle.quantize_q8(synth.activation(cols, seed), qa)
+    return w, q, d
+
+
+@pytest.mark.parametrize("fmt,rows,cols,qa,regime", _cases())
+def test_matvec_parity_small(fmt, rows, cols, qa, regime):
+    name = f"matvec fmt={fmt} {rows}x{cols} qa={qa} {regime}"
+    log(name)
+    w, q, d = _inputs(fmt, rows, cols, qa, regime, seed=rows * 7 + cols)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
+
+
+@pytest.mark.parametrize("fmt", [Q1, Q2])
+@pytest.mark.parametrize("ncols", [2, 4, 16])
+def test_matvec_columns(fmt, ncols):
+    rows, cols, qa = 200, 33 * 128, 128
+    log(f"columns fmt={fmt} ncols={ncols}")
+    w = synth.blocks(fmt, rows, cols, 31)
+    qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 31, c), qa)[:2] for c in range(ncols)])
+    q, d = np.stack(qs), np.stack(ds)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, f"columns fmt={fmt} ncols={ncols}")
+
+
+# ------------------------------------------------- full-size single products
+FULL = [
+    (Q1, 4096, 4096), (Q1, 12288, 4096), (Q1, 4096, 12288), (Q1, 151936, 4096),
+    (Q2, 4096, 4096), (Q2, 1024, 4096), (Q2, 12288, 4096), (Q2, 4096, 12288),
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols", FULL, ids=[f"q{f}-{r}x{c}" for f, r, c in FULL])
+def test_matvec_full_size(fmt, rows, cols):
+    name = f"full fmt={fmt} {rows}x{cols}"
+    log(name)
+    w = synth.blocks(fmt, rows, cols, 41, rows, cols)
+    x = synth.activation(cols, 41, rows)
+    q_ref, d_ref, _ = oracle.quantize_q8(x, 128)
+    q, d = quantize_gpu(x, 128)
+    assert np.array_equal(q, q_ref) and same_bits(d, d_ref)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q_ref, d_ref, 128, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, 128), y_ref, name)
+
+
+@pytest.mark.parametrize("rows", [12288, 151936])
+def test_small_batch_full_size(rows):
+    cols, qa = 4096, 128
+    w = synth.q1_0_blocks(rows, cols, 51, rows)
+    for ncols in (1, 4, 8, 16):
+        name = f"small batch Q1_0 {rows}x{cols} N={ncols}"
+        log(name)
+        qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 51, c), qa)[:2] for c in range(ncols)])
+        q, d = np.stack(qs), np.stack(ds)
+        y_ref = oracle.matvec(Q1, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+        assert_parity(matvec_gpu(Q1, w, rows, cols, q, d, qa), y_ref, name)
+
+
+# ------------------------------------------------------------ token sweeps
+def _check_sweep(fmt, shapes, seed):
+    t = torch()
+    log(f"sweep fmt={fmt}: staging {len(shapes)} products")
+    wl = SweepWorkload(fmt, shapes, seed)
+    try:
+        wl.run()
+        t.cuda.synchronize()
+        y = wl.y.cpu().numpy()
+        q_gpu, d_gpu = wl.q.cpu().numpy(), wl.d.cpu().numpy()
+        q_ref, d_ref, _ = oracle.quantize_q8(wl.x, wl.qa)
+        assert np.array_equal(q_gpu, q_ref) and same_bits(d_gpu, d_ref)
+        bad = 0
+        for i, (name, rows, cols) in enumerate(shapes):
+            k0 = wl.koff[i]
+            y_ref = oracle.matvec(fmt, wl.canon[i], rows, cols, q_ref[k0:k0 + cols],
+                                  d_ref[k0 // wl.qa:(k0 + cols) // wl.qa], wl.qa, threads=THREADS)[0]
+            yi = y[wl.yoff[i]:wl.yoff[i + 1]]
+            nbad = int(np.count_nonzero(yi.view(np.uint32) != y_ref.view(np.uint32)))
+            if nbad:
+                log(f"  {name}: {nbad} of {rows} rows differ")
+            bad += nbad
+        log(f"sweep fmt={fmt}: {wl.rows_total} outputs checked, {bad} differ")
+        assert bad == 0
+        # the sweep and the single-product call agree bit for bit, and repeat runs are identical
+        for i in (0, 6, len(shapes) - 1):
+            a = wl.entries[i][1]
+            yi = t.empty(shapes[i][1], dtype=t.float32, device="cuda")
+            import ternary_quantized_gemv_amd as bq
+            (bq.bq_q1_0_matvec if fmt == Q1 else bq.bq_q2_0_matvec)(wl.weights[i], a, yi)
+            t.cuda.synchronize()
+            assert same_bits(yi.cpu().numpy(), y[wl.yoff[i]:wl.yoff[i + 1]])
+        wl.run()
+        t.cuda.synchronize()
+        assert same_bits(wl.y.cpu().numpy(), y)
+    finally:
+        wl.close()
+
+
+def test_sweep_q1_0_decode_token():
+    _check_sweep(Q1, synth.decode_sweep_shapes(), seed=61)
+
+
+def test_sweep_q2_0_decode_token():
+    _check_sweep(Q2, synth.decode_sweep_shapes(), seed=62)
+
+
+def test_sweep_ragged_mix():
+    shapes = [("a", 1, 128), ("b", 100, 33 * 128), ("c", 65, 4096), ("d", 700, 12288), ("e", 64, 256)]
+    _check_sweep(Q1, shapes, seed=63)
+
+
+def test_gpu_errors_are_reported():
+    import ternary_quantized_gemv_amd as bq
+    t = torch()
+    x = t.zeros(256, device="cuda")
+    with pytest.raises(bq.BQError) as e:
+        bq.bq_quantize_act_q8(x, 48, t.zeros(256, dtype=t.int8, device="cuda"), t.zeros(8, device="cuda"))
+    assert e.value.code == bq.BQ_EARG and "bq_quantize_act_q8" in str(e.value)
