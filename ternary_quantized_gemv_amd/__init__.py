@@ -52,10 +52,31 @@ class bq_gemv(ctypes.Structure):
     _fields_ = [("w", bq_weights), ("a", bq_act), ("y", ctypes.c_void_p)]
 
 
+def _hip_runtimes() -> set:
+    """Paths of every HIP runtime library mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ternary_quantized_gemv_amd.build`")
+    # torch ships its own HIP runtime (same soname).  Loading torch first lets
+    # libbq bind to that already-loaded copy, so device pointers and streams
+    # from torch are valid in libbq's calls.  Two runtimes in one process would
+    # each see the device separately, so that case is refused below.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(runtimes)}); import torch before anything "
+                          "that links libamdhip64 so that libbq shares torch's runtime")
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.bq_abi_version.restype = ctypes.c_int
     lib.bq_abi_version.argtypes = []
