@@ -22,7 +22,7 @@
  *   [VK]   vkML "Shaders and the GLSL layer", section "f16 is storage, never
  *          arithmetic" (an f16 load is an exact widening).
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   R1  Q1_0 block = f16 scale (little-endian) then 16 payload bytes; weight k
  *       of the block is bit (k & 7) of byte (k >> 3); bit 1 -> +1, 0 -> -1.
  *   R2  Q2_0 block = f16 scale then 16 payload bytes of 2-bit codes; weight k
