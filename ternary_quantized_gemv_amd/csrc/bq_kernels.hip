@@ -56,9 +56,36 @@ constexpr int kSlotsPerBlock = 32;                                   // nibbles 
 constexpr int kSlotFloats = 16;                                      // entries per nibble table
 constexpr int kTableFloats = kChunkBlocks * kSlotsPerBlock * kSlotFloats;  // 64 KiB
 constexpr int kScaleFloats = kChunkBlocks * 4;                       // d1 per sub-block
-constexpr int kWaves = 8;                                            // wavefronts per workgroup
+#ifndef BQ_WAVES
+#define BQ_WAVES 8
+#endif
+#ifndef BQ_PREFETCH
+#define BQ_PREFETCH 4
+#endif
+#ifndef BQ_PIPE
+#define BQ_PIPE 1
+#endif
+constexpr int kWaves = BQ_WAVES;                                     // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kPrefetch = 4;                                         // blocks loaded ahead
+constexpr int kPrefetch = BQ_PREFETCH;                               // blocks loaded ahead
+#ifdef BQ_WPE
+#define BQ_KATTR __attribute__((amdgpu_waves_per_eu(BQ_WPE, BQ_WPE)))
+#else
+#define BQ_KATTR
+#endif
+#ifndef BQ_MAX_ROUNDS
+#define BQ_MAX_ROUNDS 3
+#endif
+#ifndef BQ_TAIL_ITEMS
+#define BQ_TAIL_ITEMS 1024
+#endif
+// Sweep work items of single-chunk products hold up to kMaxRounds tiles per
+// wavefront, all served by one table; the last kTailItems items of the
+// dispatch order are cut back to one tile per wavefront so the end of the
+// launch drains in small pieces.
+constexpr int kMaxRounds = BQ_MAX_ROUNDS;
+static_assert(kChunkBlocks % kPrefetch == 0, "a chunk must hold a whole number of prefetch rounds");
+constexpr int kTailItems = BQ_TAIL_ITEMS;
 
 struct GemvDesc {
     const u32x4 *bits;    // payload plane
@@ -75,9 +102,27 @@ struct GemvDesc {
 struct WorkItem {
     int32_t gemv;
     int32_t tile0;
-    int32_t ntiles;
+    int32_t ntiles;  // tiles tile0 .. tile0+ntiles-1; wavefront w takes tile0+w, tile0+w+kWaves, ...
     int32_t pad;
 };
+
+typedef const float __attribute__((address_space(4))) *cfptr;
+
+// Weight planes are read through buffer resources: the wave-uniform base of
+// a tile sits in scalar registers, each lane adds its 16-byte offset, and the
+// block offset is a scalar constant, so a load costs no vector address math.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t rsrc_of(const u32x4 *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(base), (short)0, 0x7FFFFFF0, 0x00020000);
+}
+
+// 16 bytes at base + voff + soff, streamed (non-temporal).
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
 {
@@ -85,14 +130,18 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
 }
 
 // --------------------------------------------------------------- tables
+// Each thread writes one quarter (4 entries, 16 bytes) of a slot's table per
+// step, so a wavefront's stores cover 1 KiB of consecutive LDS addresses.
+//
 // Q1_0: slot t of a chunk covers chunk values 4t..4t+3 (block t/32, sub-block
-// (t/8)%4, lane t%8).  Entry n: s = sum_i (bit i of n ? q_i : -q_i), where the
-// negation of -128 stays -128; on sub-block 0 the entry is d1*s instead.
+// (t/8)%4, lane t%8).  Entry n = 4h + e: s = sum_i (bit i of n ? q_i : -q_i),
+// where the negation of -128 stays -128; on sub-block 0 the entry is d1*s.
 template <int QA>
 __device__ void build_table_q1(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
 {
-    const int nslots = nbc * kSlotsPerBlock;
-    for (int t = threadIdx.x; t < nslots; t += blockDim.x) {
+    const int nquarters = nbc * kSlotsPerBlock * 4;
+    for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
+        const int t = u >> 2, h = u & 3;
         const uint32_t w4 = *reinterpret_cast<const uint32_t *>(q + k0 + 4 * t);
         int p1[4], p0[4];
 #pragma unroll
@@ -101,49 +150,38 @@ __device__ void build_table_q1(float *T, float *D1, const int8_t *q, const float
             p1[i] = v;
             p0[i] = v == -128 ? -128 : -v;
         }
-        int lo[4], hi[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            lo[x] = ((x & 1) ? p1[0] : p0[0]) + ((x & 2) ? p1[1] : p0[1]);
-            hi[x] = ((x & 1) ? p1[2] : p0[2]) + ((x & 2) ? p1[3] : p0[3]);
-        }
+        const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
         const bool first = ((t >> 3) & 3) == 0;
-        const float d1 = d[(k0 + 4 * t) / QA];
-        f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+        const float d1 = first ? d[(k0 + 4 * t) / QA] : 0.0f;
+        f32x4 v;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float s = (float)(lo[e] + hi[h]);
-                v[e] = first ? d1 * s : s;
-            }
-            dst[h] = v;
+        for (int e = 0; e < 4; ++e) {
+            const int lo = ((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]);
+            const float sf = (float)(lo + hi);
+            v[e] = first ? d1 * sf : sf;
         }
+        reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
     }
     for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x)
         D1[i] = d[(k0 + 32 * i) / QA];
 }
 
 // Q2_0: slot t of a chunk covers chunk values 2t and 2t+1 (the low or high
-// nibble of payload byte t/2 of its block).  Entry n = (a, b) codes:
-// (a-1)*q_2t + (b-1)*q_2t+1.
+// nibble of payload byte t/2 of its block).  Entry n = 4h + e holds the codes
+// (e, h): (e-1)*q_2t + (h-1)*q_2t+1.
 template <int QA>
 __device__ void build_table_q2(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
 {
-    const int nslots = nbc * kSlotsPerBlock;
-    for (int t = threadIdx.x; t < nslots; t += blockDim.x) {
+    const int nquarters = nbc * kSlotsPerBlock * 4;
+    for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
+        const int t = u >> 2, h = u & 3;
         const uint32_t w2 = *reinterpret_cast<const uint16_t *>(q + k0 + 2 * t);
         const int qa0 = (int8_t)(w2 & 0xFF), qa1 = (int8_t)(w2 >> 8);
-        f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+        f32x4 v;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
-            dst[h] = v;
-        }
+        for (int e = 0; e < 4; ++e)
+            v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
+        reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
     }
     // d1 per (block, sub-block): D1[4b + j], j = 0, 1.
     for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x) {
@@ -163,6 +201,13 @@ __device__ __forceinline__ float tab(const float *T, int slot, uint32_t idx4)
 // spelled out so that it also costs a single instruction.
 __device__ __forceinline__ uint32_t nib4(uint32_t w, int m)
 {
+#ifdef BQ_NO_SDWA
+    if (m > 0) {
+        uint32_t t = w >> (8 * m);
+        asm volatile("" : "+v"(t));
+        return t & 0x3Cu;
+    }
+#endif
     if (m == 1) {
         uint32_t r;
         asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
@@ -173,22 +218,57 @@ __device__ __forceinline__ uint32_t nib4(uint32_t w, int m)
     return (w >> (8 * m)) & 0x3Cu;
 }
 
-typedef const u32x4 __attribute__((address_space(1))) *gptr;
+// ------------------------------------------------------- activation scales
+// d1 of the four sub-blocks of block b of a chunk.  When a full chunk has at
+// most 32 distinct activation scales they sit in scalar registers for the
+// whole chunk (loaded once, wave-uniform); otherwise they are read from the
+// chunk's LDS copy.
+template <int FMT, int QA>
+struct ChunkScales {
+    static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
+    static constexpr int ND = kChunkBlocks * BL / QA;
+    static constexpr bool kScalar = ND <= 32;
+    float dv[kScalar ? ND : 1];
 
-__device__ __forceinline__ u32x4 gload(const u32x4 *p)
-{
-    return __builtin_nontemporal_load((gptr)(p));
-}
+    __device__ __forceinline__ void load(const float *d_chunk)
+    {
+        if (kScalar) {
+            // the address is wave-uniform; say so, so that the loads are scalar
+            const uint64_t a = (uint64_t)d_chunk;
+            const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+            const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+            const cfptr gc = (cfptr)(const float *)((hi << 32) | lo);
+#pragma unroll
+            for (int i = 0; i < (kScalar ? ND : 1); ++i) {
+                dv[i] = gc[i];
+                asm volatile("" : "+s"(dv[i]));  // load all of them here, once per chunk
+            }
+        }
+    }
+
+    __device__ __forceinline__ f32x4 get(const float *__restrict__ D1, int b) const
+    {
+        f32x4 r;
+        if (kScalar) {
+            constexpr int sub = FMT == BQ_Q1_0 ? 4 : 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r[j] = j < sub ? dv[((BL * b + 32 * j) / QA) % (kScalar ? ND : 1)] : 0.0f;
+        } else {
+            r = *reinterpret_cast<const f32x4 *>(D1 + 4 * b);
+        }
+        return r;
+    }
+};
 
 // ------------------------------------------------------------ block math
 // The eight lane chains of one block of the calling lane's row.  `b` is the
 // block's index inside the table chunk; v its four payload words; d0 its
 // widened scale.
 template <int FMT>
-__device__ __forceinline__ void block_math(const float *__restrict__ T, const float *__restrict__ D1, int b,
-                                           u32x4 v, float d0, float acc[8])
+__device__ __forceinline__ void block_math(const float *__restrict__ T, const f32x4 d1, int b, u32x4 v, float d0,
+                                           float acc[8])
 {
-    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1 + 4 * b);
     float ab[8];
     if (FMT == BQ_Q1_0) {
 #pragma unroll
@@ -201,6 +281,10 @@ __device__ __forceinline__ void block_math(const float *__restrict__ T, const fl
                 const float t = tab(T, b * kSlotsPerBlock + j * 8 + L, idx);
                 ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
             }
+#ifdef BQ_SPLIT
+            if (j % BQ_SPLIT == BQ_SPLIT - 1)
+                __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     } else {
 #pragma unroll
@@ -224,6 +308,15 @@ __device__ __forceinline__ void block_math(const float *__restrict__ T, const fl
     }
 }
 
+// The eight table reads of sub-block j of a Q1_0 block.
+__device__ __forceinline__ void lookups_q1(const float *__restrict__ T, int b, int j, uint32_t wa, float t[8])
+{
+    const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+#pragma unroll
+    for (int L = 0; L < 8; ++L)
+        t[L] = tab(T, b * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1));
+}
+
 __device__ __forceinline__ float scale_of(u32x4 sc, int b)
 {
     const uint32_t sw = sc[(b & 7) >> 1];
@@ -231,102 +324,192 @@ __device__ __forceinline__ float scale_of(u32x4 sc, int b)
 }
 
 // Payload words of the first kPrefetch blocks of a full chunk, plus its first
-// two scale groups; issued before the table build so their latency overlaps it.
+// two scale groups.
 struct Prefetch {
     u32x4 buf[kPrefetch];
     u32x4 sc0, sc1;
 };
 
-__device__ __forceinline__ void prefetch_chunk(Prefetch &pf, const u32x4 *wp, const u32x4 *sp)
+constexpr uint32_t kStep = kTileRows * 16;  // bytes of one block (or scale group) of a tile
+
+__device__ __forceinline__ void prefetch_chunk(Prefetch &pf, rsrc_t w, rsrc_t sc, uint32_t lo)
 {
 #pragma unroll
     for (int i = 0; i < kPrefetch; ++i)
-        pf.buf[i] = gload(wp + i * kTileRows);
-    pf.sc0 = gload(sp);
-    pf.sc1 = gload(sp + kTileRows);
+        pf.buf[i] = bload(w, lo, i * kStep);
+    pf.sc0 = bload(sc, lo, 0);
+    pf.sc1 = bload(sc, lo, kStep);
 }
 
-// A full chunk of 32 blocks: loads run kPrefetch blocks ahead; every index is
-// a compile-time constant, so each table read carries its slot as an
-// immediate LDS offset.
-template <int FMT>
+// A full chunk of 32 blocks.  Loads run kPrefetch blocks ahead; the last
+// iterations already load the first blocks and scale groups of the next full
+// chunk this wavefront will run (wn, sn), if has_next.  Every index is a
+// compile-time constant, so each table read carries its slot as an immediate
+// LDS offset.  For Q1_0 the table reads of block b+1 are issued, sub-block by
+// sub-block, between the fma steps of block b.
+template <int FMT, int QA>
 __device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, const float *__restrict__ D1,
-                                               const u32x4 *wp, const u32x4 *sp, Prefetch &pf, float acc[8])
+                                               const ChunkScales<FMT, QA> &cs, rsrc_t wp, rsrc_t sp, rsrc_t wn,
+                                               rsrc_t sn, bool has_next, uint32_t lo, Prefetch &pf, float acc[8])
 {
     u32x4 sc = pf.sc0, sc_next = pf.sc1;
+    float tc[32], tn[32];
+    if (FMT == BQ_Q1_0 && BQ_PIPE) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lookups_q1(T, 0, j, pf.buf[0][j], tc + 8 * j);
+    }
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         if ((b & 7) == 0 && b > 0) {
             sc = sc_next;
             if (b / 8 + 1 < kChunkBlocks / 8)
-                sc_next = gload(sp + (b / 8 + 1) * kTileRows);
+                sc_next = bload(sp, lo, (b / 8 + 1) * kStep);
+            else if (has_next)
+                sc_next = bload(sn, lo, 0);
         }
         const u32x4 v = pf.buf[b % kPrefetch];
         if (b + kPrefetch < kChunkBlocks)
-            pf.buf[b % kPrefetch] = gload(wp + (b + kPrefetch) * kTileRows);
-        block_math<FMT>(T, D1, b, v, scale_of(sc, b), acc);
+            pf.buf[b % kPrefetch] = bload(wp, lo, (b + kPrefetch) * kStep);
+        else if (has_next)
+            pf.buf[b % kPrefetch] = bload(wn, lo, (b + kPrefetch - kChunkBlocks) * kStep);
+        const f32x4 d1 = cs.get(D1, b);
+        float d0 = scale_of(sc, b);
+        // widen once: eight v_fmac_f32 then run at full rate, where v_fma_mix_f32
+        // (the compiler's choice for an f16 operand) runs at half rate
+        asm volatile("" : "+v"(d0));
+        if (FMT == BQ_Q1_0 && BQ_PIPE) {
+            const u32x4 vn = pf.buf[(b + 1) % kPrefetch];
+            float ab[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (b + 1 < kChunkBlocks)
+                    lookups_q1(T, b + 1, j, vn[j], tn + 8 * j);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int L = 0; L < 8; ++L)
+                    ab[L] = j == 0 ? tc[L] : __builtin_fmaf(d1[j], tc[8 * j + L], ab[L]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int L = 0; L < 8; ++L) {
+                acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
+                asm volatile("" : "+v"(acc[L]));
+            }
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                tc[i] = tn[i];
+        } else {
+            block_math<FMT>(T, d1, b, v, d0, acc);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
+    pf.sc0 = sc_next;
+    if (has_next)
+        pf.sc1 = bload(sn, lo, kStep);
 }
 
 // A partial chunk (rows whose length is not a multiple of 32 blocks): plain
 // loop, no prefetch.
 template <int FMT>
-__device__ void run_tail_chunk(const float *__restrict__ T, const float *__restrict__ D1, const u32x4 *wp,
-                               const u32x4 *sp, int nbc, float acc[8])
+__device__ void run_tail_chunk(const float *__restrict__ T, const float *__restrict__ D1, rsrc_t wp, rsrc_t sp,
+                               uint32_t lo, int nbc, float acc[8])
 {
     for (int b = 0; b < nbc; ++b) {
-        const u32x4 v = gload(wp + b * kTileRows);
-        const u32x4 sc = gload(sp + (b / 8) * kTileRows);
-        block_math<FMT>(T, D1, b, v, scale_of(sc, b), acc);
+        const u32x4 v = bload(wp, lo, b * kStep);
+        const u32x4 sc = bload(sp, lo, (b / 8) * kStep);
+        block_math<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * b), b, v, scale_of(sc, b), acc);
     }
 }
 
-// Rows [64*tile0, 64*(tile0+ntiles)) of one product; the calling workgroup
-// has kWaves wavefronts, wavefront w taking tile tile0 + w.
-template <int FMT, int QA>
-__device__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1)
+__device__ __forceinline__ void store_row(const GemvDesc &g, int tile, int lane, const float acc[8])
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const bool active = wave < ntiles;
-    const int tile = tile0 + wave;
+    const int row = tile * kTileRows + lane;
+    const float y = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
+    if (row < g.rows)
+        g.y[row] = y;
+}
+
+// Rows [64*tile0, 64*(tile0+ntiles)) of one product; wavefront w takes tiles
+// tile0 + w, tile0 + w + kWaves, ...  Rows of at most one chunk share one
+// table for every tile of the item; longer rows (ntiles <= kWaves) walk the
+// chunks with a table rebuild between barriers.
+template <int FMT, int QA>
+__device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1)
+{
+    // the wavefront index is wave-uniform: say so, so that tile addresses live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int per_chunk = FMT == BQ_Q1_0 ? 128 * kChunkBlocks : 64 * kChunkBlocks;
-    const u32x4 *wp = g.bits + ((int64_t)tile * g.nb) * kTileRows + lane;
-    const u32x4 *sp = g.scales + ((int64_t)tile * g.ng) * kTileRows + lane;
+    const int tend = tile0 + ntiles;
+    const uint32_t lo = (uint32_t)lane * 16;
+    auto wtile = [&](int tile, int cb) { return rsrc_of(g.bits + ((int64_t)tile * g.nb + cb) * kTileRows); };
+    auto stile = [&](int tile, int cb) { return rsrc_of(g.scales + ((int64_t)tile * g.ng + cb / 8) * kTileRows); };
     float acc[8];
+    Prefetch pf;
+
+    if (g.nb <= kChunkBlocks) {
+        const int nbc = g.nb;
+        int tile = tile0 + wave;
+        if (tile < tend && nbc == kChunkBlocks)
+            prefetch_chunk(pf, wtile(tile, 0), stile(tile, 0), lo);
+        if (FMT == BQ_Q1_0)
+            build_table_q1<QA>(T, D1, g.q, g.d, 0, nbc);
+        else
+            build_table_q2<QA>(T, D1, g.q, g.d, 0, nbc);
+        __syncthreads();
+        ChunkScales<FMT, QA> cs;
+        if (nbc == kChunkBlocks)
+            cs.load(g.d);
+        for (; tile < tend; tile += kWaves) {
+#pragma unroll
+            for (int L = 0; L < 8; ++L)
+                acc[L] = 0.0f;
+            const bool has_next = tile + kWaves < tend;
+            if (nbc == kChunkBlocks)
+                run_full_chunk<FMT, QA>(T, D1, cs, wtile(tile, 0), stile(tile, 0), wtile(tile + kWaves, 0),
+                                        stile(tile + kWaves, 0), has_next, lo, pf, acc);
+            else
+                run_tail_chunk<FMT>(T, D1, wtile(tile, 0), stile(tile, 0), lo, nbc, acc);
+            store_row(g, tile, lane, acc);
+        }
+        return;
+    }
+
+    const int tile = tile0 + wave;
+    const bool active = tile < tend;
 #pragma unroll
     for (int L = 0; L < 8; ++L)
         acc[L] = 0.0f;
+    if (active)
+        prefetch_chunk(pf, wtile(tile, 0), stile(tile, 0), lo);
     for (int cb = 0; cb < g.nb; cb += kChunkBlocks) {
         const int nbc = min(kChunkBlocks, g.nb - cb);
-        const u32x4 *wc = wp + (int64_t)cb * kTileRows;
-        const u32x4 *sc = sp + (int64_t)(cb / 8) * kTileRows;
-        Prefetch pf;
-        if (active && nbc == kChunkBlocks)
-            prefetch_chunk(pf, wc, sc);
-        __syncthreads();  // every wavefront is done with the previous table
+        const int k0 = (cb / kChunkBlocks) * per_chunk;
+        if (cb > 0)
+            __syncthreads();  // every wavefront is done with the previous table
         if (FMT == BQ_Q1_0)
-            build_table_q1<QA>(T, D1, g.q, g.d, (cb / kChunkBlocks) * per_chunk, nbc);
+            build_table_q1<QA>(T, D1, g.q, g.d, k0, nbc);
         else
-            build_table_q2<QA>(T, D1, g.q, g.d, (cb / kChunkBlocks) * per_chunk, nbc);
+            build_table_q2<QA>(T, D1, g.q, g.d, k0, nbc);
         __syncthreads();
         if (active) {
-            if (nbc == kChunkBlocks)
-                run_full_chunk<FMT>(T, D1, wc, sc, pf, acc);
-            else
-                run_tail_chunk<FMT>(T, D1, wc, sc, nbc, acc);
+            if (nbc == kChunkBlocks) {
+                ChunkScales<FMT, QA> cs;
+                cs.load(g.d + k0 / QA);
+                const bool has_next = cb + 2 * kChunkBlocks <= g.nb;
+                run_full_chunk<FMT, QA>(T, D1, cs, wtile(tile, cb), stile(tile, cb), wtile(tile, cb + kChunkBlocks),
+                                        stile(tile, cb + kChunkBlocks), has_next, lo, pf, acc);
+            } else {
+                run_tail_chunk<FMT>(T, D1, wtile(tile, cb), stile(tile, cb), lo, nbc, acc);
+            }
         }
     }
-    if (active) {
-        const int row = tile * kTileRows + lane;
-        const float y = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
-        if (row < g.rows)
-            g.y[row] = y;
-    }
+    if (active)
+        store_row(g, tile, lane, acc);
 }
 
 template <int FMT, int QA>
-__global__ __launch_bounds__(kThreads) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int tiles)
+__global__ __launch_bounds__(kThreads) BQ_KATTR void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int tiles)
 {
     __shared__ float T[kTableFloats];
     __shared__ float D1[kScaleFloats];
@@ -339,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(GemvDesc g, int64_t ld
 }
 
 template <int FMT, int QA>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(const GemvDesc *__restrict__ descs,
+__global__ __launch_bounds__(kThreads) BQ_KATTR void sweep_kernel(const GemvDesc *__restrict__ descs,
                                                          const WorkItem *__restrict__ items)
 {
     __shared__ float T[kTableFloats];
@@ -534,7 +717,6 @@ BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **pla
     const int fmt = list[0].w.fmt, qa = list[0].a.qa;
     std::vector<GemvDesc> descs((size_t)count);
     std::vector<WorkItem> items;
-    std::vector<int64_t> cost;
     for (int i = 0; i < count; ++i) {
         const bq_gemv &e = list[i];
         char where[96];
@@ -552,28 +734,40 @@ BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **pla
             return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
         descs[(size_t)i] = make_desc(&e.w, &e.a, e.y);
         const int tiles = (int)tiles_of(e.w.rows);
-        for (int t = 0; t < tiles; t += kWaves) {
+        const int per_item = descs[(size_t)i].nb <= kChunkBlocks ? kWaves * kMaxRounds : kWaves;
+        for (int t = 0; t < tiles; t += per_item) {
             WorkItem it;
             it.gemv = i;
             it.tile0 = t;
-            it.ntiles = std::min(kWaves, tiles - t);
+            it.ntiles = std::min(per_item, tiles - t);
             it.pad = 0;
             items.push_back(it);
         }
     }
     // Most work first: the hardware dispatches workgroups in order, so the
-    // short items fill the tail.
-    std::vector<size_t> order(items.size());
-    for (size_t i = 0; i < order.size(); ++i)
-        order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
-        const int64_t ca = (int64_t)items[a].ntiles * descs[(size_t)items[a].gemv].nb;
-        const int64_t cb = (int64_t)items[b].ntiles * descs[(size_t)items[b].gemv].nb;
-        return ca > cb;
-    });
-    std::vector<WorkItem> sorted(items.size());
-    for (size_t i = 0; i < order.size(); ++i)
-        sorted[i] = items[order[i]];
+    // short items fill the tail.  The last kTailItems are cut to one tile per
+    // wavefront.
+    auto cost = [&](const WorkItem &w) { return (int64_t)w.ntiles * descs[(size_t)w.gemv].nb; };
+    auto by_cost = [&](const WorkItem &a, const WorkItem &b) { return cost(a) > cost(b); };
+    std::stable_sort(items.begin(), items.end(), by_cost);
+    std::vector<WorkItem> tail;
+    size_t head = items.size();
+    while (head > 0 && tail.size() < (size_t)kTailItems) {
+        const WorkItem w = items[--head];
+        if (descs[(size_t)w.gemv].nb > kChunkBlocks || w.ntiles <= kWaves) {
+            tail.push_back(w);
+            continue;
+        }
+        for (int t = 0; t < w.ntiles; t += kWaves) {
+            WorkItem piece = w;
+            piece.tile0 = w.tile0 + t;
+            piece.ntiles = std::min(kWaves, w.ntiles - t);
+            tail.push_back(piece);
+        }
+    }
+    std::stable_sort(tail.begin(), tail.end(), by_cost);
+    std::vector<WorkItem> sorted(items.begin(), items.begin() + (ptrdiff_t)head);
+    sorted.insert(sorted.end(), tail.begin(), tail.end());
 
     const size_t dbytes = descs.size() * sizeof(GemvDesc);
     const size_t ibytes = sorted.size() * sizeof(WorkItem);
