@@ -532,6 +532,207 @@ __global__ __launch_bounds__(kThreads) BQ_KATTR void sweep_kernel(const GemvDesc
     run_item<FMT, QA>(g, it.tile0, it.ntiles, T, D1);
 }
 
+// ------------------------------------------------------------ small batch
+// ncols in [2, 16] activation columns against one matrix.  Lane 8r + L of a
+// wavefront owns lane group L of row r, so each lane carries one f32 chain
+// per column; a wavefront covers kBatchRowGroups groups of 8 rows, a
+// workgroup 8 wavefronts.  A workgroup takes at most 4 columns; the column
+// groups of one row block are launched on one XCD (workgroup ids 8 apart), so
+// the weights come from HBM once and from that XCD's L2 for the other column
+// groups.
+//
+// The integer lane-group sums come from v_dot4: the lane's 4 weights are
+// widened to four bytes by a small LDS table, and each column's 4 activation
+// bytes come from an LDS copy of the chunk's activations.
+// Q1_0: s = dot4(w, q) with the weights widened to +1/-1 bytes, as long as
+// no activation byte of the chunk is -128.  Otherwise the wrap of int8
+// negation (-(-128) = -128) is kept by a second form: with b_i the sign bits,
+// P_i = b_i ? q_i : wrap8(-q_i) = wrap8(-q_i) + 2 b_i q'_i, where q'_i = q_i
+// except q'_i = 0 for q_i = -128, so s = dot4(2b, q') + sum_i wrap8(-q_i),
+// exact in int32, with the second term staged per lane group.
+// Q2_0: s = dot4(c - 1, q) (no wrap).
+constexpr int kBatchWaves = 8;
+constexpr int kBatchThreads = kBatchWaves * 64;
+constexpr int kBatchRowGroups = 2;                                     // 8-row groups per wavefront
+constexpr int kBatchRows = kBatchWaves * 8 * kBatchRowGroups;          // 128 rows per workgroup
+constexpr int kBatchValues = 1024;                                     // activation values per chunk
+constexpr int kBatchCols = 4;                                          // columns per workgroup
+
+template <int FMT>
+struct BatchShape {
+    static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;  // values per block
+    static constexpr int SUB = BL / 32;                   // sub-blocks per block
+    static constexpr int CB = kBatchValues / BL;          // blocks per chunk
+    static constexpr int GROUPS = CB * SUB * 8;           // lane groups per chunk
+};
+
+// Row block and column group of this workgroup.  The launch has 8 * ceil(rb/8)
+// * cgroups workgroups; ids that differ by a multiple of 8 share an XCD.
+__device__ __forceinline__ void batch_place(int cgroups, int &rb, int &cg)
+{
+    const int id = blockIdx.x, slot = id & 7, rest = id >> 3;
+    cg = rest % cgroups;
+    rb = (rest / cgroups) * 8 + slot;
+}
+
+template <int FMT, int QA, int NC>
+__global__ __launch_bounds__(kBatchThreads) void batch_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int ncols,
+                                                              int cgroups)
+{
+    using S = BatchShape<FMT>;
+    constexpr int NW = FMT == BQ_Q1_0 ? S::GROUPS * NC : 1;
+    __shared__ int32_t Y[S::GROUPS * NC];  // [block][sub][L][column]: activation bytes
+    __shared__ int32_t YW[NW];             // Q1_0: the bytes with -128 replaced by 0
+    __shared__ int32_t Z[NW];              // Q1_0: sum of wrap8(-q) per lane group
+    __shared__ float DS[S::CB * S::SUB * NC];          // [block][sub][column]: activation scales
+    __shared__ uint32_t X[FMT == BQ_Q1_0 ? 32 : 256];  // widening tables (Q1_0: +-1 bytes, then 2b bytes)
+    __shared__ int any_min;                            // some q == -128 in this chunk (Q1_0)
+
+    int rb, cg;
+    batch_place(cgroups, rb, cg);
+    const int row0 = rb * kBatchRows;
+    if (row0 >= g.rows)
+        return;  // padding workgroup (the grid is a multiple of 8 row blocks)
+    const int c0 = cg * NC;
+    const int nc = min(NC, ncols - c0);
+    const int8_t *q = g.q + c0 * ld_q;
+    const float *d = g.d + c0 * ld_d;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int L = lane & 7;
+    int rows[kBatchRowGroups];
+    bool live[kBatchRowGroups];  // the 8-row group starts inside the matrix (so inside its tiles)
+    rsrc_t wr[kBatchRowGroups], sr[kBatchRowGroups];
+    uint32_t lo[kBatchRowGroups];
+#pragma unroll
+    for (int k = 0; k < kBatchRowGroups; ++k) {
+        const int rbase = row0 + (wave * kBatchRowGroups + k) * 8;  // wave-uniform, a multiple of 8
+        live[k] = rbase < g.rows;
+        const int tile = live[k] ? rbase / kTileRows : 0;
+        rows[k] = rbase + (lane >> 3);
+        wr[k] = rsrc_of(g.bits + (int64_t)tile * g.nb * kTileRows);
+        sr[k] = rsrc_of(g.scales + (int64_t)tile * g.ng * kTileRows);
+        lo[k] = (uint32_t)(rows[k] % kTileRows) * 16;
+    }
+
+    for (int i = threadIdx.x; i < (FMT == BQ_Q1_0 ? 32 : 256); i += blockDim.x) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t byte;
+            if (FMT == BQ_Q1_0)
+                byte = i < 16 ? (((i >> e) & 1) ? 0x01u : 0xFFu) : ((i >> e) & 1) * 2u;
+            else
+                byte = (uint32_t)(uint8_t)(((i >> (2 * e)) & 3) - 1);
+            v |= byte << (8 * e);
+        }
+        X[i] = v;
+    }
+
+    float acc[kBatchRowGroups][NC];
+#pragma unroll
+    for (int k = 0; k < kBatchRowGroups; ++k)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            acc[k][c] = 0.0f;
+
+    for (int cb = 0; cb < g.nb; cb += S::CB) {
+        const int nbc = min(S::CB, g.nb - cb);
+        const int k0 = cb * S::BL;
+        __syncthreads();  // the previous chunk's copies are no longer read
+        if (threadIdx.x == 0)
+            any_min = 0;
+        __syncthreads();
+        int saw_min = 0;
+        for (int i = threadIdx.x; i < S::GROUPS * NC; i += blockDim.x) {
+            const int c = i % NC, grp = i / NC;  // grp = (block * SUB + sub) * 8 + L
+            const int blk = grp / (S::SUB * 8);
+            uint32_t y = 0, yw = 0;
+            int32_t z = 0;
+            if (c < nc && blk < nbc) {
+                y = *reinterpret_cast<const uint32_t *>(q + c * ld_q + k0 + 4 * grp);
+                if (FMT == BQ_Q1_0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = (int8_t)(y >> (8 * e));
+                        z += v == -128 ? -128 : -v;
+                        saw_min |= v == -128;
+                        yw |= (v == -128 ? 0u : (uint32_t)(uint8_t)v) << (8 * e);
+                    }
+                }
+            }
+            Y[i] = (int32_t)y;
+            if (FMT == BQ_Q1_0) {
+                YW[i] = (int32_t)yw;
+                Z[i] = z;
+            }
+        }
+        for (int i = threadIdx.x; i < S::CB * S::SUB * NC; i += blockDim.x) {
+            const int c = i % NC, bs = i / NC;  // bs = block * SUB + sub
+            const int blk = bs / S::SUB;
+            DS[i] = (c < nc && blk < nbc) ? d[c * ld_d + (k0 + 32 * bs) / QA] : 0.0f;
+        }
+        if (FMT == BQ_Q1_0 && saw_min)
+            any_min = 1;  // every writer stores 1
+        __syncthreads();
+        const bool wrap = FMT == BQ_Q1_0 && any_min;
+
+        for (int blk = 0; blk < nbc; ++blk) {
+            const int b = cb + blk;
+#pragma unroll
+            for (int k = 0; k < kBatchRowGroups; ++k) {
+                if (!live[k])
+                    continue;
+                const u32x4 w = bload(wr[k], lo[k], (uint32_t)b * kStep);
+                const u32x4 scv = bload(sr[k], lo[k], (uint32_t)(b / 8) * kStep);
+                float d0 = scale_of(scv, b);
+                asm volatile("" : "+v"(d0));
+                float ab[NC];
+#pragma unroll
+                for (int j = 0; j < S::SUB; ++j) {
+                    uint32_t a4;
+                    if (FMT == BQ_Q1_0) {
+                        a4 = __builtin_amdgcn_alignbit(w[j], w[j], 4 * L) & 0x3Cu;
+                    } else {
+                        const uint32_t wj = (L & 4) ? w[2 * j + 1] : w[2 * j];
+                        a4 = __builtin_amdgcn_alignbit(wj, wj, 8 * (L & 3)) & 0x3FCu;
+                    }
+                    const int32_t xw = (int32_t)X[(a4 >> 2) + (wrap ? 16 : 0)];
+                    const int gbase = ((blk * S::SUB + j) * 8 + L) * NC;
+                    const int dbase = (blk * S::SUB + j) * NC;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        int32_t sv;
+                        if (FMT == BQ_Q1_0 && wrap)
+                            sv = __builtin_amdgcn_sdot4(xw, YW[gbase + c], Z[gbase + c], false);
+                        else
+                            sv = __builtin_amdgcn_sdot4(xw, Y[gbase + c], 0, false);
+                        const float t = (float)sv;
+                        const float d1 = DS[dbase + c];
+                        ab[c] = j == 0 ? d1 * t : __builtin_fmaf(d1, t, ab[c]);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc[k][c] = __builtin_fmaf(d0, ab[c], acc[k][c]);
+            }
+        }
+    }
+
+    // y = ((a0+a4)+(a2+a6)) + ((a1+a5)+(a3+a7)) over the 8 lanes of the row
+#pragma unroll
+    for (int k = 0; k < kBatchRowGroups; ++k)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float v = acc[k][c];
+            v = v + __shfl_xor(v, 4, 64);
+            v = v + __shfl_xor(v, 2, 64);
+            v = v + __shfl_xor(v, 1, 64);
+            if (L == 0 && c < nc && rows[k] < g.rows)
+                g.y[(int64_t)(c0 + c) * g.rows + rows[k]] = v;
+        }
+}
+
 // ------------------------------------------------------------ quantizer
 // Each thread quantizes 4 consecutive values; QA/4 threads share a block and
 // combine their |x| maxima with butterfly shuffles (max is exact in any order).
@@ -648,8 +849,30 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
         return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", fn);
     const GemvDesc g = make_desc(w, a, y);
     const int tiles = (int)tiles_of(w->rows);
-    const dim3 grid((tiles + kWaves - 1) / kWaves, a->ncols);
     hipStream_t st = static_cast<hipStream_t>(s);
+    if (a->ncols > 1) {
+        const int nc = a->ncols;
+        const int per = nc <= 2 ? 2 : kBatchCols;
+        const int cgroups = (nc + per - 1) / per;
+        const int64_t rblocks = (w->rows + kBatchRows - 1) / kBatchRows;
+        const dim3 grid((unsigned)(((rblocks + 7) / 8) * 8 * cgroups));
+#define BQ_BATCH(NC)                                                                                           \
+    do {                                                                                                        \
+        if (a->qa == 32)                                                                                        \
+            hipLaunchKernelGGL((batch_kernel<FMT, 32, NC>), grid, dim3(kBatchThreads), 0, st, g, a->ld_q, a->ld_d, nc, cgroups); \
+        else if (a->qa == 64)                                                                                   \
+            hipLaunchKernelGGL((batch_kernel<FMT, 64, NC>), grid, dim3(kBatchThreads), 0, st, g, a->ld_q, a->ld_d, nc, cgroups); \
+        else                                                                                                    \
+            hipLaunchKernelGGL((batch_kernel<FMT, 128, NC>), grid, dim3(kBatchThreads), 0, st, g, a->ld_q, a->ld_d, nc, cgroups); \
+    } while (0)
+        if (per == 2)
+            BQ_BATCH(2);
+        else
+            BQ_BATCH(kBatchCols);
+#undef BQ_BATCH
+        return hip_check(fn, hipGetLastError());
+    }
+    const dim3 grid((tiles + kWaves - 1) / kWaves, 1);
     switch (a->qa) {
     case 32: hipLaunchKernelGGL((matvec_kernel<FMT, 32>), grid, dim3(kThreads), 0, st, g, a->ld_q, a->ld_d, tiles); break;
     case 64: hipLaunchKernelGGL((matvec_kernel<FMT, 64>), grid, dim3(kThreads), 0, st, g, a->ld_q, a->ld_d, tiles); break;

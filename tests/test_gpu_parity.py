@@ -125,6 +125,37 @@ def test_matvec_columns(fmt, ncols):
     assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, f"columns fmt={fmt} ncols={ncols}")
 
 
+def _batch_cases():
+    out = []
+    for fmt in (Q1, Q2):
+        for rows, nb in ((100, 33), (72, 17), (64, 8), (129, 9)):
+            for ncols in (2, 3, 5, 8, 16):
+                for qa, regime in ((128, "quant"), (32, "raw"), (64, "raw"), (64, "mixed")):
+                    if (nb * QK[fmt]) % qa == 0:
+                        out.append((fmt, rows, nb * QK[fmt], ncols, qa, regime))
+    return out
+
+
+@pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", _batch_cases())
+def test_small_batch_parity(fmt, rows, cols, ncols, qa, regime):
+    """Several activation columns against one matrix (weights read once); the raw
+    regime plants q = -128, which exercises the wrap of int8 negation in Q1_0."""
+    name = f"batch fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
+    log(name)
+    w = synth.blocks(fmt, rows, cols, rows + ncols)
+    if regime in ("raw", "mixed"):
+        qs, ds = zip(*[synth.raw_q8(cols, qa, 7 * c + rows, force_min=regime == "raw") for c in range(ncols)])
+        if regime == "mixed":  # one -128 in the first and in the last 1024 values of column ncols-1 only
+            qs = [q.copy() for q in qs]
+            qs[-1][5] = -128
+            qs[-1][cols - 3] = -128
+    else:
+        qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, rows, c), qa)[:2] for c in range(ncols)])
+    q, d = np.stack(qs), np.stack(ds)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
+
+
 # ------------------------------------------------- full-size single products
 FULL = [
     (Q1, 4096, 4096), (Q1, 12288, 4096), (Q1, 4096, 12288), (Q1, 151936, 4096),
@@ -145,17 +176,17 @@ def test_matvec_full_size(fmt, rows, cols):
     assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, 128), y_ref, name)
 
 
-@pytest.mark.parametrize("rows", [12288, 151936])
-def test_small_batch_full_size(rows):
+@pytest.mark.parametrize("fmt,rows", [(Q1, 12288), (Q1, 151936), (Q2, 12288)])
+def test_small_batch_full_size(fmt, rows):
     cols, qa = 4096, 128
-    w = synth.q1_0_blocks(rows, cols, 51, rows)
+    w = synth.blocks(fmt, rows, cols, 51, rows)
     for ncols in (1, 4, 8, 16):
-        name = f"small batch Q1_0 {rows}x{cols} N={ncols}"
+        name = f"small batch fmt={fmt} {rows}x{cols} N={ncols}"
         log(name)
         qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 51, c), qa)[:2] for c in range(ncols)])
         q, d = np.stack(qs), np.stack(ds)
-        y_ref = oracle.matvec(Q1, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
-        assert_parity(matvec_gpu(Q1, w, rows, cols, q, d, qa), y_ref, name)
+        y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+        assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
 
 
 # ------------------------------------------------------------ token sweeps
