@@ -12,8 +12,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbq.so")
-SOURCES = [os.path.join(CSRC, "bq_kernels.hip"), os.path.join(CSRC, "bq_pack.cpp")]
-HEADERS = [os.path.join(CSRC, "bq_layout.h"), os.path.join(ROOT, "include", "bq.h")]
+SOURCES = [os.path.join(CSRC, f) for f in ("bq_sweep.hip", "bq_split.hip", "bq_batch.hip", "bq_quantize.hip",
+                                            "bq_api.cpp", "bq_pack.cpp")]
+HEADERS = [os.path.join(CSRC, f) for f in ("bq_layout.h", "bq_types.h", "bq_device.h")] + [os.path.join(ROOT, "include", "bq.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -53,10 +54,10 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def asm(out: str) -> str:
-    """Device assembly of the kernels (for inspection)."""
+def asm(out: str, source: str = "bq_sweep.hip") -> str:
+    """Device assembly of the kernels of one source file (for inspection)."""
     cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only", "-S",
-           "-o", out, SOURCES[0]]
+           "-o", out, os.path.join(CSRC, source)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out
 

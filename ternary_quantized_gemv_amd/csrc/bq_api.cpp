@@ -1,0 +1,259 @@
+// bq_api.cpp -- the GPU entry points of the C ABI (include/bq.h): argument
+// checks (before any launch; errors are return codes plus a thread-local
+// message naming the call), the choice of kernel, and sweep plans.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/bq.h"
+#include "bq_layout.h"
+#include "bq_types.h"
+
+namespace bq {
+
+// ------------------------------------------------------------ validation
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static int hip_check(const char *fn, hipError_t e)
+{
+    if (e != hipSuccess)
+        return set_error(BQ_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    return BQ_OK;
+}
+
+static int check_weights(const char *fn, const bq_weights *w, int fmt)
+{
+    if (!w)
+        return set_error(BQ_EARG, "%s: null weights", fn);
+    if (w->fmt != fmt)
+        return set_error(BQ_EARG, "%s: weights format %d, expected %d", fn, (int)w->fmt, fmt);
+    if (w->reserved != 0)
+        return set_error(BQ_EARG, "%s: weights.reserved must be 0", fn);
+    if (w->rows < 1 || w->rows >= (int64_t(1) << 31) || w->cols < 1 || w->cols >= (int64_t(1) << 31))
+        return set_error(BQ_EARG, "%s: rows %lld / cols %lld out of range", fn, (long long)w->rows,
+                         (long long)w->cols);
+    if (w->cols % block_len(fmt))
+        return set_error(BQ_EARG, "%s: cols %lld not a multiple of %d", fn, (long long)w->cols, block_len(fmt));
+    if (!w->bits || !w->scales)
+        return set_error(BQ_EARG, "%s: null weight plane", fn);
+    if (!aligned(w->bits, 16) || !aligned(w->scales, 16))
+        return set_error(BQ_EALIGN, "%s: weight planes must be 16-byte aligned", fn);
+    return BQ_OK;
+}
+
+static int check_act(const char *fn, const bq_act *a, int64_t cols, int max_cols)
+{
+    if (!a)
+        return set_error(BQ_EARG, "%s: null activation", fn);
+    if (a->n != cols)
+        return set_error(BQ_EARG, "%s: activation length %lld != weight cols %lld", fn, (long long)a->n,
+                         (long long)cols);
+    if (a->qa != 32 && a->qa != 64 && a->qa != 128)
+        return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)a->qa);
+    if (a->n % a->qa)
+        return set_error(BQ_EARG, "%s: n %lld not a multiple of qa %d", fn, (long long)a->n, (int)a->qa);
+    if (a->ncols < 1 || a->ncols > max_cols)
+        return set_error(BQ_EARG, "%s: ncols %d not in [1, %d]", fn, (int)a->ncols, max_cols);
+    if (!a->q || !a->d)
+        return set_error(BQ_EARG, "%s: null activation pointer", fn);
+    if (a->ncols > 1 && (a->ld_q < a->n || a->ld_d < a->n / a->qa))
+        return set_error(BQ_EARG, "%s: leading dimensions too small", fn);
+    if (!aligned(a->q, 16) || (a->ncols > 1 && a->ld_q % 16) || !aligned(a->d, 4))
+        return set_error(BQ_EALIGN, "%s: q must be 16-byte aligned (ld_q a multiple of 16), d 4-byte aligned", fn);
+    return BQ_OK;
+}
+
+static GemvDesc make_desc(const bq_weights *w, const bq_act *a, float *y)
+{
+    GemvDesc g;
+    memset(&g, 0, sizeof g);
+    const int64_t nb = w->cols / block_len(w->fmt);
+    g.bits = static_cast<const u32x4 *>(w->bits);
+    g.scales = reinterpret_cast<const u32x4 *>(w->scales);
+    g.q = a->q;
+    g.d = a->d;
+    g.y = y;
+    g.rows = (int32_t)w->rows;
+    g.nb = (int32_t)nb;
+    g.ng = (int32_t)groups_of(nb);
+    return g;
+}
+
+template <int FMT>
+static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, float *y, bq_stream s)
+{
+    int rc = check_weights(fn, w, FMT);
+    if (!rc)
+        rc = check_act(fn, a, w->cols, 16);
+    if (rc)
+        return rc;
+    if (!y)
+        return set_error(BQ_EARG, "%s: null y", fn);
+    if (!aligned(y, 4))
+        return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", fn);
+    const GemvDesc g = make_desc(w, a, y);
+    const int tiles = (int)tiles_of(w->rows);
+    hipStream_t st = static_cast<hipStream_t>(s);
+    hipError_t e;
+    if (a->ncols >= kMfMinCols)
+        e = launch_batch(FMT, a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
+    else if (tiles <= kSplitMaxTiles)
+        e = launch_split(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
+    else
+        e = launch_rows(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
+    return hip_check(fn, e);
+}
+
+}  // namespace bq
+
+using namespace bq;
+
+struct bq_sweep {
+    int fmt;
+    int qa;
+    int nitems;
+    int count;
+    void *dev;  // descriptors, then work items
+    const GemvDesc *descs;
+    const WorkItem *items;
+};
+
+BQ_EXPORT int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s)
+{
+    const char *fn = "bq_quantize_act_q8";
+    if (qa != 32 && qa != 64 && qa != 128)
+        return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)qa);
+    if (n < 0 || n % qa)
+        return set_error(BQ_EARG, "%s: n %lld is not a non-negative multiple of qa %d", fn, (long long)n, (int)qa);
+    if (!x || !q || !d)
+        return set_error(BQ_EARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4))
+        return set_error(BQ_EALIGN, "%s: x must be 16-byte aligned, q and d 4-byte aligned", fn);
+    if (n == 0)
+        return BQ_OK;
+    return hip_check(fn, launch_quantize(x, n, qa, q, d, static_cast<hipStream_t>(s)));
+}
+
+BQ_EXPORT int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
+{
+    return launch_matvec<BQ_Q1_0>("bq_q1_0_matvec", w, a, y, s);
+}
+
+BQ_EXPORT int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
+{
+    return launch_matvec<BQ_Q2_0>("bq_q2_0_matvec", w, a, y, s);
+}
+
+BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan)
+{
+    const char *fn = "bq_sweep_create";
+    if (!plan)
+        return set_error(BQ_EARG, "%s: null plan pointer", fn);
+    *plan = nullptr;
+    if (!list || count < 1)
+        return set_error(BQ_EARG, "%s: empty list", fn);
+    const int fmt = list[0].w.fmt, qa = list[0].a.qa;
+    std::vector<GemvDesc> descs((size_t)count);
+    std::vector<WorkItem> items;
+    for (int i = 0; i < count; ++i) {
+        const bq_gemv &e = list[i];
+        char where[96];
+        snprintf(where, sizeof where, "%s: entry %d", fn, i);
+        if (e.w.fmt != fmt || e.a.qa != qa)
+            return set_error(BQ_EARG, "%s: every entry must share the format and qa of entry 0", where);
+        int rc = check_weights(where, &e.w, fmt);
+        if (!rc)
+            rc = check_act(where, &e.a, e.w.cols, 1);
+        if (rc)
+            return rc;
+        if (!e.y)
+            return set_error(BQ_EARG, "%s: null y", where);
+        if (!aligned(e.y, 4))
+            return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
+        descs[(size_t)i] = make_desc(&e.w, &e.a, e.y);
+        const int tiles = (int)tiles_of(e.w.rows);
+        const int per_item = descs[(size_t)i].nb <= kChunkBlocks ? kWaves * kMaxRounds : kWaves;
+        for (int t = 0; t < tiles; t += per_item) {
+            WorkItem it;
+            it.gemv = i;
+            it.tile0 = t;
+            it.ntiles = std::min(per_item, tiles - t);
+            it.pad = 0;
+            items.push_back(it);
+        }
+    }
+    // Most work first: the hardware dispatches workgroups in order, so the
+    // short items fill the tail.  The last kTailItems are cut to one tile per
+    // wavefront.
+    auto cost = [&](const WorkItem &w) { return (int64_t)w.ntiles * descs[(size_t)w.gemv].nb; };
+    auto by_cost = [&](const WorkItem &a, const WorkItem &b) { return cost(a) > cost(b); };
+    std::stable_sort(items.begin(), items.end(), by_cost);
+    std::vector<WorkItem> tail;
+    size_t head = items.size();
+    while (head > 0 && tail.size() < (size_t)kTailItems) {
+        const WorkItem w = items[--head];
+        if (descs[(size_t)w.gemv].nb > kChunkBlocks || w.ntiles <= kWaves) {
+            tail.push_back(w);
+            continue;
+        }
+        for (int t = 0; t < w.ntiles; t += kWaves) {
+            WorkItem piece = w;
+            piece.tile0 = w.tile0 + t;
+            piece.ntiles = std::min(kWaves, w.ntiles - t);
+            tail.push_back(piece);
+        }
+    }
+    std::stable_sort(tail.begin(), tail.end(), by_cost);
+    std::vector<WorkItem> sorted(items.begin(), items.begin() + (ptrdiff_t)head);
+    sorted.insert(sorted.end(), tail.begin(), tail.end());
+
+    const size_t dbytes = descs.size() * sizeof(GemvDesc);
+    const size_t ibytes = sorted.size() * sizeof(WorkItem);
+    void *dev = nullptr;
+    if (hipMalloc(&dev, dbytes + ibytes) != hipSuccess)
+        return set_error(BQ_ENOMEM, "%s: hipMalloc of %zu bytes failed", fn, dbytes + ibytes);
+    hipError_t e = hipMemcpy(dev, descs.data(), dbytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(static_cast<char *>(dev) + dbytes, sorted.data(), ibytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(dev);
+        return set_error(BQ_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    }
+    bq_sweep *p = new (std::nothrow) bq_sweep;
+    if (!p) {
+        (void)hipFree(dev);
+        return set_error(BQ_ENOMEM, "%s: out of host memory", fn);
+    }
+    p->fmt = fmt;
+    p->qa = qa;
+    p->count = count;
+    p->nitems = (int)sorted.size();
+    p->dev = dev;
+    p->descs = static_cast<const GemvDesc *>(dev);
+    p->items = reinterpret_cast<const WorkItem *>(static_cast<char *>(dev) + dbytes);
+    *plan = p;
+    return BQ_OK;
+}
+
+BQ_EXPORT int bq_token_sweep(const bq_sweep *plan, bq_stream s)
+{
+    const char *fn = "bq_token_sweep";
+    if (!plan)
+        return set_error(BQ_EARG, "%s: null plan", fn);
+    return hip_check(fn, launch_sweep(plan->fmt, plan->qa, (unsigned)plan->nitems, plan->descs, plan->items,
+                                      static_cast<hipStream_t>(s)));
+}
+
+BQ_EXPORT void bq_sweep_destroy(bq_sweep *plan)
+{
+    if (!plan)
+        return;
+    (void)hipDeviceSynchronize();
+    (void)hipFree(plan->dev);
+    delete plan;
+}

@@ -1,0 +1,124 @@
+// bq_device.h -- internal to libbq: device helpers shared by the kernel
+// sources: buffer loads of the packed planes, f16 widening, and the LDS
+// nibble tables that turn an activation chunk into per-nibble partial sums.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/bq.h"
+#include "bq_types.h"
+
+namespace bq {
+
+typedef const float __attribute__((address_space(4))) *cfptr;
+
+// Weight planes are read through buffer resources: the wave-uniform base of
+// a tile sits in scalar registers, each lane adds its 16-byte offset, and the
+// block offset is a scalar constant, so a load costs no vector address math.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t rsrc_of(const u32x4 *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(base), (short)0, 0x7FFFFFF0, 0x00020000);
+}
+
+// 16 bytes at base + voff + soff, streamed (non-temporal).
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ float scale_of(u32x4 sc, int b)
+{
+    const uint32_t sw = sc[(b & 7) >> 1];
+    return f16_bits_to_f32((b & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+}
+
+// --------------------------------------------------------------- tables
+// Each thread writes one quarter (4 entries, 16 bytes) of a slot's table per
+// step, so a wavefront's stores cover 1 KiB of consecutive LDS addresses.
+//
+// Q1_0: slot t of a chunk covers chunk values 4t..4t+3 (block t/32, sub-block
+// (t/8)%4, lane t%8).  Entry n = 4h + e: s = sum_i (bit i of n ? q_i : -q_i),
+// where the negation of -128 stays -128; on sub-block 0 the entry is d1*s.
+template <int QA>
+__device__ void build_table_q1(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
+{
+    const int nquarters = nbc * kSlotsPerBlock * 4;
+    for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
+        const int t = u >> 2, h = u & 3;
+        const uint32_t w4 = *reinterpret_cast<const uint32_t *>(q + k0 + 4 * t);
+        int p1[4], p0[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int v = (int8_t)(w4 >> (8 * i));
+            p1[i] = v;
+            p0[i] = v == -128 ? -128 : -v;
+        }
+        const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
+        const bool first = ((t >> 3) & 3) == 0;
+        const float d1 = first ? d[(k0 + 4 * t) / QA] : 0.0f;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int lo = ((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]);
+            const float sf = (float)(lo + hi);
+            v[e] = first ? d1 * sf : sf;
+        }
+        reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
+    }
+    for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x)
+        D1[i] = d[(k0 + 32 * i) / QA];
+}
+
+// Q2_0: slot t of a chunk covers chunk values 2t and 2t+1 (the low or high
+// nibble of payload byte t/2 of its block).  Entry n = 4h + e holds the codes
+// (e, h): (e-1)*q_2t + (h-1)*q_2t+1.
+template <int QA>
+__device__ void build_table_q2(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
+{
+    const int nquarters = nbc * kSlotsPerBlock * 4;
+    for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
+        const int t = u >> 2, h = u & 3;
+        const uint32_t w2 = *reinterpret_cast<const uint16_t *>(q + k0 + 2 * t);
+        const int qa0 = (int8_t)(w2 & 0xFF), qa1 = (int8_t)(w2 >> 8);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
+        reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
+    }
+    // d1 per (block, sub-block): D1[4b + j], j = 0, 1.
+    for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x) {
+        const int b = i >> 2, j = i & 3;
+        D1[i] = j < 2 ? d[(k0 + 64 * b + 32 * j) / QA] : 0.0f;
+    }
+}
+
+// LDS read of entry (byte offset idx4 = nibble*4) of the table at slot `slot`.
+__device__ __forceinline__ float tab(const float *T, int slot, uint32_t idx4)
+{
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(T) + slot * (kSlotFloats * 4) + idx4);
+}
+
+// Byte m of w masked to bits 2..5: the byte offset of a nibble's table entry.
+// The compiler selects bytes 0, 2 and 3 with SDWA on its own; byte 1 is
+// spelled out so that it also costs a single instruction.
+__device__ __forceinline__ uint32_t nib4(uint32_t w, int m)
+{
+    if (m == 1) {
+        uint32_t r;
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+            : "=v"(r)
+            : "v"(w), "v"(0x3Cu));
+        return r;
+    }
+    return (w >> (8 * m)) & 0x3Cu;
+}
+
+}  // namespace bq

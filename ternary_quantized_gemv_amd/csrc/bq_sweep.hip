@@ -1,0 +1,374 @@
+// bq_sweep.hip -- the one-row-per-lane kernels: a single product
+// (matvec_kernel, one grid row per activation column) and the sweep of many
+// products in one launch (sweep_kernel).
+//
+// How the work maps onto CDNA4
+// ----------------------------
+// * One wavefront owns 64 rows (lane i = row 64t+i) and carries all eight
+//   lane accumulators of its row in registers.  Rows never split across
+//   threads, so the result does not depend on the grid.
+// * The weights stream from HBM once: per block each lane issues one 16-byte
+//   load of its row's payload, and the layout (bq_layout.h) makes the 64
+//   loads of a wavefront one contiguous KiB.  Loads run kPrefetch blocks
+//   ahead of the arithmetic.
+// * The activation never meets the weights as bytes.  For each group of
+//   weights that shares one 4-bit nibble of packed weights (Q1_0: 4 signs;
+//   Q2_0: 2 codes) the workgroup first tabulates, in LDS, the partial sum for
+//   all 16 nibble values (exact small integers held as floats; for Q1_0's
+//   first sub-block the table already holds the rounded product d1*s, which
+//   is the same single rounding the order prescribes).  The inner loop is
+//   then: byte-select the nibble (SDWA), one LDS read, one fma.  All 64
+//   lanes of a wavefront read the same 16-entry table, so reads never
+//   conflict on LDS banks.
+// * A table covers a chunk of 32 blocks (64 KiB); longer rows walk several
+//   chunks, rebuilding the table between barriers while the accumulators
+//   stay in registers.
+// * The sweep runs all products of a decode token in one launch: one
+//   workgroup per work item (up to 8 tiles of one matrix), ordered from the
+//   most to the least work so the hardware's in-order dispatch balances the
+//   GPU.
+#include "bq_device.h"
+
+namespace bq {
+
+// ------------------------------------------------------- activation scales
+// d1 of the four sub-blocks of block b of a chunk.  When a full chunk has at
+// most 32 distinct activation scales they sit in scalar registers for the
+// whole chunk (loaded once, wave-uniform); otherwise they are read from the
+// chunk's LDS copy.
+template <int FMT, int QA>
+struct ChunkScales {
+    static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
+    static constexpr int ND = kChunkBlocks * BL / QA;
+    static constexpr bool kScalar = ND <= 32;
+    float dv[kScalar ? ND : 1];
+
+    __device__ __forceinline__ void load(const float *d_chunk)
+    {
+        if (kScalar) {
+            // the address is wave-uniform; say so, so that the loads are scalar
+            const uint64_t a = (uint64_t)d_chunk;
+            const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+            const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+            const cfptr gc = (cfptr)(const float *)((hi << 32) | lo);
+#pragma unroll
+            for (int i = 0; i < (kScalar ? ND : 1); ++i) {
+                dv[i] = gc[i];
+                asm volatile("" : "+s"(dv[i]));  // load all of them here, once per chunk
+            }
+        }
+    }
+
+    __device__ __forceinline__ f32x4 get(const float *__restrict__ D1, int b) const
+    {
+        f32x4 r;
+        if (kScalar) {
+            constexpr int sub = FMT == BQ_Q1_0 ? 4 : 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r[j] = j < sub ? dv[((BL * b + 32 * j) / QA) % (kScalar ? ND : 1)] : 0.0f;
+        } else {
+            r = *reinterpret_cast<const f32x4 *>(D1 + 4 * b);
+        }
+        return r;
+    }
+};
+
+// ------------------------------------------------------------ block math
+// The eight lane chains of one block of the calling lane's row.  `b` is the
+// block's index inside the table chunk; v its four payload words; d0 its
+// widened scale.
+template <int FMT>
+__device__ __forceinline__ void block_math(const float *__restrict__ T, const f32x4 d1, int b, u32x4 v, float d0,
+                                           float acc[8])
+{
+    float ab[8];
+    if (FMT == BQ_Q1_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t wa = v[j];
+            const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+#pragma unroll
+            for (int L = 0; L < 8; ++L) {
+                const uint32_t idx = nib4((L & 1) ? wb : wa, L >> 1);
+                const float t = tab(T, b * kSlotsPerBlock + j * 8 + L, idx);
+                ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t wa = v[m];
+            const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+            const int j = m >> 1;
+#pragma unroll
+            for (int beta = 0; beta < 4; ++beta) {
+                const int L = 4 * (m & 1) + beta;
+                const int slot = b * kSlotsPerBlock + m * 8 + 2 * beta;
+                const float s = tab(T, slot, nib4(wa, beta)) + tab(T, slot + 1, nib4(wb, beta));
+                ab[L] = j == 0 ? d1[0] * s : __builtin_fmaf(d1[1], s, ab[L]);
+            }
+        }
+    }
+#pragma unroll
+    for (int L = 0; L < 8; ++L) {
+        acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
+        asm volatile("" : "+v"(acc[L]));  // keep each block's chain inside its own code
+    }
+}
+
+// The eight table reads of sub-block j of a Q1_0 block.
+__device__ __forceinline__ void lookups_q1(const float *__restrict__ T, int b, int j, uint32_t wa, float t[8])
+{
+    const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+#pragma unroll
+    for (int L = 0; L < 8; ++L)
+        t[L] = tab(T, b * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1));
+}
+
+// Payload words of the first kPrefetch blocks of a full chunk, plus its first
+// two scale groups.
+struct Prefetch {
+    u32x4 buf[kPrefetch];
+    u32x4 sc0, sc1;
+};
+
+__device__ __forceinline__ void prefetch_chunk(Prefetch &pf, rsrc_t w, rsrc_t sc, uint32_t lo)
+{
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i)
+        pf.buf[i] = bload(w, lo, i * kStep);
+    pf.sc0 = bload(sc, lo, 0);
+    pf.sc1 = bload(sc, lo, kStep);
+}
+
+// A full chunk of 32 blocks.  Loads run kPrefetch blocks ahead; the last
+// iterations already load the first blocks and scale groups of the next full
+// chunk this wavefront will run (wn, sn), if has_next.  Every index is a
+// compile-time constant, so each table read carries its slot as an immediate
+// LDS offset.  For Q1_0 the table reads of block b+1 are issued, sub-block by
+// sub-block, between the fma steps of block b.
+template <int FMT, int QA>
+__device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, const float *__restrict__ D1,
+                                               const ChunkScales<FMT, QA> &cs, rsrc_t wp, rsrc_t sp, rsrc_t wn,
+                                               rsrc_t sn, bool has_next, uint32_t lo, Prefetch &pf, float acc[8])
+{
+    u32x4 sc = pf.sc0, sc_next = pf.sc1;
+    float tc[32], tn[32];
+    if (FMT == BQ_Q1_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lookups_q1(T, 0, j, pf.buf[0][j], tc + 8 * j);
+    }
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+        if ((b & 7) == 0 && b > 0) {
+            sc = sc_next;
+            if (b / 8 + 1 < kChunkBlocks / 8)
+                sc_next = bload(sp, lo, (b / 8 + 1) * kStep);
+            else if (has_next)
+                sc_next = bload(sn, lo, 0);
+        }
+        const u32x4 v = pf.buf[b % kPrefetch];
+        if (b + kPrefetch < kChunkBlocks)
+            pf.buf[b % kPrefetch] = bload(wp, lo, (b + kPrefetch) * kStep);
+        else if (has_next)
+            pf.buf[b % kPrefetch] = bload(wn, lo, (b + kPrefetch - kChunkBlocks) * kStep);
+        const f32x4 d1 = cs.get(D1, b);
+        float d0 = scale_of(sc, b);
+        // widen once: eight v_fmac_f32 then run at full rate, where v_fma_mix_f32
+        // (the compiler's choice for an f16 operand) runs at half rate
+        asm volatile("" : "+v"(d0));
+        if (FMT == BQ_Q1_0) {
+            const u32x4 vn = pf.buf[(b + 1) % kPrefetch];
+            float ab[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (b + 1 < kChunkBlocks)
+                    lookups_q1(T, b + 1, j, vn[j], tn + 8 * j);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int L = 0; L < 8; ++L)
+                    ab[L] = j == 0 ? tc[L] : __builtin_fmaf(d1[j], tc[8 * j + L], ab[L]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int L = 0; L < 8; ++L) {
+                acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
+                asm volatile("" : "+v"(acc[L]));
+            }
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                tc[i] = tn[i];
+        } else {
+            block_math<FMT>(T, d1, b, v, d0, acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    pf.sc0 = sc_next;
+    if (has_next)
+        pf.sc1 = bload(sn, lo, kStep);
+}
+
+// A partial chunk (rows whose length is not a multiple of 32 blocks): plain
+// loop, no prefetch.
+template <int FMT>
+__device__ void run_tail_chunk(const float *__restrict__ T, const float *__restrict__ D1, rsrc_t wp, rsrc_t sp,
+                               uint32_t lo, int nbc, float acc[8])
+{
+    for (int b = 0; b < nbc; ++b) {
+        const u32x4 v = bload(wp, lo, b * kStep);
+        const u32x4 sc = bload(sp, lo, (b / 8) * kStep);
+        block_math<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * b), b, v, scale_of(sc, b), acc);
+    }
+}
+
+__device__ __forceinline__ void store_row(const GemvDesc &g, int tile, int lane, const float acc[8])
+{
+    const int row = tile * kTileRows + lane;
+    const float y = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
+    if (row < g.rows)
+        g.y[row] = y;
+}
+
+// Rows [64*tile0, 64*(tile0+ntiles)) of one product; wavefront w takes tiles
+// tile0 + w, tile0 + w + kWaves, ...  Rows of at most one chunk share one
+// table for every tile of the item; longer rows (ntiles <= kWaves) walk the
+// chunks with a table rebuild between barriers.
+template <int FMT, int QA>
+__device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1)
+{
+    // the wavefront index is wave-uniform: say so, so that tile addresses live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int per_chunk = FMT == BQ_Q1_0 ? 128 * kChunkBlocks : 64 * kChunkBlocks;
+    const int tend = tile0 + ntiles;
+    const uint32_t lo = (uint32_t)lane * 16;
+    auto wtile = [&](int tile, int cb) { return rsrc_of(g.bits + ((int64_t)tile * g.nb + cb) * kTileRows); };
+    auto stile = [&](int tile, int cb) { return rsrc_of(g.scales + ((int64_t)tile * g.ng + cb / 8) * kTileRows); };
+    float acc[8];
+    Prefetch pf;
+
+    if (g.nb <= kChunkBlocks) {
+        const int nbc = g.nb;
+        int tile = tile0 + wave;
+        if (tile < tend && nbc == kChunkBlocks)
+            prefetch_chunk(pf, wtile(tile, 0), stile(tile, 0), lo);
+        if (FMT == BQ_Q1_0)
+            build_table_q1<QA>(T, D1, g.q, g.d, 0, nbc);
+        else
+            build_table_q2<QA>(T, D1, g.q, g.d, 0, nbc);
+        __syncthreads();
+        ChunkScales<FMT, QA> cs;
+        if (nbc == kChunkBlocks)
+            cs.load(g.d);
+        for (; tile < tend; tile += kWaves) {
+#pragma unroll
+            for (int L = 0; L < 8; ++L)
+                acc[L] = 0.0f;
+            const bool has_next = tile + kWaves < tend;
+            if (nbc == kChunkBlocks)
+                run_full_chunk<FMT, QA>(T, D1, cs, wtile(tile, 0), stile(tile, 0), wtile(tile + kWaves, 0),
+                                        stile(tile + kWaves, 0), has_next, lo, pf, acc);
+            else
+                run_tail_chunk<FMT>(T, D1, wtile(tile, 0), stile(tile, 0), lo, nbc, acc);
+            store_row(g, tile, lane, acc);
+        }
+        return;
+    }
+
+    const int tile = tile0 + wave;
+    const bool active = tile < tend;
+#pragma unroll
+    for (int L = 0; L < 8; ++L)
+        acc[L] = 0.0f;
+    if (active)
+        prefetch_chunk(pf, wtile(tile, 0), stile(tile, 0), lo);
+    for (int cb = 0; cb < g.nb; cb += kChunkBlocks) {
+        const int nbc = min(kChunkBlocks, g.nb - cb);
+        const int k0 = (cb / kChunkBlocks) * per_chunk;
+        if (cb > 0)
+            __syncthreads();  // every wavefront is done with the previous table
+        if (FMT == BQ_Q1_0)
+            build_table_q1<QA>(T, D1, g.q, g.d, k0, nbc);
+        else
+            build_table_q2<QA>(T, D1, g.q, g.d, k0, nbc);
+        __syncthreads();
+        if (active) {
+            if (nbc == kChunkBlocks) {
+                ChunkScales<FMT, QA> cs;
+                cs.load(g.d + k0 / QA);
+                const bool has_next = cb + 2 * kChunkBlocks <= g.nb;
+                run_full_chunk<FMT, QA>(T, D1, cs, wtile(tile, cb), stile(tile, cb), wtile(tile, cb + kChunkBlocks),
+                                        stile(tile, cb + kChunkBlocks), has_next, lo, pf, acc);
+            } else {
+                run_tail_chunk<FMT>(T, D1, wtile(tile, cb), stile(tile, cb), lo, nbc, acc);
+            }
+        }
+    }
+    if (active)
+        store_row(g, tile, lane, acc);
+}
+
+template <int FMT, int QA>
+__global__ __launch_bounds__(kThreads) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int tiles)
+{
+    __shared__ float T[kTableFloats];
+    __shared__ float D1[kScaleFloats];
+    const int c = blockIdx.y;  // activation column
+    g.q += c * ld_q;
+    g.d += c * ld_d;
+    g.y += (int64_t)c * g.rows;
+    const int tile0 = blockIdx.x * kWaves;
+    run_item<FMT, QA>(g, tile0, min(kWaves, tiles - tile0), T, D1);
+}
+
+template <int FMT, int QA>
+__global__ __launch_bounds__(kThreads) void sweep_kernel(const GemvDesc *__restrict__ descs,
+                                                         const WorkItem *__restrict__ items)
+{
+    __shared__ float T[kTableFloats];
+    __shared__ float D1[kScaleFloats];
+    const WorkItem it = items[blockIdx.x];
+    const GemvDesc g = descs[it.gemv];
+    run_item<FMT, QA>(g, it.tile0, it.ntiles, T, D1);
+}
+
+template <int FMT>
+static hipError_t rows_fmt(int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols, hipStream_t st)
+{
+    const dim3 grid((tiles + kWaves - 1) / kWaves, ncols);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((matvec_kernel<FMT, 32>), grid, dim3(kThreads), 0, st, g, ld_q, ld_d, tiles); break;
+    case 64: hipLaunchKernelGGL((matvec_kernel<FMT, 64>), grid, dim3(kThreads), 0, st, g, ld_q, ld_d, tiles); break;
+    default: hipLaunchKernelGGL((matvec_kernel<FMT, 128>), grid, dim3(kThreads), 0, st, g, ld_q, ld_d, tiles); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                       hipStream_t st)
+{
+    return fmt == BQ_Q1_0 ? rows_fmt<BQ_Q1_0>(qa, g, ld_q, ld_d, tiles, ncols, st)
+                          : rows_fmt<BQ_Q2_0>(qa, g, ld_q, ld_d, tiles, ncols, st);
+}
+
+template <int FMT>
+static hipError_t sweep_fmt(int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items, hipStream_t st)
+{
+    const dim3 grid(nitems);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((sweep_kernel<FMT, 32>), grid, dim3(kThreads), 0, st, descs, items); break;
+    case 64: hipLaunchKernelGGL((sweep_kernel<FMT, 64>), grid, dim3(kThreads), 0, st, descs, items); break;
+    default: hipLaunchKernelGGL((sweep_kernel<FMT, 128>), grid, dim3(kThreads), 0, st, descs, items); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
+                        hipStream_t st)
+{
+    return fmt == BQ_Q1_0 ? sweep_fmt<BQ_Q1_0>(qa, nitems, descs, items, st)
+                          : sweep_fmt<BQ_Q2_0>(qa, nitems, descs, items, st);
+}
+
+}  // namespace bq

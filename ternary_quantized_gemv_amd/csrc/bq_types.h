@@ -1,0 +1,84 @@
+// bq_types.h -- internal to libbq: types, sizes and kernel launchers shared
+// by the kernel sources (bq_sweep.hip, bq_split.hip, bq_batch.hip,
+// bq_quantize.hip) and the C ABI entry points (bq_api.cpp).
+//
+// Every output row is computed in the dot-product order of bankML's GPU page
+// ("gpu/ -- the video-card component", section "kernels.rs -- the Q1_0
+// kernels"): per block, eight lanes of exact integer sums over four
+// consecutive weights of each 32-weight sub-block; ab = d1*s on the first
+// sub-block, ab = fma(d1, s, ab) on the others; acc = fma(d0, ab, acc); then
+// the tree ((a0+a4)+(a2+a6)) + ((a1+a5)+(a3+a7)).  All kernels are built with
+// -ffp-contract=off and every fused step is an explicit fma, so the compiler
+// neither fuses nor splits what that order prescribes.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "bq_layout.h"
+
+namespace bq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunkBlocks = 32;                                     // blocks per LDS table
+constexpr int kSlotsPerBlock = 32;                                   // nibbles per block
+constexpr int kSlotFloats = 16;                                      // entries per nibble table
+constexpr int kTableFloats = kChunkBlocks * kSlotsPerBlock * kSlotFloats;  // 64 KiB
+constexpr int kScaleFloats = kChunkBlocks * 4;                       // d1 per sub-block
+constexpr int kWaves = 8;                                            // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kPrefetch = 4;                                         // blocks loaded ahead
+// Sweep work items of single-chunk products hold up to kMaxRounds tiles per
+// wavefront, all served by one table; the last kTailItems items of the
+// dispatch order are cut back to one tile per wavefront so the end of the
+// launch drains in small pieces.
+constexpr int kMaxRounds = 3;
+constexpr int kTailItems = 1024;
+
+constexpr uint32_t kStep = kTileRows * 16;  // bytes of one block (or scale group) of a tile
+
+struct GemvDesc {
+    const u32x4 *bits;    // payload plane
+    const u32x4 *scales;  // scale plane: 8 f16 per lane per 16 bytes
+    const int8_t *q;      // activation quants of this product
+    const float *d;       // activation scales
+    float *y;             // output
+    int32_t rows;
+    int32_t nb;  // blocks per row
+    int32_t ng;  // scale groups (of 8 blocks) per row
+    int32_t pad;
+};
+
+struct WorkItem {
+    int32_t gemv;
+    int32_t tile0;
+    int32_t ntiles;  // tiles tile0 .. tile0+ntiles-1; wavefront w takes tile0+w, tile0+w+kWaves, ...
+    int32_t pad;
+};
+
+// Kernel launchers (host side).  Each validates nothing: the entry points in
+// bq_api.cpp check every argument first.  They return hipGetLastError().
+//
+// launch_rows: one row per lane, one grid row per activation column (bq_sweep.hip).
+hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                       hipStream_t st);
+// launch_sweep: the work items of a sweep plan (bq_sweep.hip).
+hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
+                        hipStream_t st);
+// launch_split: four wavefronts per 64-row tile (bq_split.hip).
+hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                        hipStream_t st);
+// launch_batch: ncols columns on the matrix cores (bq_batch.hip).
+hipError_t launch_batch(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols, hipStream_t st);
+// launch_quantize: n values in blocks of qa (bq_quantize.hip).
+hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st);
+
+// Single-column products of at most this many 64-row tiles use launch_split.
+constexpr int kSplitMaxTiles = 1024;
+// At least this many activation columns use launch_batch; fewer run the
+// single-column kernels once per column.
+constexpr int kMfMinCols = 5;
+
+}  // namespace bq
