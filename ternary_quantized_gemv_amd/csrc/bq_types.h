@@ -51,12 +51,16 @@ struct GemvDesc {
     int32_t pad;
 };
 
+// A work item of a sweep: tiles tile0 .. tile0 + ntiles - 1 of product gemv;
+// wavefront w takes tiles tile0 + w, tile0 + w + kWaves, ...
 struct WorkItem {
     int32_t gemv;
     int32_t tile0;
-    int32_t ntiles;  // tiles tile0 .. tile0+ntiles-1; wavefront w takes tile0+w, tile0+w+kWaves, ...
+    int32_t ntiles;
     int32_t pad;
 };
+constexpr int kSplit = 4;                     // wavefronts per tile of split_kernel
+constexpr int kSplitTiles = kWaves / kSplit;  // tiles per split_kernel workgroup
 
 // Kernel launchers (host side).  Each validates nothing: the entry points in
 // bq_api.cpp check every argument first.  They return hipGetLastError().
@@ -67,7 +71,7 @@ hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // launch_sweep: the work items of a sweep plan (bq_sweep.hip).
 hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
                         hipStream_t st);
-// launch_split: four wavefronts per 64-row tile (bq_split.hip).
+// launch_split: four wavefronts per 64-row tile (bq_sweep.hip).
 hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
                         hipStream_t st);
 // launch_batch: ncols columns on the matrix cores (bq_batch.hip).
