@@ -8,6 +8,15 @@ Weights are packed and copied to the GPU once, before timing; inputs are
 seeded synthetic data with the workload's shapes and distributions.
 
 Prints ONE JSON line.  python bench.py [--steps K] [--warmup W] [--fmt q1_0|q2_0]
+
+Other workloads (each prints its own JSON line; not the headline):
+  --workload gemv   single products at the configured shapes (Q1_0 4096x4096,
+                    12288x4096, 4096x12288, 151936x4096; Q2_0 4096x4096,
+                    1024x4096, 12288x4096, 4096x12288): us per product, GB/s,
+                    fraction of HBM peak, ms per token-equivalent
+  --workload batch  Q1_0 12288x4096 and 151936x4096 with N = 1, 4, 8, 16
+                    activation columns: us per call against the HBM and the
+                    fp32 vector-ALU rooflines
 """
 from __future__ import annotations
 
@@ -23,7 +32,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
-PROFILE = os.path.join(ROOT, "profiles", "sweep_kernel_q1_0_decode_token.json")
+VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
+# algorithmic bytes of one decode token (weights + q + d + y of the 253 products)
+TOKEN_BYTES = {"Q1_0": 1071847552, "Q2_0": 2136111232}
+PROFILES = {"Q1_0": os.path.join(ROOT, "profiles", "sweep_kernel_q1_0_decode_token.json"),
+            "Q2_0": os.path.join(ROOT, "profiles", "sweep_kernel_q2_0_decode_token.json")}
 
 
 def log(*a):
@@ -35,7 +48,7 @@ def measured_traffic(fmt_name: str):
     or None when the kernel sources changed since the counters were taken."""
     import hashlib
     try:
-        with open(PROFILE) as f:
+        with open(PROFILES[fmt_name]) as f:
             prof = json.load(f)
         h = hashlib.sha256()
         for p in prof["kernel_sources"]:
@@ -43,7 +56,7 @@ def measured_traffic(fmt_name: str):
                 h.update(f.read())
     except (OSError, KeyError, ValueError):
         return None
-    if fmt_name != "Q1_0" or h.hexdigest() != prof.get("kernel_sources_sha256"):
+    if h.hexdigest() != prof.get("kernel_sources_sha256"):
         return None
     return prof.get("traffic_bytes_per_launch")
 
@@ -92,12 +105,119 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
     }
 
 
+def timed_calls(fn, reps: int) -> float:
+    """Mean microseconds per call of fn(i) over reps back-to-back calls on the
+    current stream (HIP events around the batch)."""
+    import torch
+
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def weight_copies(bq, fmt, rows, cols, seed, total=1.1e9, cap=512):
+    """Device copies of one packed matrix, enough to total about 1.1 GB, so a
+    timed batch that cycles through them streams from HBM (the 256 MB
+    last-level cache cannot hold them)."""
+    import synth
+
+    canon = synth.blocks(fmt, rows, cols, seed, rows)
+    w0 = bq.Weights.upload(fmt, canon, rows, cols)
+    n = max(1, min(cap, int(total // canon.size)))
+    ws = [w0] + [bq.Weights(fmt, rows, cols, w0.bits.clone(), w0.scales.clone()) for _ in range(n - 1)]
+    return ws, canon.size
+
+
+def quantized_columns(bq, cols, ncols, seed):
+    import torch
+    import synth
+
+    x = torch.from_numpy(np.stack([synth.activation(cols, seed, 500 + c) for c in range(ncols)])).to("cuda")
+    q = torch.empty((ncols, cols), dtype=torch.int8, device="cuda")
+    d = torch.empty((ncols, cols // 128), dtype=torch.float32, device="cuda")
+    for c in range(ncols):
+        bq.bq_quantize_act_q8(x[c], 128, q[c], d[c])
+    return bq.Act(q, d, cols, 128, ncols)
+
+
+def bench_gemv(args):
+    import torch
+    import ternary_quantized_gemv_amd as bq
+
+    shapes = [(bq.BQ_Q1_0, 4096, 4096), (bq.BQ_Q1_0, 12288, 4096), (bq.BQ_Q1_0, 4096, 12288),
+              (bq.BQ_Q1_0, 151936, 4096), (bq.BQ_Q2_0, 4096, 4096), (bq.BQ_Q2_0, 1024, 4096),
+              (bq.BQ_Q2_0, 12288, 4096), (bq.BQ_Q2_0, 4096, 12288)]
+    rows_out = []
+    for fmt, rows, cols in shapes:
+        ws, wbytes = weight_copies(bq, fmt, rows, cols, args.seed)
+        a = quantized_columns(bq, cols, 1, args.seed)
+        y = torch.empty(rows, device="cuda")
+        f = bq.bq_q1_0_matvec if fmt == bq.BQ_Q1_0 else bq.bq_q2_0_matvec
+        us = timed_calls(lambda i: f(ws[i % len(ws)], a, y), max(args.steps, 2 * len(ws)))
+        nbytes = wbytes + cols + 4 * (cols // 128) + 4 * rows
+        gbs = nbytes / us / 1e3
+        name = "Q1_0" if fmt == bq.BQ_Q1_0 else "Q2_0"
+        rows_out.append({"fmt": name, "shape": f"{rows}x{cols}", "us_per_product": round(us, 2),
+                         "algorithmic_bytes": nbytes, "GB_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "ms_per_token_equiv": round(TOKEN_BYTES[name] / (gbs * 1e9) * 1e3, 3),
+                         "weight_copies": len(ws)})
+        log(f"gemv {name} {rows}x{cols}: {us:.2f} us, {gbs:.0f} GB/s")
+        del ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "single-product us and HBM GB/s (% of peak) at the configured shapes",
+                      "unit": "us", "higher_is_better": False, "n_gpus": 1,
+                      "dtype": "int8xQ->f32", "data": "synthetic (seeded)",
+                      "config": {"workload": "single Q1_0 / Q2_0 products, one activation vector, qa 128; "
+                                             "each timed batch cycles through ~1.1 GB of weight copies"},
+                      "results": rows_out}), flush=True)
+
+
+def bench_batch(args):
+    import torch
+    import ternary_quantized_gemv_amd as bq
+
+    rows_out = []
+    for rows in (12288, 151936):
+        cols = 4096
+        ws, wbytes = weight_copies(bq, bq.BQ_Q1_0, rows, cols, args.seed)
+        for ncols in (1, 4, 8, 16):
+            a = quantized_columns(bq, cols, ncols, args.seed)
+            y = torch.empty(ncols * rows, device="cuda")
+            us = timed_calls(lambda i: bq.bq_q1_0_matvec(ws[i % len(ws)], a, y), max(args.steps // 4, 2 * len(ws)))
+            nbytes = wbytes + ncols * (cols + 4 * (cols // 128) + 4 * rows)
+            flops = rows * cols * ncols * 0.625  # 0.3125 f32 multiply-adds per weight per column
+            hbm_us = nbytes / (HBM_PEAK_GBS * 1e3)
+            valu_us = flops / (VALU_PEAK_TFLOPS * 1e6)
+            bound = "hbm" if hbm_us >= valu_us else "alu"
+            rows_out.append({"shape": f"{rows}x{cols}", "ncols": ncols, "us_per_call": round(us, 2),
+                             "GB_s": round(nbytes / us / 1e3, 1), "TFLOP_s": round(flops / us / 1e6, 2),
+                             "bound": bound, "roofline_us": round(max(hbm_us, valu_us), 2),
+                             "frac": round(max(hbm_us, valu_us) / us, 4)})
+            log(f"batch {rows}x{cols} N={ncols}: {us:.2f} us")
+        del ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "small-batch Q1_0 us per call against the HBM and fp32 vector rooflines",
+                      "unit": "us", "higher_is_better": False, "n_gpus": 1,
+                      "dtype": "int8xQ1_0->f32", "data": "synthetic (seeded)",
+                      "config": {"workload": "Q1_0 12288x4096 and 151936x4096, N = 1, 4, 8, 16 activation "
+                                             "columns, qa 128; peaks 8 TB/s and 157.3 TFLOP/s"},
+                      "results": rows_out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--fmt", choices=["q1_0", "q2_0"], default="q1_0")
+    ap.add_argument("--workload", choices=["sweep", "gemv", "batch"], default="sweep")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -120,6 +240,10 @@ def main():
     if not torch.cuda.is_available():
         log("bench.py: no GPU visible")
         sys.exit(1)
+    if args.workload == "gemv":
+        return bench_gemv(args)
+    if args.workload == "batch":
+        return bench_batch(args)
     fmt = bq.BQ_Q1_0 if args.fmt == "q1_0" else bq.BQ_Q2_0
     shapes = synth.decode_sweep_shapes()
     t0 = time.time()

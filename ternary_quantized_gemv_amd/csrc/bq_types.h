@@ -79,10 +79,4 @@ hipError_t launch_batch(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_
 // launch_quantize: n values in blocks of qa (bq_quantize.hip).
 hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st);
 
-// Single-column products of at most this many 64-row tiles use launch_split.
-constexpr int kSplitMaxTiles = 1024;
-// At least this many activation columns use launch_batch; fewer run the
-// single-column kernels once per column.
-constexpr int kMfMinCols = 5;
-
 }  // namespace bq

@@ -136,22 +136,50 @@ def _batch_cases():
     return out
 
 
-@pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", _batch_cases())
-def test_small_batch_parity(fmt, rows, cols, ncols, qa, regime):
-    """Several activation columns against one matrix (weights read once); the raw
-    regime plants q = -128, which exercises the wrap of int8 negation in Q1_0."""
-    name = f"batch fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
-    log(name)
+def _batch_inputs(fmt, rows, cols, ncols, qa, regime):
+    """Seeded weights and ncols activation columns.  "quant": the quantizer's
+    output; "raw": raw int8 quants with q = -128 planted (the wrap of int8
+    negation in Q1_0); "mixed": -128 only near both ends of the last column."""
     w = synth.blocks(fmt, rows, cols, rows + ncols)
     if regime in ("raw", "mixed"):
         qs, ds = zip(*[synth.raw_q8(cols, qa, 7 * c + rows, force_min=regime == "raw") for c in range(ncols)])
-        if regime == "mixed":  # one -128 in the first and in the last 1024 values of column ncols-1 only
+        if regime == "mixed":
             qs = [q.copy() for q in qs]
             qs[-1][5] = -128
             qs[-1][cols - 3] = -128
     else:
         qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, rows, c), qa)[:2] for c in range(ncols)])
-    q, d = np.stack(qs), np.stack(ds)
+    return w, np.stack(qs), np.stack(ds)
+
+
+@pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", _batch_cases())
+def test_small_batch_parity(fmt, rows, cols, ncols, qa, regime):
+    """Several activation columns against one small matrix (the single-column
+    kernels, one grid row per column)."""
+    name = f"batch fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
+    log(name)
+    w, q, d = _batch_inputs(fmt, rows, cols, ncols, qa, regime)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
+
+
+# Tall matrices (more than 1024 row tiles): five or more columns run on the
+# matrix cores, fewer on the one-row-per-lane kernel; ragged row counts, ragged
+# last chunks (blocks not a multiple of 4), every qa and the -128 regimes.
+TALL = [
+    (Q1, 65600, 640, 5, 128, "quant"), (Q1, 65600, 640, 16, 32, "raw"), (Q1, 65601, 384, 8, 64, "mixed"),
+    (Q1, 65536 + 64 * 7 + 3, 4096, 9, 128, "quant"), (Q1, 65600, 640, 3, 32, "raw"), (Q1, 65600, 256, 1, 64, "raw"),
+    (Q2, 65600, 320, 5, 64, "raw"), (Q2, 65600, 448, 16, 32, "quant"), (Q2, 65700, 4096, 12, 128, "quant"),
+    (Q2, 65601, 192, 13, 64, "mixed"), (Q2, 65600, 320, 2, 32, "raw"),
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", TALL,
+                         ids=[f"q{f}-{r}x{c}-n{n}-qa{a}-{g}" for f, r, c, n, a, g in TALL])
+def test_small_batch_tall(fmt, rows, cols, ncols, qa, regime):
+    name = f"tall batch fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
+    log(name)
+    w, q, d = _batch_inputs(fmt, rows, cols, ncols, qa, regime)
     y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
     assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
 
