@@ -20,12 +20,13 @@ namespace bq {
 // * single-column products of at most kSplitMaxTiles 64-row tiles run four
 //   wavefronts per tile (launch_split), larger ones one row per lane;
 // * several columns run those kernels once per column (one grid row each),
-//   except at least kMfMinCols columns on a matrix of more than
-//   kSplitMaxTiles tiles, which run on the matrix cores (launch_batch): there
-//   the per-column kernels re-stream the weights once per column, while on
-//   smaller matrices their extra parallelism wins.
+//   except at least kColsMinCols columns on a matrix of more than
+//   kSplitMaxTiles tiles, which run four columns per workgroup from
+//   interleaved tables (launch_cols): there the per-column kernels re-stream
+//   the weights once per column, while on smaller matrices their extra
+//   parallelism wins.
 constexpr int kSplitMaxTiles = 1024;
-constexpr int kMfMinCols = 5;
+constexpr int kColsMinCols = 4;
 
 // ------------------------------------------------------------ validation
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -111,8 +112,8 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
     const int tiles = (int)tiles_of(w->rows);
     hipStream_t st = static_cast<hipStream_t>(s);
     hipError_t e;
-    if (a->ncols >= kMfMinCols && tiles > kSplitMaxTiles)
-        e = launch_batch(FMT, a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
+    if (a->ncols >= kColsMinCols && tiles > kSplitMaxTiles)
+        e = launch_cols(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
     else if (tiles <= kSplitMaxTiles)
         e = launch_split(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
     else

@@ -163,14 +163,16 @@ def test_small_batch_parity(fmt, rows, cols, ncols, qa, regime):
     assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
 
 
-# Tall matrices (more than 1024 row tiles): five or more columns run on the
-# matrix cores, fewer on the one-row-per-lane kernel; ragged row counts, ragged
-# last chunks (blocks not a multiple of 4), every qa and the -128 regimes.
+# Tall matrices (more than 1024 row tiles): four or more columns run four per
+# workgroup from interleaved tables (including a last group of 1-3 columns),
+# fewer on the one-row-per-lane kernel; ragged row counts, ragged last chunks
+# (blocks not a multiple of 4), every qa and the -128 regimes.
 TALL = [
     (Q1, 65600, 640, 5, 128, "quant"), (Q1, 65600, 640, 16, 32, "raw"), (Q1, 65601, 384, 8, 64, "mixed"),
     (Q1, 65536 + 64 * 7 + 3, 4096, 9, 128, "quant"), (Q1, 65600, 640, 3, 32, "raw"), (Q1, 65600, 256, 1, 64, "raw"),
+    (Q1, 65600, 1152, 4, 32, "raw"), (Q1, 65600, 128, 6, 128, "mixed"),
     (Q2, 65600, 320, 5, 64, "raw"), (Q2, 65600, 448, 16, 32, "quant"), (Q2, 65700, 4096, 12, 128, "quant"),
-    (Q2, 65601, 192, 13, 64, "mixed"), (Q2, 65600, 320, 2, 32, "raw"),
+    (Q2, 65601, 192, 13, 64, "mixed"), (Q2, 65600, 320, 2, 32, "raw"), (Q2, 65600, 576, 4, 64, "raw"),
 ]
 
 
