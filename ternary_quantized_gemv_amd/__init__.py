@@ -6,7 +6,7 @@ ROCm device become device pointers, numpy arrays become host pointers, and a
 nonzero return code becomes a ``BQError`` carrying ``bq_last_error()``.  Every
 step of the computation runs in the HIP kernels of ``libbq.so``; importing
 this package fails if the library has not been built
-(``python -m ternary_quantized_gemv_amd.build``).
+(``python ternary_quantized_gemv_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -63,7 +63,7 @@ def _hip_runtimes() -> set:
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ternary_quantized_gemv_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python ternary_quantized_gemv_amd/build.py`")
     # torch ships its own HIP runtime (same soname).  Loading torch first lets
     # libbq bind to that already-loaded copy, so device pointers and streams
     # from torch are valid in libbq's calls.  Two runtimes in one process would

@@ -1,6 +1,6 @@
 """Builds libbq.so (HIP for gfx950) in-tree with hipcc.
 
-python -m ternary_quantized_gemv_amd.build
+python ternary_quantized_gemv_amd/build.py   (runs without importing the package)
 """
 from __future__ import annotations
 
