@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbq.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("bq_sweep.hip", "bq_cols.hip", "bq_quantize.hip", "bq_api.cpp",
                                             "bq_pack.cpp")]
-HEADERS = [os.path.join(CSRC, f) for f in ("bq_layout.h", "bq_types.h", "bq_device.h")] + [os.path.join(ROOT, "include", "bq.h")]
+HEADERS = [os.path.join(CSRC, f) for f in ("bq_layout.h", "bq_types.h", "bq_device.h", "bq_launch.h")] + [os.path.join(ROOT, "include", "bq.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

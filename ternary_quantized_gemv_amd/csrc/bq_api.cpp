@@ -12,6 +12,7 @@
 
 #include "../../include/bq.h"
 #include "bq_layout.h"
+#include "bq_launch.h"
 #include "bq_types.h"
 
 namespace bq {

@@ -16,6 +16,7 @@
 // 64-row tile each, so three workgroups share a CU (registers allow three
 // wavefronts per SIMD).
 #include "bq_device.h"
+#include "bq_launch.h"
 
 namespace bq {
 
@@ -54,44 +55,65 @@ __device__ void build_cols(f32x4 *T, float *D1, const GemvDesc &g, int64_t ld_q,
                            int k0, int nbc)
 {
     constexpr int S = FMT == BQ_Q1_0 ? 4 : 2;
-    // unit u = (slot t, quarter h, column c): entries 4h..4h+3 of column c
+    constexpr int kThreadsHere = kColsWaves * 64;
+    constexpr int kIters = kColsChunk * kSlotsPerBlock * 4 * kColsNC / kThreadsHere;
+    // unit u = (slot t, quarter h, column c): entries 4h..4h+3 of column c.
+    // All of a thread's loads are issued before any is used.
     const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
     float *Tf = reinterpret_cast<float *>(T);
-    for (int u = threadIdx.x; u < nunits; u += blockDim.x) {
+    uint32_t wq[kIters];
+    float d1[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int u = threadIdx.x + it * kThreadsHere;
+        const int c = u % kColsNC, t = u / (4 * kColsNC);
+        const bool ok = u < nunits && c0 + c < ncols;
+        const int cc = ok ? c0 + c : c0;
+        const int8_t *q = g.q + (int64_t)cc * ld_q + k0;
+        if (FMT == BQ_Q1_0) {
+            wq[it] = ok ? *reinterpret_cast<const uint32_t *>(q + 4 * t) : 0u;
+            d1[it] = ok && ((t >> 3) & 3) == 0 ? g.d[(int64_t)cc * ld_d + (k0 + 4 * t) / QA] : 0.0f;
+        } else {
+            wq[it] = ok ? *reinterpret_cast<const uint16_t *>(q + 2 * t) : 0u;
+            d1[it] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int u = threadIdx.x + it * kThreadsHere;
+        if (u >= nunits)
+            break;
         const int c = u % kColsNC, h = (u / kColsNC) & 3, t = u / (4 * kColsNC);
-        const bool ok = c0 + c < ncols;
-        const int8_t *q = g.q + (int64_t)(ok ? c0 + c : c0) * ld_q + k0;
         float v[4];
         if (FMT == BQ_Q1_0) {
-            const uint32_t w4 = *reinterpret_cast<const uint32_t *>(q + 4 * t);
             int p1[4], p0[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int x = (int8_t)(w4 >> (8 * i));
+                const int x = (int8_t)(wq[it] >> (8 * i));
                 p1[i] = x;
                 p0[i] = x == -128 ? -128 : -x;
             }
             const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
             const bool first = ((t >> 3) & 3) == 0;
-            const float d1 = first ? g.d[(int64_t)(ok ? c0 + c : c0) * ld_d + (k0 + 4 * t) / QA] : 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int lo = ((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]);
                 const float sf = (float)(lo + hi);
-                v[e] = ok ? (first ? d1 * sf : sf) : 0.0f;
+                v[e] = first ? d1[it] * sf : sf;
             }
         } else {
-            const uint32_t w2 = *reinterpret_cast<const uint16_t *>(q + 2 * t);
-            const int qa0 = (int8_t)(w2 & 0xFF), qa1 = (int8_t)(w2 >> 8);
+            const int qa0 = (int8_t)(wq[it] & 0xFF), qa1 = (int8_t)(wq[it] >> 8);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = ok ? (float)((e - 1) * qa0 + (h - 1) * qa1) : 0.0f;
+                v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
         }
+        // a column past ncols loaded zeros: its entries are 0 (Q1_0 d1 = 0 on sub-block 0, and
+        // the integer sums of zero quants are 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             Tf[(t * 16 + 4 * h + e) * kColsNC + c] = v[e];
     }
-    for (int i = threadIdx.x; i < nbc * S * kColsNC; i += blockDim.x) {
+    for (int i = threadIdx.x; i < nbc * S * kColsNC; i += kThreadsHere) {
         const int sb = i / kColsNC, c = i % kColsNC;
         const bool ok = c0 + c < ncols;
         D1[i] = ok ? g.d[(int64_t)(c0 + c) * ld_d + (k0 + 32 * sb) / QA] : 0.0f;

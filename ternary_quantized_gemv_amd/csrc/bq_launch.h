@@ -1,0 +1,27 @@
+// bq_launch.h -- internal to libbq: the host-side kernel launchers that the
+// kernel sources define and the C ABI entry points (bq_api.cpp) call.
+#pragma once
+
+#include "bq_types.h"
+
+namespace bq {
+
+// Kernel launchers (host side).  Each validates nothing: the entry points in
+// bq_api.cpp check every argument first.  They return hipGetLastError().
+//
+// launch_rows: one row per lane, one grid row per activation column (bq_sweep.hip).
+hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                       hipStream_t st);
+// launch_sweep: the work items of a sweep plan (bq_sweep.hip).
+hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
+                        hipStream_t st);
+// launch_split: four wavefronts per 64-row tile (bq_sweep.hip).
+hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                        hipStream_t st);
+// launch_cols: ncols columns, four per workgroup, one row per lane (bq_cols.hip).
+hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                       hipStream_t st);
+// launch_quantize: n values in blocks of qa (bq_quantize.hip).
+hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st);
+
+}  // namespace bq

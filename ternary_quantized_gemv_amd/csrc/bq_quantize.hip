@@ -1,6 +1,7 @@
 // bq_quantize.hip -- the activation quantizer: per block of qa values,
 // d = amax / 127 and q = round-half-away(x / d).
 #include "bq_device.h"
+#include "bq_launch.h"
 
 namespace bq {
 

@@ -29,6 +29,7 @@
 //   most to the least work so the hardware's in-order dispatch balances the
 //   GPU.
 #include "bq_device.h"
+#include "bq_launch.h"
 
 namespace bq {
 

@@ -1,6 +1,6 @@
-// bq_types.h -- internal to libbq: types, sizes and kernel launchers shared
-// by the kernel sources (bq_sweep.hip, bq_cols.hip, bq_quantize.hip) and the
-// C ABI entry points (bq_api.cpp).
+// bq_types.h -- internal to libbq: types and sizes shared by the kernel
+// sources (bq_sweep.hip, bq_cols.hip, bq_quantize.hip) and the C ABI entry
+// points (bq_api.cpp).  The launchers are declared in bq_launch.h.
 //
 // Every output row is computed in the dot-product order of bankML's GPU page
 // ("gpu/ -- the video-card component", section "kernels.rs -- the Q1_0
@@ -61,23 +61,5 @@ struct WorkItem {
 };
 constexpr int kSplit = 4;                     // wavefronts per tile of split_kernel
 constexpr int kSplitTiles = kWaves / kSplit;  // tiles per split_kernel workgroup
-
-// Kernel launchers (host side).  Each validates nothing: the entry points in
-// bq_api.cpp check every argument first.  They return hipGetLastError().
-//
-// launch_rows: one row per lane, one grid row per activation column (bq_sweep.hip).
-hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
-                       hipStream_t st);
-// launch_sweep: the work items of a sweep plan (bq_sweep.hip).
-hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
-                        hipStream_t st);
-// launch_split: four wavefronts per 64-row tile (bq_sweep.hip).
-hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
-                        hipStream_t st);
-// launch_cols: ncols columns, four per workgroup, one row per lane (bq_cols.hip).
-hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
-                       hipStream_t st);
-// launch_quantize: n values in blocks of qa (bq_quantize.hip).
-hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st);
 
 }  // namespace bq
