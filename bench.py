@@ -17,6 +17,9 @@ Other workloads (each prints its own JSON line; not the headline):
   --workload batch  Q1_0 12288x4096 and 151936x4096 with N = 1, 4, 8, 16
                     activation columns: us per call against the HBM and the
                     fp32 vector-ALU rooflines
+  --workload chain  the token as 145 dependent groups (each group's
+                    activation is the quantized output of the previous one):
+                    ms per token launched eagerly and replayed from a graph
 """
 from __future__ import annotations
 
@@ -211,13 +214,67 @@ def bench_batch(args):
                       "results": rows_out}), flush=True)
 
 
+def bench_chain(args):
+    import torch
+    import synth
+    import ternary_quantized_gemv_amd as bq
+    from ternary_quantized_gemv_amd.staging import StagedChain
+
+    fmt = bq.BQ_Q1_0 if args.fmt == "q1_0" else bq.BQ_Q2_0
+    shapes = synth.decode_sweep_shapes()
+    canon = [synth.blocks(fmt, r, c, args.seed, i) for i, (_, r, c) in enumerate(shapes)]
+    x0 = synth.activation(shapes[0][2], args.seed, 999)
+    ch = StagedChain(fmt, canon, shapes, x0)
+    del canon
+    K, W = max(20, args.steps // 4), max(5, args.warmup // 10)
+
+    def per_token(fn):
+        for _ in range(W):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    eager_ms = per_token(ch.run)
+    ref = ch.y.cpu().numpy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ch.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ch.run()
+    graph_ms = per_token(graph.replay)
+    same = bool(np.array_equal(ch.y.cpu().numpy().view(np.uint32), ref.view(np.uint32)))
+    nbytes = ch.token_bytes()
+    name = "Q1_0" if fmt == bq.BQ_Q1_0 else "Q2_0"
+    print(json.dumps({"metric": f"ms per token for the {name} decode token as 145 dependent groups",
+                      "unit": "ms", "higher_is_better": False, "n_gpus": 1, "dtype": f"int8x{name}->f32",
+                      "data": "synthetic (seeded)",
+                      "config": {"workload": "36 layers x ({q,k,v}, {o}, {gate,up}, {down}) + {lm_head}; each "
+                                             "group's activation is the quantized output of the previous "
+                                             "group; one quantize + one sweep launch per group",
+                                 "launches_per_token": ch.launches(), "token_bytes": nbytes},
+                      "eager_ms_per_token": round(eager_ms, 4), "graph_ms_per_token": round(graph_ms, 4),
+                      "graph_GB_s": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
+                      "graph_replay_equals_eager": same}), flush=True)
+    ch.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--fmt", choices=["q1_0", "q2_0"], default="q1_0")
-    ap.add_argument("--workload", choices=["sweep", "gemv", "batch"], default="sweep")
+    ap.add_argument("--workload", choices=["sweep", "gemv", "batch", "chain"], default="sweep")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -244,6 +301,8 @@ def main():
         return bench_gemv(args)
     if args.workload == "batch":
         return bench_batch(args)
+    if args.workload == "chain":
+        return bench_chain(args)
     fmt = bq.BQ_Q1_0 if args.fmt == "q1_0" else bq.BQ_Q2_0
     shapes = synth.decode_sweep_shapes()
     t0 = time.time()

@@ -80,3 +80,88 @@ class StagedSweep:
 
     def close(self):
         self.plan.destroy()
+
+
+# ------------------------------------------------------------------ chain
+def chain_groups(n_layers: int, lm_head: bool = True):
+    """The dependency order of one decode token over the products of
+    synth.decode_sweep_shapes(n_layers): per layer {q, k, v}, {o}, {gate, up},
+    {down}, then {lm_head}.  Returns [(product indices, source index)]: the
+    group's input is the output of product `source` (-1: the token's input
+    vector).  The products' own data dependencies (attention, the gated
+    activation) are replaced by the nearest output of the right length:
+    o takes q's output, gate and up take o's, down takes up's, and the next
+    layer (or the LM head) takes down's."""
+    groups = []
+    prev = -1
+    for layer in range(n_layers):
+        base = 7 * layer
+        q, k, v, o, gate, up, down = range(base, base + 7)
+        groups.append(([q, k, v], prev))
+        groups.append(([o], q))
+        groups.append(([gate, up], o))
+        groups.append(([down], up))
+        prev = down
+    if lm_head:
+        groups.append(([7 * n_layers], prev))
+    return groups
+
+
+class StagedChain:
+    """One decode token as a chain of dependent launches: for every group of
+    chain_groups(), one quantizer launch on the group's input (the previous
+    group's output) and one sweep launch over the group's products, all on
+    one stream.  Products of a group share one quantized activation."""
+
+    def __init__(self, fmt: int, canon, shapes, x0, qa: int = 128, n_layers: int = None):
+        import torch
+
+        self.fmt, self.qa = fmt, qa
+        self.shapes = [(str(n), int(r), int(c)) for n, r, c in shapes]
+        n_layers = (len(self.shapes) - 1) // 7 if n_layers is None else n_layers
+        self.groups = chain_groups(n_layers, lm_head=len(self.shapes) == 7 * n_layers + 1)
+        self.yoff = np.concatenate([[0], np.cumsum([r for _, r, _ in self.shapes])]).astype(np.int64)
+        self.weights = [Weights.upload(fmt, c, r, k) for c, (_, r, k) in zip(canon, self.shapes)]
+        self.weight_bytes = int(sum(c.size for c in canon))
+        self.x0 = torch.from_numpy(np.asarray(x0, np.float32).ravel()).to("cuda")
+        self.y = torch.full((int(self.yoff[-1]),), float("nan"), dtype=torch.float32, device="cuda")
+        self.stages = []
+        for prods, src in self.groups:
+            cols = self.shapes[prods[0]][2]
+            if any(self.shapes[p][2] != cols for p in prods):
+                raise ValueError("a group's products must share their input length")
+            xin = self.x0 if src < 0 else self.output(src)
+            if xin.numel() != cols:
+                raise ValueError("a group's input length must match its products")
+            q = torch.empty(cols, dtype=torch.int8, device="cuda")
+            d = torch.empty(cols // qa, dtype=torch.float32, device="cuda")
+            a = Act(q, d, cols, qa, 1)
+            plan = bq_sweep_create([(self.weights[p], a, self.output(p)) for p in prods])
+            self.stages.append((xin, q, d, plan))
+
+    def output(self, i: int):
+        return self.y[int(self.yoff[i]):int(self.yoff[i + 1])]
+
+    def run(self, stream=None):
+        for xin, q, d, plan in self.stages:
+            bq_quantize_act_q8(xin, self.qa, q, d, stream)
+            bq_token_sweep(plan, stream)
+
+    def launches(self) -> int:
+        return 2 * len(self.stages)
+
+    def token_bytes(self) -> int:
+        """Algorithmic bytes of one token: weights, every activation quantized
+        (f32 read, int8 + f32 scales written, then read by the products) and
+        every output written."""
+        n = 0
+        for prods, _ in self.groups:
+            cols = self.shapes[prods[0]][2]
+            n += 4 * cols + cols + 4 * (cols // self.qa)               # quantizer
+            n += len(prods) * (cols + 4 * (cols // self.qa))           # products read the activation
+        return self.weight_bytes + n + 4 * int(self.yoff[-1])
+
+    def close(self):
+        for _, _, _, plan in self.stages:
+            plan.destroy()
+        self.stages = []
