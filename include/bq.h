@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 1
+#define BQ_ABI_VERSION 2
 
 /* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
  * then 16 payload bytes).
@@ -145,6 +145,20 @@ int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *
  * call); a->n must equal w->cols.  Allocates nothing.  Asynchronous on s. */
 int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
 int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
+
+/* One group of a dependency-ordered decode step in ONE launch: the count
+ * products (1..4) that read the same activation -- bankML "gpu/ -- the
+ * video-card component", section "Limitations": Q/K/V, and gate/up, are
+ * submitted together with one wait per group.  x (device, 16-byte aligned)
+ * holds the f32 activation of length w[0].cols; it is quantized in blocks of
+ * qa exactly as bq_quantize_act_q8 would (the quants stay on chip) and
+ * y[i] (device, 4-byte aligned, w[i].rows floats) receives what
+ * bq_q1_0_matvec / bq_q2_0_matvec would write for w[i] and those quants.
+ * Every w[i] must share w[0]'s format and cols (a multiple of qa); qa is
+ * 32, 64 or 128.  No y[i] may overlap x.  w and y are host arrays of count
+ * entries, read during the call.  Allocates nothing.  Asynchronous on s. */
+int bq_group_matvec(const bq_weights *w, int32_t count, const float *x, int32_t qa, float *const *y,
+                    bq_stream s);
 
 /* A plan for many independent products run by ONE kernel launch (the 253
  * products of one decode token: bankML "par.rs -- the persistent thread pool

@@ -26,7 +26,7 @@ BLOCK_BYTES = 18
 
 EXPORTS = (
     "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
-    "bq_quantize_act_q8", "bq_q1_0_matvec", "bq_q2_0_matvec",
+    "bq_quantize_act_q8", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
     "bq_sweep_create", "bq_token_sweep", "bq_sweep_destroy",
 )
 
@@ -94,6 +94,8 @@ def _load() -> ctypes.CDLL:
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(bq_weights), ctypes.POINTER(bq_act), vp, vp]
     lib.bq_sweep_create.restype = ctypes.c_int
+    lib.bq_group_matvec.restype = ctypes.c_int
+    lib.bq_group_matvec.argtypes = [ctypes.POINTER(bq_weights), i32, vp, i32, ctypes.POINTER(vp), vp]
     lib.bq_sweep_create.argtypes = [ctypes.POINTER(bq_gemv), i32, ctypes.POINTER(vp)]
     lib.bq_token_sweep.restype = ctypes.c_int
     lib.bq_token_sweep.argtypes = [vp, vp]
@@ -213,6 +215,34 @@ def bq_q1_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
 
 def bq_q2_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
     _matvec(lib.bq_q2_0_matvec, w, a, y, stream)
+
+
+class GroupCall:
+    """The marshalled arguments of one bq_group_matvec call (weights, the f32
+    activation x, qa, one output per product), kept so that the call can be
+    issued repeatedly without rebuilding them."""
+
+    def __init__(self, weights, x, qa: int, ys):
+        n = len(weights)
+        if len(ys) != n:
+            raise BQError(BQ_EARG, "bq_group_matvec: one output per product")
+        if n and x.numel() != weights[0].cols:
+            raise BQError(BQ_EARG, "bq_group_matvec: x length differs from the weights' cols")
+        if any(y.numel() < w.rows for w, y in zip(weights, ys)):
+            raise BQError(BQ_EARG, "bq_group_matvec: an output is shorter than its product's rows")
+        self.w = (bq_weights * n)(*[w.c() for w in weights])
+        self.y = (ctypes.c_void_p * n)(*[_dev(y, "y") for y in ys])
+        self.n, self.x, self.qa = n, _dev(x, "x"), qa
+        self._keep = (list(weights), x, list(ys))
+
+    def launch(self, stream=None) -> None:
+        _check(lib.bq_group_matvec(self.w, self.n, self.x, self.qa, self.y, _stream(stream)))
+
+
+def bq_group_matvec(weights, x, qa: int, ys, stream=None) -> None:
+    """weights: [Weights] sharing format and cols; x: float32 device tensor
+    (cols); ys: float32 device tensors, one per product (rows)."""
+    GroupCall(weights, x, qa, ys).launch(stream)
 
 
 class Sweep:

@@ -28,6 +28,11 @@ namespace bq {
 //   parallelism wins.
 constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
+// bq_group_matvec: groups of at most kWideMaxTiles tiles give each tile a
+// workgroup of sixteen wavefronts (wide_kernel), larger groups put two tiles
+// in a workgroup of eight (group_kernel): once the GPU is full, fewer table
+// builds win over more wavefronts per tile.
+constexpr int kWideMaxTiles = 512;
 
 // ------------------------------------------------------------ validation
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -160,6 +165,60 @@ BQ_EXPORT int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_
 BQ_EXPORT int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
 {
     return launch_matvec<BQ_Q2_0>("bq_q2_0_matvec", w, a, y, s);
+}
+
+BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x, int32_t qa, float *const *y,
+                              bq_stream s)
+{
+    const char *fn = "bq_group_matvec";
+    if (!w || !y)
+        return set_error(BQ_EARG, "%s: null weights or outputs", fn);
+    if (count < 1 || count > kGroupMax)
+        return set_error(BQ_EARG, "%s: count %d not in [1, %d]", fn, (int)count, kGroupMax);
+    if (qa != 32 && qa != 64 && qa != 128)
+        return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)qa);
+    if (!x)
+        return set_error(BQ_EARG, "%s: null x", fn);
+    if (!aligned(x, 16))
+        return set_error(BQ_EALIGN, "%s: x must be 16-byte aligned", fn);
+    const int fmt = w[0].fmt;
+    if (fmt != BQ_Q1_0 && fmt != BQ_Q2_0)
+        return set_error(BQ_EARG, "%s: weights format %d unknown", fn, fmt);
+    GroupArgs args;
+    memset(&args, 0, sizeof args);
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        char where[96];
+        snprintf(where, sizeof where, "%s: product %d", fn, i);
+        const int rc = check_weights(where, &w[i], fmt);
+        if (rc)
+            return rc;
+        if (w[i].cols != w[0].cols)
+            return set_error(BQ_EARG, "%s: cols %lld differ from product 0's %lld", where, (long long)w[i].cols,
+                             (long long)w[0].cols);
+        if (!y[i])
+            return set_error(BQ_EARG, "%s: null y", where);
+        if (!aligned(y[i], 4))
+            return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
+        tiles += tiles_of(w[i].rows);
+    }
+    if (w[0].cols % qa)
+        return set_error(BQ_EARG, "%s: cols %lld not a multiple of qa %d", fn, (long long)w[0].cols, (int)qa);
+    const int tpw = tiles > kWideMaxTiles ? 2 : 0;  // 0: one tile per wide workgroup
+    const int per_wg = tpw ? tpw : 1;
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
+        bq_act none;
+        memset(&none, 0, sizeof none);
+        args.p[i] = make_desc(&w[i], &none, y[i]);
+        wgs += (tiles_of(w[i].rows) + per_wg - 1) / per_wg;
+        if (wgs >= (int64_t(1) << 31))
+            return set_error(BQ_EARG, "%s: too many rows", fn);
+        args.wg_end[i] = (int32_t)wgs;
+    }
+    args.x = x;
+    args.nprod = count;
+    return hip_check(fn, launch_group(fmt, qa, tpw, args, static_cast<hipStream_t>(s)));
 }
 
 BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan)

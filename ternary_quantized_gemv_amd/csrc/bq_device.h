@@ -39,6 +39,17 @@ __device__ __forceinline__ float scale_of(u32x4 sc, int b)
     return f16_bits_to_f32((b & 1) ? (sw >> 16) : (sw & 0xFFFFu));
 }
 
+// The activation quantizer's rule for one value x of a block whose scale is
+// db = amax / 127: x / db (correctly rounded) rounded half away from zero,
+// clamped to [-127, 127]; a zero block gives 0.
+__device__ __forceinline__ int quant_of(float x, float db)
+{
+    if (db == 0.0f)
+        return 0;
+    const float r = fminf(fmaxf(__builtin_roundf(x / db), -127.0f), 127.0f);
+    return (int)r;
+}
+
 // --------------------------------------------------------------- tables
 // Each thread writes one quarter (4 entries, 16 bytes) of a slot's table per
 // step, so a wavefront's stores cover 1 KiB of consecutive LDS addresses.

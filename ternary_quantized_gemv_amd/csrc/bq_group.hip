@@ -1,0 +1,510 @@
+// bq_group.hip -- one group of a dependency-ordered decode step in one
+// launch: the products that read the same activation (bankML "gpu/" page,
+// section "Limitations": Q/K/V, and gate/up, submitted together with one wait
+// per group) run from an f32 vector that each workgroup quantizes itself
+// while it fills its LDS table, so a group needs no separate quantizer launch
+// and the int8 vector never goes to memory.
+//
+// The block arithmetic is split_kernel's (bq_split.h): four wavefronts per
+// 64-row tile, one tile (or two, for groups with many tiles) per workgroup,
+// so the few hundred tiles of a decode group spread over the whole GPU.  Bits are those
+// of bq_quantize_act_q8 followed by bq_q1_0_matvec / bq_q2_0_matvec.
+#include "bq_device.h"
+#include "bq_launch.h"
+#include "bq_split.h"
+
+namespace bq {
+
+// The f32 activation values of one table chunk held by one thread: NT
+// threads take 8 consecutive values each per step.
+template <int FMT, int NT>
+struct XChunk {
+    static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
+    static constexpr int kSteps = (kChunkBlocks * BL + NT * 8 - 1) / (NT * 8);
+    f32x4 v[2 * kSteps];
+};
+
+// Load the values of chunk blocks cb .. cb + nbc - 1.  Every load is issued
+// (past the chunk's end a thread re-reads the chunk's last 8 values and
+// drops them), so the loads count the same on every path.
+template <int FMT, int NT>
+__device__ __forceinline__ void load_x(XChunk<FMT, NT> &xc, const float *__restrict__ x, int cb, int nbc)
+{
+    constexpr int BL = XChunk<FMT, NT>::BL;
+    const int nvals = nbc * BL;
+    const float *xp = x + (int64_t)cb * BL;
+#pragma unroll
+    for (int s = 0; s < XChunk<FMT, NT>::kSteps; ++s) {
+        const int v0 = min(s * NT * 8 + (int)threadIdx.x * 8, nvals - 8);
+        xc.v[2 * s] = *reinterpret_cast<const f32x4 *>(xp + v0);
+        xc.v[2 * s + 1] = *reinterpret_cast<const f32x4 *>(xp + v0 + 4);
+    }
+}
+
+// Fill the table (and D1) of a chunk of nbc blocks from the values in xc.
+// The QA / 8 threads of one activation block combine their |x| maxima with
+// butterfly shuffles (max is exact in any order), take d = amax / 127 and the
+// quants by the quantizer's rule (quant_of), and write the 16-entry tables of
+// the nibble slots their 8 values cover.  Quants lie in [-127, 127], so the
+// Q1_0 negation needs no -128 case.
+template <int FMT, int QA, int NT>
+__device__ __forceinline__ void build_x(float *T, float *D1, const XChunk<FMT, NT> &xc, int nbc)
+{
+    constexpr int kLanes = QA / 8;
+    const int nvals = nbc * XChunk<FMT, NT>::BL;
+#pragma unroll
+    for (int s = 0; s < XChunk<FMT, NT>::kSteps; ++s) {
+        const int v0 = s * NT * 8 + (int)threadIdx.x * 8;
+        const bool ok = v0 < nvals;  // whole activation blocks are in or out
+        const f32x4 a = xc.v[2 * s], b = xc.v[2 * s + 1];
+        float m = fmaxf(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))),
+                        fmaxf(fmaxf(fabsf(b[0]), fabsf(b[1])), fmaxf(fabsf(b[2]), fabsf(b[3]))));
+#pragma unroll
+        for (int off = 1; off < kLanes; off <<= 1)
+            m = fmaxf(m, __shfl_xor(m, off, 64));
+        if (!ok)
+            continue;
+        const float db = m / 127.0f;
+        int qv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qv[e] = quant_of(a[e], db);
+            qv[e + 4] = quant_of(b[e], db);
+        }
+        if (FMT == BQ_Q1_0) {
+            // slot t: values 4t .. 4t+3; entry 4h + e = sum of +-q_i by bit i
+            // of the nibble, times d1 on a block's first sub-block
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = v0 / 4 + u;
+                const int *qs = qv + 4 * u;
+                const bool first = ((t >> 3) & 3) == 0;
+                f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const int hi = ((h & 1) ? qs[2] : -qs[2]) + ((h & 2) ? qs[3] : -qs[3]);
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int lo = ((e & 1) ? qs[0] : -qs[0]) + ((e & 2) ? qs[1] : -qs[1]);
+                        const float sf = (float)(lo + hi);
+                        v[e] = first ? db * sf : sf;
+                    }
+                    dst[h] = v;
+                }
+            }
+            if ((v0 & 31) == 0)
+                D1[v0 / 32] = db;
+        } else {
+            // slot t: values 2t, 2t+1; entry 4h + e = (e-1) q_2t + (h-1) q_2t+1
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = v0 / 2 + u;
+                const int q0 = qv[2 * u], q1 = qv[2 * u + 1];
+                f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = (float)((e - 1) * q0 + (h - 1) * q1);
+                    dst[h] = v;
+                }
+            }
+            if ((v0 & 31) == 0) {
+                // d1 of sub-block j of block b at D1[4b + j], j = 0, 1; 2 and 3 unused
+                const int sb = v0 / 32;
+                D1[4 * (sb >> 1) + (sb & 1)] = db;
+                if ((sb & 1) == 0)
+                    D1[4 * (sb >> 1) + 2] = D1[4 * (sb >> 1) + 3] = 0.0f;
+            }
+        }
+    }
+}
+
+// One workgroup: TPW tiles of one product, four wavefronts per tile
+// (wavefront k: lane groups k and k + 4, as split_kernel).  Each wavefront
+// keeps kDepth blocks of its tile's payload (16 bytes per lane each) in
+// flight in a register ring: the first ones are requested with the
+// activation, before the table is built, and each block walked requests the
+// block kDepth ahead (across chunk ends), while the next chunk's activation
+// is requested as soon as the current table is built.
+constexpr int kDepth = 16;      // payload blocks in flight per wavefront
+constexpr int kScaleSlots = 4;  // scale groups held (the current one, two ahead, one spare)
+static_assert(kChunkBlocks % kDepth == 0 && kDepth % kGroup == 0, "ring slots must be static");
+
+template <int FMT, int QA, int TPW>
+__global__ __launch_bounds__(TPW * kSplit * 64) void group_kernel(GroupArgs a)
+{
+    constexpr int NT = TPW * kSplit * 64;
+    __shared__ float T[kTableFloats];
+    __shared__ float D1[kScaleFloats];
+    __shared__ float P[TPW][kSplit][64];
+    // the product of this workgroup (wave-uniform selects, no indexed copy)
+    const int wg = blockIdx.x;
+    GemvDesc g = a.p[0];
+    int wg0 = 0;
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < a.nprod && wg >= a.wg_end[i - 1]) {
+            g = a.p[i];
+            wg0 = a.wg_end[i - 1];
+        }
+    const int tiles = (g.rows + kTileRows - 1) / kTileRows;
+    const int tile0 = (wg - wg0) * TPW;
+    const int ntiles = min(TPW, tiles - tile0);
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int tl = wave / kSplit, k = wave % kSplit;
+    const int tile = tile0 + tl;
+    const bool live = tl < ntiles;
+    // a wavefront past the last tile reads the first tile and stores nothing
+    const rsrc_t wp = rsrc_of(g.bits + (int64_t)(live ? tile : tile0) * g.nb * kTileRows);
+    const rsrc_t sp = rsrc_of(g.scales + (int64_t)(live ? tile : tile0) * g.ng * kTileRows);
+    const uint32_t lo = (uint32_t)lane * 16;
+    const uint32_t sh = FMT == BQ_Q1_0 ? 8u * (k >> 1) + 4u * (k & 1) : 8u * k;
+    const int nb = g.nb, ng = g.ng;
+
+    // Requests go out in the order of use (vector memory counts complete in
+    // order): the chunk's activation, then per block its payload, preceded
+    // by the scale group it opens.  Every request is unconditional (past the
+    // row's end a wavefront re-reads its last block or chunk and drops it),
+    // so the counts are the same on every path.
+    XChunk<FMT, NT> xc;
+    u32x4 p[kDepth], sc[kScaleSlots];
+    // (scheduling barriers keep the compiler from reordering these requests)
+    load_x<FMT, NT>(xc, a.x, 0, min(kChunkBlocks, nb));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < kDepth; ++b) {
+        if (b % kGroup == 0)
+            sc[(b / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
+        p[b] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    float acc0 = 0.0f, acc1 = 0.0f;
+    for (int cb = 0; cb < nb; cb += kChunkBlocks) {
+        const int nbc = min(kChunkBlocks, nb - cb);
+        if (cb > 0)
+            __syncthreads();  // every wavefront is done with the previous table
+        build_x<FMT, QA, NT>(T, D1, xc, nbc);
+        __syncthreads();
+        // the next chunk's activation (the last chunk re-reads itself)
+        const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;
+        load_x<FMT, NT>(xc, a.x, nx, min(kChunkBlocks, nb - nx));
+#pragma unroll
+        for (int i = 0; i < kChunkBlocks; ++i) {
+            if (i < nbc)
+                split_block<FMT>(T, D1, i, p[i % kDepth], scale_of(sc[(i / kGroup) % kScaleSlots], i), k, sh, acc0,
+                                 acc1);
+            // block i + kDepth of the row takes the register block i leaves
+            const int b = cb + i + kDepth;
+            if ((i + kDepth) % kGroup == 0)
+                sc[((i + kDepth) / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
+            p[i % kDepth] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
+        }
+    }
+
+    P[tl][k][lane] = acc0 + acc1;  // p_k = a_k + a_(k+4)
+    __syncthreads();
+    if (k == 0 && live) {
+        const int row = tile * kTileRows + lane;
+        const float y = (P[tl][0][lane] + P[tl][2][lane]) + (P[tl][1][lane] + P[tl][3][lane]);
+        if (row < g.rows)
+            g.y[row] = y;
+    }
+}
+
+// ------------------------------------------------------------- wide tiles
+// One 64-row tile per workgroup of kWideWaves wavefronts, for groups whose
+// tiles are fewer than the GPU's compute units' worth of work.  A chunk runs
+// in three phases separated by barriers:
+//   A  every thread quantizes its share of the chunk's activation into the
+//      LDS table (build_x);
+//   B  wavefront w computes ab, the sub-block chain of all eight lane groups,
+//      of its two blocks 2w and 2w+1 for its 64 rows and puts them in LDS;
+//   C  wavefronts 0..7 (lane group L = w, row = lane) extend the block chain
+//      acc = fma(d0, ab, acc) over the chunk's blocks in order.
+// ab values are exact functions of one block, so computing them in parallel
+// changes nothing; the only sequential step, C, runs in block order as the
+// dot-product order prescribes.  The next chunk's activation, payload and
+// scales are requested as soon as the registers they replace are consumed.
+constexpr int kWideWaves = 16;
+constexpr int kWideThreads = kWideWaves * 64;
+static_assert(kChunkBlocks == 2 * kWideWaves, "two blocks per wavefront and chunk");
+
+// Phase A of the wide kernel: thread t owns nibble slot t of the chunk
+// (Q1_0: values 4t .. 4t+3; Q2_0: values 2t, 2t+1), so all sixteen
+// wavefronts share the work.  XSlot holds its values until the build.
+template <int FMT>
+struct XSlot {
+    static constexpr int V = FMT == BQ_Q1_0 ? 4 : 2;
+    float v[V];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restrict__ x, int cb, int nbc)
+{
+    constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64, V = XSlot<FMT>::V;
+    // past the chunk's end a thread re-reads the chunk's last slot (and drops it)
+    const int v0 = min((int)threadIdx.x * V, nbc * BL - V);
+    const float *xp = x + (int64_t)cb * BL + v0;
+    if (FMT == BQ_Q1_0) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(xp);
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            xs.v[i] = t[i];
+    } else {
+        const float2 t = *reinterpret_cast<const float2 *>(xp);
+        xs.v[0] = t.x;
+        xs.v[1] = t.y;
+    }
+}
+
+// The quantizer's per-block maximum (butterfly over the QA / V threads of an
+// activation block; max is exact in any order), its quants, and the slot's
+// 16-entry table.  Entries are sums of quants, exact in f32, formed from
+// converted quants; on a Q1_0 block's first sub-block they are multiplied by
+// d1 (one rounding, as the order prescribes).
+template <int FMT, int QA>
+__device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT> &xs, int nbc)
+{
+    constexpr int V = XSlot<FMT>::V, kLanes = QA / V;
+    const int t = threadIdx.x;
+    float m = fabsf(xs.v[0]);
+#pragma unroll
+    for (int i = 1; i < V; ++i)
+        m = fmaxf(m, fabsf(xs.v[i]));
+#pragma unroll
+    for (int off = 1; off < kLanes; off <<= 1)
+        m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (t >= nbc * kSlotsPerBlock)
+        return;
+    const float db = m / 127.0f;
+    float f[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        f[i] = (float)quant_of(xs.v[i], db);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+    if (FMT == BQ_Q1_0) {
+        // entry 4h + e: +-q0 +-q1 by bits 0, 1 of e, +-q2 +-q3 by bits 0, 1 of h
+        float lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo[e] = ((e & 1) ? f[0] : -f[0]) + ((e & 2) ? f[1] : -f[1]);
+            hi[e] = ((e & 1) ? f[2] : -f[2]) + ((e & 2) ? f[3] : -f[3]);
+        }
+        const bool first = ((t >> 3) & 3) == 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = first ? db * (lo[e] + hi[h]) : lo[e] + hi[h];
+            dst[h] = v;
+        }
+        if ((t & 7) == 0)
+            D1[t / 8] = db;
+    } else {
+        // entry 4h + e: (e-1) q0 + (h-1) q1
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = (float)(e - 1) * f[0] + (float)(h - 1) * f[1];
+            dst[h] = v;
+        }
+        if ((t & 15) == 0) {
+            // d1 of sub-block j of block b at D1[4b + j], j = 0, 1; 2 and 3 unused
+            const int sb = t / 16;
+            D1[4 * (sb >> 1) + (sb & 1)] = db;
+            if ((sb & 1) == 0)
+                D1[4 * (sb >> 1) + 2] = D1[4 * (sb >> 1) + 3] = 0.0f;
+        }
+    }
+}
+
+// ab of the eight lane groups of chunk block B (payload v) for the calling lane's row.
+template <int FMT, int B>
+__device__ __forceinline__ void block_ab(const float *__restrict__ T, const float *__restrict__ D1, u32x4 v,
+                                         float ab[8])
+{
+    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1 + 4 * B);
+    if (FMT == BQ_Q1_0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t wa = v[j];
+            const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+#pragma unroll
+            for (int L = 0; L < 8; ++L) {
+                const float t = tab(T, B * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1));
+                ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t wa = v[m];
+            const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+            const int j = m >> 1;
+#pragma unroll
+            for (int beta = 0; beta < 4; ++beta) {
+                const int L = 4 * (m & 1) + beta;
+                const int slot = B * kSlotsPerBlock + m * 8 + 2 * beta;
+                const float sv = tab(T, slot, nib4(wa, beta)) + tab(T, slot + 1, nib4(wb, beta));
+                ab[L] = j == 0 ? d1[0] * sv : __builtin_fmaf(d1[1], sv, ab[L]);
+            }
+        }
+    }
+}
+
+// Phase B for the wavefront whose blocks are W2 and W2 + 1.
+template <int FMT, int W2>
+__device__ __forceinline__ void phase_b(const float *__restrict__ T, const float *__restrict__ D1,
+                                        float (*AB)[8][64], const u32x4 (&v)[2], int nbc, int lane)
+{
+    float ab[8];
+    if (W2 < nbc) {
+        block_ab<FMT, W2>(T, D1, v[0], ab);
+#pragma unroll
+        for (int L = 0; L < 8; ++L)
+            AB[W2][L][lane] = ab[L];
+    }
+    if (W2 + 1 < nbc) {
+        block_ab<FMT, W2 + 1>(T, D1, v[1], ab);
+#pragma unroll
+        for (int L = 0; L < 8; ++L)
+            AB[W2 + 1][L][lane] = ab[L];
+    }
+}
+
+template <int FMT, int QA>
+__global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
+{
+    __shared__ float T[kTableFloats];
+    __shared__ float AB[kChunkBlocks][8][64];
+    __shared__ float D1[kScaleFloats];
+    const int wg = blockIdx.x;
+    GemvDesc g = a.p[0];
+    int wg0 = 0;
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < a.nprod && wg >= a.wg_end[i - 1]) {
+            g = a.p[i];
+            wg0 = a.wg_end[i - 1];
+        }
+    const int tile = wg - wg0;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const rsrc_t wp = rsrc_of(g.bits + (int64_t)tile * g.nb * kTileRows);
+    const rsrc_t sp = rsrc_of(g.scales + (int64_t)tile * g.ng * kTileRows);
+    const uint32_t lo = (uint32_t)lane * 16;
+    const int nb = g.nb, ng = g.ng;
+
+    // Requests in the order of use (vector memory counts complete in order);
+    // all unconditional, clamped to the row's last block / scale group.
+    XSlot<FMT> xs;
+    u32x4 v[2], sc[kChunkBlocks / kGroup];
+    auto request = [&](int cb) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            v[i] = bload(wp, lo, (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
+    };
+    auto request_scales = [&](int cb) {
+#pragma unroll
+        for (int j = 0; j < kChunkBlocks / kGroup; ++j)
+            sc[j] = bload(sp, lo, (uint32_t)min(cb / kGroup + j, ng - 1) * kStep);
+    };
+    load_slot<FMT>(xs, a.x, 0, min(kChunkBlocks, nb));
+    __builtin_amdgcn_sched_barrier(0);
+    request(0);
+    __builtin_amdgcn_sched_barrier(0);
+    request_scales(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float acc = 0.0f;  // wavefronts 0..7: lane group `wave` of row `lane`
+    for (int cb = 0; cb < nb; cb += kChunkBlocks) {
+        const int nbc = min(kChunkBlocks, nb - cb);
+        const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;  // the last chunk re-reads itself
+        // A
+        build_slot<FMT, QA>(T, D1, xs, nbc);
+        __syncthreads();
+        load_slot<FMT>(xs, a.x, nx, min(kChunkBlocks, nb - nx));
+        // B (wavefront-uniform dispatch, so that every table offset is a constant)
+        switch (wave) {
+#define BQ_PHASE_B(w) \
+    case w: phase_b<FMT, 2 * (w)>(T, D1, AB, v, nbc, lane); break;
+            BQ_PHASE_B(0) BQ_PHASE_B(1) BQ_PHASE_B(2) BQ_PHASE_B(3) BQ_PHASE_B(4) BQ_PHASE_B(5)
+            BQ_PHASE_B(6) BQ_PHASE_B(7) BQ_PHASE_B(8) BQ_PHASE_B(9) BQ_PHASE_B(10) BQ_PHASE_B(11)
+            BQ_PHASE_B(12) BQ_PHASE_B(13) BQ_PHASE_B(14) BQ_PHASE_B(15)
+#undef BQ_PHASE_B
+        default: break;
+        }
+        request(nx);
+        __syncthreads();
+        // C
+        if (wave < 8) {
+            // all reads first, then the chain; blocks past a short last chunk
+            // leave acc unchanged (a select, so the reads need no branches)
+            float abv[kChunkBlocks];
+#pragma unroll
+            for (int b = 0; b < kChunkBlocks; ++b)
+                abv[b] = AB[b][wave][lane];
+#pragma unroll
+            for (int b = 0; b < kChunkBlocks; ++b) {
+                const float next = __builtin_fmaf(scale_of(sc[b / kGroup], b), abv[b], acc);
+                acc = b < nbc ? next : acc;
+            }
+        }
+        request_scales(nx);
+        // the next chunk's phase A writes only T and D1, which phase C does not read;
+        // its barrier orders this phase C before the next phase B writes AB
+    }
+    __syncthreads();
+    if (wave < 8)
+        AB[0][wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        const int row = tile * kTileRows + lane;
+        const float y = ((AB[0][0][lane] + AB[0][4][lane]) + (AB[0][2][lane] + AB[0][6][lane])) +
+                        ((AB[0][1][lane] + AB[0][5][lane]) + (AB[0][3][lane] + AB[0][7][lane]));
+        if (row < g.rows)
+            g.y[row] = y;
+    }
+}
+
+template <int FMT>
+static void wide_qa(int qa, const GroupArgs &a, hipStream_t st)
+{
+    const dim3 grid(a.wg_end[a.nprod - 1]), block(kWideThreads);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((wide_kernel<FMT, 32>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((wide_kernel<FMT, 64>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((wide_kernel<FMT, 128>), grid, block, 0, st, a); break;
+    }
+}
+
+template <int FMT, int TPW>
+static void group_qa(int qa, const GroupArgs &a, hipStream_t st)
+{
+    const dim3 grid(a.wg_end[a.nprod - 1]), block(TPW * kSplit * 64);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((group_kernel<FMT, 32, TPW>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((group_kernel<FMT, 64, TPW>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((group_kernel<FMT, 128, TPW>), grid, block, 0, st, a); break;
+    }
+}
+
+hipError_t launch_group(int fmt, int qa, int tpw, const GroupArgs &a, hipStream_t st)
+{
+    if (tpw == 0)
+        fmt == BQ_Q1_0 ? wide_qa<BQ_Q1_0>(qa, a, st) : wide_qa<BQ_Q2_0>(qa, a, st);
+    else if (fmt == BQ_Q1_0)
+        tpw == 2 ? group_qa<BQ_Q1_0, 2>(qa, a, st) : group_qa<BQ_Q1_0, 1>(qa, a, st);
+    else
+        tpw == 2 ? group_qa<BQ_Q2_0, 2>(qa, a, st) : group_qa<BQ_Q2_0, 1>(qa, a, st);
+    return hipGetLastError();
+}
+
+}  // namespace bq

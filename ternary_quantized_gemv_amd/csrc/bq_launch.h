@@ -21,6 +21,10 @@ hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_
 // launch_cols: ncols columns, four per workgroup, one row per lane (bq_cols.hip).
 hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
                        hipStream_t st);
+// launch_group: a group of products sharing one f32 activation, quantized
+// inside the kernel; tpw = 0: one tile per sixteen-wavefront workgroup, else
+// tpw tiles (1 or 2) per workgroup of four wavefronts per tile (bq_group.hip).
+hipError_t launch_group(int fmt, int qa, int tpw, const GroupArgs &a, hipStream_t st);
 // launch_quantize: n values in blocks of qa (bq_quantize.hip).
 hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st);
 

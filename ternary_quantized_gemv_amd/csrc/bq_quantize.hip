@@ -24,15 +24,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     const float db = m / 127.0f;
     uint32_t packed = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        int qv = 0;
-        if (db != 0.0f) {
-            float r = __builtin_roundf(v[e] / db);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            qv = (int)r;
-        }
-        packed |= (uint32_t)(qv & 0xFF) << (8 * e);
-    }
+    for (int e = 0; e < 4; ++e)
+        packed |= (uint32_t)(quant_of(v[e], db) & 0xFF) << (8 * e);
     reinterpret_cast<uint32_t *>(q)[i] = packed;
     if ((i & (QA / 4 - 1)) == 0)
         d[i / (QA / 4)] = db;

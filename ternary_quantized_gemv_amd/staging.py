@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import Act, Weights, bq_quantize_act_q8, bq_sweep_create, bq_token_sweep, BLOCK_LEN
+from . import Act, GroupCall, Weights, bq_quantize_act_q8, bq_sweep_create, bq_token_sweep, BLOCK_LEN
 
 
 class StagedSweep:
@@ -108,15 +108,16 @@ def chain_groups(n_layers: int, lm_head: bool = True):
 
 
 class StagedChain:
-    """One decode token as a chain of dependent launches: for every group of
-    chain_groups(), one quantizer launch on the group's input (the previous
-    group's output) and one sweep launch over the group's products, all on
-    one stream.  Products of a group share one quantized activation."""
+    """One decode token as a chain of dependent launches over the groups of
+    chain_groups(), all on one stream.  fused=True: one bq_group_matvec launch
+    per group, which quantizes the group's input (the previous group's f32
+    output) inside the kernel.  fused=False: a bq_quantize_act_q8 launch into
+    an int8 buffer, then a sweep launch over the group's products."""
 
-    def __init__(self, fmt: int, canon, shapes, x0, qa: int = 128, n_layers: int = None):
+    def __init__(self, fmt: int, canon, shapes, x0, qa: int = 128, n_layers: int = None, fused: bool = True):
         import torch
 
-        self.fmt, self.qa = fmt, qa
+        self.fmt, self.qa, self.fused = fmt, qa, fused
         self.shapes = [(str(n), int(r), int(c)) for n, r, c in shapes]
         n_layers = (len(self.shapes) - 1) // 7 if n_layers is None else n_layers
         self.groups = chain_groups(n_layers, lm_head=len(self.shapes) == 7 * n_layers + 1)
@@ -133,35 +134,46 @@ class StagedChain:
             xin = self.x0 if src < 0 else self.output(src)
             if xin.numel() != cols:
                 raise ValueError("a group's input length must match its products")
-            q = torch.empty(cols, dtype=torch.int8, device="cuda")
-            d = torch.empty(cols // qa, dtype=torch.float32, device="cuda")
-            a = Act(q, d, cols, qa, 1)
-            plan = bq_sweep_create([(self.weights[p], a, self.output(p)) for p in prods])
-            self.stages.append((xin, q, d, plan))
+            if fused:
+                self.stages.append(GroupCall([self.weights[p] for p in prods], xin, qa,
+                                             [self.output(p) for p in prods]))
+            else:
+                q = torch.empty(cols, dtype=torch.int8, device="cuda")
+                d = torch.empty(cols // qa, dtype=torch.float32, device="cuda")
+                a = Act(q, d, cols, qa, 1)
+                plan = bq_sweep_create([(self.weights[p], a, self.output(p)) for p in prods])
+                self.stages.append((xin, q, d, plan))
 
     def output(self, i: int):
         return self.y[int(self.yoff[i]):int(self.yoff[i + 1])]
 
     def run(self, stream=None):
+        if self.fused:
+            for call in self.stages:
+                call.launch(stream)
+            return
         for xin, q, d, plan in self.stages:
             bq_quantize_act_q8(xin, self.qa, q, d, stream)
             bq_token_sweep(plan, stream)
 
     def launches(self) -> int:
-        return 2 * len(self.stages)
+        return len(self.stages) * (1 if self.fused else 2)
 
     def token_bytes(self) -> int:
-        """Algorithmic bytes of one token: weights, every activation quantized
-        (f32 read, int8 + f32 scales written, then read by the products) and
-        every output written."""
+        """Algorithmic bytes of one token: weights, every group's f32 input
+        read once and every output written; unfused, also the int8 quants and
+        scales written by the quantizer and read by each product."""
         n = 0
         for prods, _ in self.groups:
             cols = self.shapes[prods[0]][2]
-            n += 4 * cols + cols + 4 * (cols // self.qa)               # quantizer
-            n += len(prods) * (cols + 4 * (cols // self.qa))           # products read the activation
+            n += 4 * cols
+            if not self.fused:
+                n += cols + 4 * (cols // self.qa)                          # quantizer writes
+                n += len(prods) * (cols + 4 * (cols // self.qa))           # products read the activation
         return self.weight_bytes + n + 4 * int(self.yoff[-1])
 
     def close(self):
-        for _, _, _, plan in self.stages:
-            plan.destroy()
+        if not self.fused:
+            for _, _, _, plan in self.stages:
+                plan.destroy()
         self.stages = []

@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert bq.bq_abi_version() == 1
+    assert bq.bq_abi_version() == 2
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
@@ -125,6 +125,33 @@ def test_gpu_entry_points_validate_before_launch():
     assert lib.bq_sweep_create(arr, 2, ctypes.byref(plan)) == bq.BQ_EARG
     assert lib.bq_token_sweep(None, None) == bq.BQ_EARG
     lib.bq_sweep_destroy(None)
+
+
+def test_group_validates_before_launch():
+    """bq_group_matvec refuses bad groups on the host (no GPU is touched)."""
+    lib = bq.lib
+    W = bq.bq_weights * 5
+    P = ctypes.c_void_p * 5
+    w = W(*[bq.bq_weights(1, 0, 64, 256, 0x1000 * (i + 1), 0x9000) for i in range(5)])
+    y = P(*[0x20000 + 0x100 * i for i in range(5)])
+    x = ctypes.c_void_p(0x40000)
+    assert lib.bq_group_matvec(w, 0, x, 128, y, None) == bq.BQ_EARG
+    assert lib.bq_group_matvec(w, 5, x, 128, y, None) == bq.BQ_EARG and "count" in bq.bq_last_error()
+    assert lib.bq_group_matvec(None, 1, x, 128, y, None) == bq.BQ_EARG
+    assert lib.bq_group_matvec(w, 1, None, 128, y, None) == bq.BQ_EARG
+    assert lib.bq_group_matvec(w, 1, ctypes.c_void_p(0x40004), 128, y, None) == bq.BQ_EALIGN
+    assert lib.bq_group_matvec(w, 1, x, 96, y, None) == bq.BQ_EARG and "qa" in bq.bq_last_error()
+    w[1].fmt = 2
+    assert lib.bq_group_matvec(w, 2, x, 128, y, None) == bq.BQ_EARG and "product 1" in bq.bq_last_error()
+    w[1].fmt, w[2].cols = 1, 384
+    assert lib.bq_group_matvec(w, 3, x, 128, y, None) == bq.BQ_EARG and "cols" in bq.bq_last_error()
+    w[2].cols = 256
+    y[3] = 0
+    assert lib.bq_group_matvec(w, 4, x, 128, y, None) == bq.BQ_EARG and "product 3" in bq.bq_last_error()
+    y[3] = 0x20002
+    assert lib.bq_group_matvec(w, 4, x, 128, y, None) == bq.BQ_EALIGN
+    w[0].fmt = 3
+    assert lib.bq_group_matvec(w, 1, x, 128, y, None) == bq.BQ_EARG
 
 
 def test_host_tensors_are_refused():

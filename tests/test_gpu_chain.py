@@ -40,20 +40,21 @@ def oracle_chain(fmt, canon, shapes, x0, wiring, qa=128):
     return ys
 
 
-def _stage(fmt, n_layers, seed):
+def _stage(fmt, n_layers, seed, fused=True):
     from ternary_quantized_gemv_amd.staging import StagedChain, chain_groups
     assert chain_groups(n_layers) == chain_wiring(n_layers)
     shapes = synth.decode_sweep_shapes(n_layers)
     canon = [synth.blocks(fmt, r, c, seed, i) for i, (_, r, c) in enumerate(shapes)]
     x0 = synth.activation(shapes[0][2], seed, 999)
-    return StagedChain(fmt, canon, shapes, x0), canon, shapes, x0
+    return StagedChain(fmt, canon, shapes, x0, fused=fused), canon, shapes, x0
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "quantize+sweep"])
 @pytest.mark.parametrize("fmt,n_layers", [(1, 36), (2, 4)])
-def test_chain_against_oracle(fmt, n_layers):
+def test_chain_against_oracle(fmt, n_layers, fused):
     t = torch()
-    log(f"chain fmt={fmt} layers={n_layers}: staging")
-    ch, canon, shapes, x0 = _stage(fmt, n_layers, 71 + fmt)
+    log(f"chain fmt={fmt} layers={n_layers} fused={fused}: staging")
+    ch, canon, shapes, x0 = _stage(fmt, n_layers, 71 + fmt, fused)
     try:
         ch.run()
         t.cuda.synchronize()
@@ -72,11 +73,12 @@ def test_chain_against_oracle(fmt, n_layers):
         ch.close()
 
 
-def test_chain_graph_replay():
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "quantize+sweep"])
+def test_chain_graph_replay(fused):
     """Capture one chain in a graph; every replay, with eager work and
     synchronisation between replays, gives the eager chain's bits."""
     t = torch()
-    ch, _, _, _ = _stage(1, 2, 81)
+    ch, _, _, _ = _stage(1, 2, 81, fused)
     try:
         ch.run()
         t.cuda.synchronize()

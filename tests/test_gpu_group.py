@@ -1,0 +1,90 @@
+"""bq_group_matvec: the products of one decode group computed from an f32
+activation that the kernel quantizes itself.  Every output must equal the
+oracle's quantize_q8 followed by its matvec, bit for bit: ragged rows, one to
+four products, one to several table chunks and a short last chunk, every qa,
+activations with zero blocks, exact ties and subnormal scales, and the
+two-tiles-per-workgroup layout used by groups of more than 512 tiles."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bqmod, dev, log, torch
+from pins import same_bits
+
+pytestmark = pytest.mark.gpu
+
+THREADS = 16
+
+
+def group_input(fmt, cols, qa, regime, seed):
+    if regime == "layer":
+        return synth.layer_shaped(fmt, 1, cols, seed, qa)[1].astype(np.float32)
+    x = synth.activation(cols, seed, qa)
+    if regime == "special":
+        nblk = cols // qa
+        picks = [
+            lambda s: s.__setitem__(slice(None), 0.0),                                      # all-zero block
+            lambda s: s.__setitem__(slice(0, 6), [127.0, 2.5, -2.5, 0.5, -0.5, 1.5]),      # d = 1: ties
+            lambda s: s.__setitem__(slice(0, 3), [5207.0, 20.5, -20.5]),                    # d = 41: x/d = k + 1/2
+            lambda s: s.__imul__(np.float32(1e-40)),                                        # subnormal scale
+            lambda s: s.__setitem__(slice(None), -3.0),                                     # constant block
+        ]
+        for i in range(nblk):
+            blk = x[i * qa:(i + 1) * qa]
+            if i % 2 == 1 or nblk == 1:
+                picks[(i // 2) % len(picks)](blk)
+    return x
+
+
+# fmt, rows of each product, blocks per row, qa, regime
+CASES = [
+    (1, [1], 1, 128, "normal"),
+    (1, [1, 63, 65, 130], 3, 32, "special"),
+    (1, [300, 64], 96, 128, "normal"),        # three table chunks
+    (1, [200], 40, 64, "special"),            # a short last chunk (32 + 8 blocks)
+    (1, [4096, 1024, 1024], 32, 128, "layer"),
+    (2, [1, 63, 65, 130], 3, 32, "special"),
+    (2, [300, 64], 64, 128, "normal"),        # two table chunks
+    (2, [129], 37, 64, "layer"),              # 32 + 5 blocks
+    (2, [12288, 12288], 64, 128, "normal"),   # 384 tiles
+    (1, [20000, 16000, 700, 5], 2, 128, "normal"),  # 575 tiles: two per workgroup, odd counts
+    (2, [40000, 3], 4, 64, "special"),              # 626 tiles: two per workgroup
+]
+
+
+@pytest.mark.parametrize("fmt,rows,nb,qa,regime", CASES)
+def test_group_against_oracle(fmt, rows, nb, qa, regime):
+    t, bq = torch(), bqmod()
+    cols = nb * bq.BLOCK_LEN[fmt]
+    seed = 500 + 7 * fmt + nb
+    log(f"group fmt={fmt} rows={rows} cols={cols} qa={qa} {regime}")
+    canon = [synth.blocks(fmt, r, cols, seed, i) for i, r in enumerate(rows)]
+    x = group_input(fmt, cols, qa, regime, seed)
+    ws = [bq.Weights.upload(fmt, c, r, cols) for c, r in zip(canon, rows)]
+    ys = [t.full((r,), float("nan"), dtype=t.float32, device="cuda") for r in rows]
+    bq.bq_group_matvec(ws, dev(x), qa, ys)
+    t.cuda.synchronize()
+    q, d, clamped = oracle.quantize_q8(x, qa)
+    assert clamped == 0
+    for i, (c, r) in enumerate(zip(canon, rows)):
+        ref = oracle.matvec(fmt, c, r, cols, q, d, qa, threads=THREADS)[0]
+        got = ys[i].cpu().numpy()
+        assert same_bits(got, ref), f"product {i}: {np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32))} differ"
+
+
+def test_group_rejects_bad_arguments():
+    t, bq = torch(), bqmod()
+    w1 = bq.Weights.upload(1, synth.blocks(1, 64, 256, 1, 0), 64, 256)
+    w2 = bq.Weights.upload(2, synth.blocks(2, 64, 256, 1, 1), 64, 256)
+    w3 = bq.Weights.upload(1, synth.blocks(1, 64, 384, 1, 2), 64, 384)
+    x = t.zeros(256, device="cuda")
+    y = [t.zeros(64, device="cuda") for _ in range(5)]
+    for ws, qa, ys, what in [([w1, w2], 128, y[:2], "format"), ([w1, w3], 128, y[:2], "cols"),
+                             ([w1] * 5, 128, y, "count"), ([w1], 48, y[:1], "qa")]:
+        with pytest.raises(bq.BQError) as e:
+            bq.bq_group_matvec(ws, x, qa, ys)
+        assert e.value.code == bq.BQ_EARG and what in str(e.value), what
+    with pytest.raises(bq.BQError) as e:
+        bq.bq_group_matvec([w1], x[1:], 128, y[:1])
+    assert e.value.code in (bq.BQ_EARG, bq.BQ_EALIGN)
