@@ -250,7 +250,7 @@ __device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restric
     // past the chunk's end a thread re-reads the chunk's last slot (and drops it)
     const int v0 = min((int)threadIdx.x * V, nbc * BL - V);
     const float *xp = x + (int64_t)cb * BL + v0;
-    if (FMT == BQ_Q1_0) {
+    if constexpr (FMT == BQ_Q1_0) {
         const f32x4 t = *reinterpret_cast<const f32x4 *>(xp);
 #pragma unroll
         for (int i = 0; i < V; ++i)
@@ -287,7 +287,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     for (int i = 0; i < V; ++i)
         f[i] = (float)quant_of(xs.v[i], db);
     f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
-    if (FMT == BQ_Q1_0) {
+    if constexpr (FMT == BQ_Q1_0) {
         // entry 4h + e: +-q0 +-q1 by bits 0, 1 of e, +-q2 +-q3 by bits 0, 1 of h
         float lo[4], hi[4];
 #pragma unroll
