@@ -8,6 +8,8 @@ Weights are packed and copied to the GPU once, before timing; inputs are
 seeded synthetic data with the workload's shapes and distributions.
 
 Prints ONE JSON line.  python bench.py [--steps K] [--warmup W] [--fmt q1_0|q2_0]
+[--act q8_128|q8_0]: q8_0 quantizes with qa 32 and f16-valued scales (the
+pages' activation flavour) instead of qa 128 with f32 scales.
 
 Other workloads (each prints its own JSON line; not the headline):
   --workload gemv   single products at the configured shapes (Q1_0 4096x4096,
@@ -18,8 +20,9 @@ Other workloads (each prints its own JSON line; not the headline):
                     activation columns: us per call against the HBM and the
                     fp32 vector-ALU rooflines
   --workload chain  the token as 145 dependent groups (each group's
-                    activation is the quantized output of the previous one):
-                    ms per token launched eagerly and replayed from a graph
+                    activation is the quantized output of the previous one),
+                    one fused launch per group: ms per token launched eagerly
+                    and replayed from a graph, beside the two-launch version
 """
 from __future__ import annotations
 
@@ -78,7 +81,7 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
     the GPU's outputs for those products bit for bit."""
     import oracle
 
-    q_ref, d_ref, _ = oracle.quantize_q8(sw.x, sw.qa)
+    q_ref, d_ref, _ = oracle.quantize_q8(sw.x, sw.qa, sw.f16_scale)
     done_bytes = 0
     secs = 0.0
     mismatched = 0
@@ -284,6 +287,8 @@ def main():
     ap.add_argument("--fmt", choices=["q1_0", "q2_0"], default="q1_0")
     ap.add_argument("--workload", choices=["sweep", "gemv", "batch", "chain"], default="sweep")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--act", choices=["q8_128", "q8_0"], default="q8_128",
+                    help="sweep activations: qa 128 with f32 scales, or qa 32 with f16-valued scales")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -316,7 +321,8 @@ def main():
     t0 = time.time()
     canon = [synth.blocks(fmt, r, c, args.seed, i) for i, (_, r, c) in enumerate(shapes)]
     x = [synth.activation(c, args.seed, 1000 + i) for i, (_, _, c) in enumerate(shapes)]
-    sw = StagedSweep(fmt, canon, shapes, x, qa=128)
+    q8_0 = args.act == "q8_0"
+    sw = StagedSweep(fmt, canon, shapes, x, qa=32 if q8_0 else 128, f16_scale=q8_0)
     log(f"staged {len(shapes)} products, {sw.weight_bytes / 1e9:.3f} GB of weights in {time.time() - t0:.1f} s")
 
     stream = torch.cuda.current_stream()
@@ -379,7 +385,8 @@ def main():
         "config": {
             "workload": f"decode token, Qwen3-8B shapes, {fmt_name}: 36 x (q 4096x4096, k 1024x4096, "
                         "v 1024x4096, o 4096x4096, gate 12288x4096, up 12288x4096, down 4096x12288) "
-                        "+ lm_head 151936x4096 = 253 GEMVs, one activation vector each, qa 128",
+                        "+ lm_head 151936x4096 = 253 GEMVs, one activation vector each, "
+                        + ("qa 32 with f16-valued scales (q8_0)" if q8_0 else "qa 128"),
             "products": len(shapes),
             "weight_bytes": sw.weight_bytes,
             "step_bytes": step_bytes,
@@ -397,7 +404,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(fmt_name),
+            "traffic": None if q8_0 else measured_traffic(fmt_name),
             "algorithmic_bytes_per_launch": sw.sweep_bytes(),
         },
         "cpu_baseline": cpu,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 2
+#define BQ_ABI_VERSION 3
 
 /* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
  * then 16 payload bytes).
@@ -138,6 +138,20 @@ int bq_unpack(int32_t fmt, const void *bits, const uint16_t *scales, int64_t row
  * (device, 4-byte aligned) n / qa floats.  qa is 32, 64 or 128; n % qa == 0.
  * Non-finite inputs are outside the contract.  Asynchronous on s. */
 int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s);
+
+/* The same quantizer with f16-valued scales, the flavour of the pages' q8_0
+ * activation (bankML "gpu/", section "kernels.rs -- the Q1_0 kernels": the
+ * activation binding holds one scale per 32 values; section "Advantages and
+ * efficiency": d1*s is exact in f32, which holds when d1 has at most 11
+ * significant bits).  Per block of qa values: d = amax / 127 (correctly
+ * rounded), then narrowed to the nearest f16 value (ties to even) and stored
+ * widened in d; q = x / d (correctly rounded) rounded half away from zero,
+ * clamped to [-127, 127] -- the clamp can bind when d falls in the f16
+ * subnormal range (amax < 127 * 2^-14).  d == 0 (also when amax / 127
+ * narrows to 0) gives q = 0.  Blocks with amax / 127 >= 65520 (d = +inf)
+ * are outside the contract, as are non-finite inputs.  Arguments, alignment
+ * and errors as bq_quantize_act_q8.  Asynchronous on s. */
+int bq_quantize_act_q8_f16(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s);
 
 /* y (device, 4-byte aligned, a.ncols * w->rows floats; column c at
  * y + c * rows) = W times each activation column, in the order given at the

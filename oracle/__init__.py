@@ -43,9 +43,11 @@ class Oracle:
         lib = ctypes.CDLL(path)
         lib.oracle_f16_to_f32.restype = ctypes.c_float
         lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
-        lib.oracle_quantize_q8.restype = ctypes.c_int64
-        lib.oracle_quantize_q8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                           ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        for f in (lib.oracle_quantize_q8, lib.oracle_quantize_q8_f16):
+            f.restype = ctypes.c_int64
+            f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         for name in ("oracle_q1_0_row", "oracle_q2_0_row"):
             f = getattr(lib, name)
             f.restype = ctypes.c_float
@@ -69,15 +71,22 @@ class Oracle:
             out[i] = f(v)
         return out
 
-    def quantize_q8(self, x: np.ndarray, qa: int):
-        """Per-block int8 quantization: returns (q int8[n], d f32[n/qa], clamped count)."""
+    def f32_to_f16(self, values) -> np.ndarray:
+        """f16 bit patterns (uint16) of f32 values, nearest with ties to even."""
+        v = np.asarray(values, dtype=np.float32).ravel()
+        return np.array([self.lib.oracle_f32_to_f16(float(x)) for x in v], dtype=np.uint16)
+
+    def quantize_q8(self, x: np.ndarray, qa: int, f16_scale: bool = False):
+        """Per-block int8 quantization: returns (q int8[n], d f32[n/qa], clamped count).
+        f16_scale: the scales are rounded to f16 values first (reading R6)."""
         x = np.ascontiguousarray(x, dtype=np.float32).ravel()
         n = x.size
         if qa <= 0 or n % qa:
             raise ValueError("length must be a multiple of qa")
         q = np.empty(n, dtype=np.int8)
         d = np.empty(n // qa, dtype=np.float32)
-        clamped = self.lib.oracle_quantize_q8(_ptr(x), n, qa, _ptr(q), _ptr(d))
+        fn = self.lib.oracle_quantize_q8_f16 if f16_scale else self.lib.oracle_quantize_q8
+        clamped = fn(_ptr(x), n, qa, _ptr(q), _ptr(d))
         return q, d, int(clamped)
 
     def row(self, fmt: int, blocks: np.ndarray, q: np.ndarray, d: np.ndarray, qa: int) -> np.float32:
@@ -138,8 +147,12 @@ def f16_to_f32(bits):
     return default().f16_to_f32(bits)
 
 
-def quantize_q8(x, qa):
-    return default().quantize_q8(x, qa)
+def quantize_q8(x, qa, f16_scale=False):
+    return default().quantize_q8(x, qa, f16_scale)
+
+
+def f32_to_f16(values):
+    return default().f32_to_f16(values)
 
 
 def row(fmt, blocks, q, d, qa):

@@ -20,7 +20,9 @@
  *          sections "Summary" and "Technical usage" (rows are independent;
  *          16-row chunks handed out from an atomic counter).
  *   [VK]   vkML "Shaders and the GLSL layer", section "f16 is storage, never
- *          arithmetic" (an f16 load is an exact widening).
+ *          arithmetic" (an f16 load is an exact widening) and section "Why
+ *          f32->f16 narrowing is done in software" (narrowing rounds to
+ *          nearest, ties to even).
  *
  * Readings taken where the pages are silent:
  *   R1  Q1_0 block = f16 scale (little-endian) then 16 payload bytes; weight k
@@ -34,6 +36,11 @@
  *   R5  the accumulators start at +0; the activation scale of sub-block j is
  *       d[(first element of j) / qa]; Q2_0 follows the same chain over its
  *       two sub-blocks.
+ *   R6  the f16-scale flavour of the quantizer (the pages' q8_0 activation
+ *       carries f16-valued scales): d = f16(amax / 127), narrowed to nearest
+ *       with ties to even, and q = round-half-away(x / d) with that d,
+ *       clamped to [-127, 127] (the clamp can bind when d lands in the f16
+ *       subnormal range); d == 0 gives q == 0.
  */
 #include <math.h>
 #include <pthread.h>
@@ -66,11 +73,40 @@ float oracle_f16_to_f32(uint16_t h)
     return sign ? -v : v;
 }
 
+/* ---------------------------------------------------------------- f32 -> f16
+ * [VK] "Why f32->f16 narrowing is done in software": round to nearest, ties
+ * to even.  Written out from the binary16 definition: the value is scaled by
+ * a power of two (exact) so that the kept bits form an integer part, which
+ * rintf rounds in the default mode (nearest, ties to even).  Normal results
+ * keep 11 significant bits (exponent -14 .. 15); below 2^-14 the grid is
+ * m * 2^-24 (subnormals; m = 1024 is the smallest normal, same bits);
+ * beyond 65504 the value rounds to infinity from 65520 on. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    float a = fabsf(f);
+    if (isnan(f))
+        return sign | 0x7E00;
+    if (a >= 65520.0f)
+        return sign | 0x7C00;
+    if (a < ldexpf(1.0f, -14))
+        return sign | (uint16_t)rintf(ldexpf(a, 24));
+    int e;
+    frexpf(a, &e); /* a = m * 2^e, m in [0.5, 1): the leading bit has weight 2^(e-1) */
+    float m = rintf(ldexpf(a, 11 - e)); /* 11 significant bits: [1024, 2048] */
+    int ex = e - 1;
+    if (m == 2048.0f) {
+        m = 1024.0f;
+        ++ex;
+    }
+    return sign | (uint16_t)(((ex + 15) << 10) | ((int)m - 1024));
+}
+
 /* ------------------------------------------------------- activation quantizer
  * Reading R4 (the pages name a q8_0 activation with one scale per block, see
  * [GPU] "kernels.rs": activation scales and int8 quants).  Returns the number
  * of values the clamp had to change (0 for finite input). */
-int64_t oracle_quantize_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d)
+static int64_t quantize(const float *x, int64_t n, int32_t qa, int f16_scale, int8_t *q, float *d)
 {
     int64_t clamped = 0;
     for (int64_t b = 0; b * qa < n; ++b) {
@@ -82,6 +118,8 @@ int64_t oracle_quantize_q8(const float *x, int64_t n, int32_t qa, int8_t *q, flo
                 amax = a;
         }
         float db = amax / 127.0f;
+        if (f16_scale)
+            db = oracle_f16_to_f32(oracle_f32_to_f16(db)); /* reading R6 */
         d[b] = db;
         for (int32_t i = 0; i < qa; ++i) {
             int v = 0;
@@ -95,6 +133,17 @@ int64_t oracle_quantize_q8(const float *x, int64_t n, int32_t qa, int8_t *q, flo
         }
     }
     return clamped;
+}
+
+int64_t oracle_quantize_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d)
+{
+    return quantize(x, n, qa, 0, q, d);
+}
+
+/* Reading R6: the same with f16-valued scales. */
+int64_t oracle_quantize_q8_f16(const float *x, int64_t n, int32_t qa, int8_t *q, float *d)
+{
+    return quantize(x, n, qa, 1, q, d);
 }
 
 /* -------------------------------------------------------------- one Q1_0 row

@@ -26,7 +26,7 @@ BLOCK_BYTES = 18
 
 EXPORTS = (
     "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
-    "bq_quantize_act_q8", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
+    "bq_quantize_act_q8", "bq_quantize_act_q8_f16", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
     "bq_sweep_create", "bq_token_sweep", "bq_sweep_destroy",
 )
 
@@ -90,6 +90,8 @@ def _load() -> ctypes.CDLL:
     lib.bq_unpack.argtypes = [i32, vp, vp, i64, i64, vp]
     lib.bq_quantize_act_q8.restype = ctypes.c_int
     lib.bq_quantize_act_q8.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.bq_quantize_act_q8_f16.restype = ctypes.c_int
+    lib.bq_quantize_act_q8_f16.argtypes = [vp, i64, i32, vp, vp, vp]
     for f in (lib.bq_q1_0_matvec, lib.bq_q2_0_matvec):
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(bq_weights), ctypes.POINTER(bq_act), vp, vp]
@@ -171,6 +173,12 @@ def bq_quantize_act_q8(x, qa: int, q, d, stream=None) -> None:
     """x: float32 device tensor (n); q: int8 device tensor (n); d: float32 device tensor (n/qa)."""
     n = x.numel()
     _check(lib.bq_quantize_act_q8(_dev(x, "x"), n, qa, _dev(q, "q"), _dev(d, "d"), _stream(stream)))
+
+
+def bq_quantize_act_q8_f16(x, qa: int, q, d, stream=None) -> None:
+    """As bq_quantize_act_q8, with the scales narrowed to f16 values."""
+    n = x.numel()
+    _check(lib.bq_quantize_act_q8_f16(_dev(x, "x"), n, qa, _dev(q, "q"), _dev(d, "d"), _stream(stream)))
 
 
 class Weights:

@@ -141,9 +141,9 @@ struct bq_sweep {
     const WorkItem *items;
 };
 
-BQ_EXPORT int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s)
+static int quantize_entry(const char *fn, const float *x, int64_t n, int32_t qa, bool f16_scale, int8_t *q,
+                          float *d, bq_stream s)
 {
-    const char *fn = "bq_quantize_act_q8";
     if (qa != 32 && qa != 64 && qa != 128)
         return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)qa);
     if (n < 0 || n % qa)
@@ -154,7 +154,17 @@ BQ_EXPORT int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *
         return set_error(BQ_EALIGN, "%s: x must be 16-byte aligned, q and d 4-byte aligned", fn);
     if (n == 0)
         return BQ_OK;
-    return hip_check(fn, launch_quantize(x, n, qa, q, d, static_cast<hipStream_t>(s)));
+    return hip_check(fn, launch_quantize(x, n, qa, f16_scale, q, d, static_cast<hipStream_t>(s)));
+}
+
+BQ_EXPORT int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s)
+{
+    return quantize_entry("bq_quantize_act_q8", x, n, qa, false, q, d, s);
+}
+
+BQ_EXPORT int bq_quantize_act_q8_f16(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s)
+{
+    return quantize_entry("bq_quantize_act_q8_f16", x, n, qa, true, q, d, s);
 }
 
 BQ_EXPORT int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)

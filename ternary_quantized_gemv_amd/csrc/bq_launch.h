@@ -25,7 +25,7 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // inside the kernel; tpw = 0: one tile per sixteen-wavefront workgroup, else
 // tpw tiles (1 or 2) per workgroup of four wavefronts per tile (bq_group.hip).
 hipError_t launch_group(int fmt, int qa, int tpw, const GroupArgs &a, hipStream_t st);
-// launch_quantize: n values in blocks of qa (bq_quantize.hip).
-hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st);
+// launch_quantize: n values in blocks of qa, f32 or f16-valued scales (bq_quantize.hip).
+hipError_t launch_quantize(const float *x, int64_t n, int qa, bool f16_scale, int8_t *q, float *d, hipStream_t st);
 
 }  // namespace bq

@@ -1,5 +1,6 @@
 // bq_quantize.hip -- the activation quantizer: per block of qa values,
-// d = amax / 127 and q = round-half-away(x / d).
+// d = amax / 127 (optionally narrowed to an f16 value, nearest with ties to
+// even) and q = round-half-away(x / d).
 #include "bq_device.h"
 #include "bq_launch.h"
 
@@ -7,7 +8,7 @@ namespace bq {
 
 // Each thread quantizes 4 consecutive values; QA/4 threads share a block and
 // combine their |x| maxima with butterfly shuffles (max is exact in any order).
-template <int QA>
+template <int QA, bool F16>
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ x, int64_t n4, int8_t *__restrict__ q,
                                                        float *__restrict__ d)
 {
@@ -21,7 +22,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
         m = fmaxf(m, __shfl_xor(m, off, 64));
     if (i >= n4)
         return;
-    const float db = m / 127.0f;
+    float db = m / 127.0f;
+    if (F16)
+        db = (float)(_Float16)db;  // v_cvt_f16_f32 rounds to nearest even; the widening is exact
     uint32_t packed = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -31,15 +34,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
         d[i / (QA / 4)] = db;
 }
 
-hipError_t launch_quantize(const float *x, int64_t n, int qa, int8_t *q, float *d, hipStream_t st)
+template <bool F16>
+static void quantize_qa(const float *x, int64_t n4, int qa, int8_t *q, float *d, hipStream_t st)
 {
-    const int64_t n4 = n / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256));
     switch (qa) {
-    case 32: hipLaunchKernelGGL((quantize_kernel<32>), grid, dim3(256), 0, st, x, n4, q, d); break;
-    case 64: hipLaunchKernelGGL((quantize_kernel<64>), grid, dim3(256), 0, st, x, n4, q, d); break;
-    default: hipLaunchKernelGGL((quantize_kernel<128>), grid, dim3(256), 0, st, x, n4, q, d); break;
+    case 32: hipLaunchKernelGGL((quantize_kernel<32, F16>), grid, dim3(256), 0, st, x, n4, q, d); break;
+    case 64: hipLaunchKernelGGL((quantize_kernel<64, F16>), grid, dim3(256), 0, st, x, n4, q, d); break;
+    default: hipLaunchKernelGGL((quantize_kernel<128, F16>), grid, dim3(256), 0, st, x, n4, q, d); break;
     }
+}
+
+hipError_t launch_quantize(const float *x, int64_t n, int qa, bool f16_scale, int8_t *q, float *d, hipStream_t st)
+{
+    f16_scale ? quantize_qa<true>(x, n / 4, qa, q, d, st) : quantize_qa<false>(x, n / 4, qa, q, d, st);
     return hipGetLastError();
 }
 

@@ -11,17 +11,20 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import Act, GroupCall, Weights, bq_quantize_act_q8, bq_sweep_create, bq_token_sweep, BLOCK_LEN
+from . import (Act, GroupCall, Weights, bq_quantize_act_q8, bq_quantize_act_q8_f16, bq_sweep_create,
+               bq_token_sweep, BLOCK_LEN)
 
 
 class StagedSweep:
-    def __init__(self, fmt: int, canon, shapes, x, qa: int = 128, keep_host: bool = True):
+    def __init__(self, fmt: int, canon, shapes, x, qa: int = 128, keep_host: bool = True,
+                 f16_scale: bool = False):
         """fmt: BQ_Q1_0 / BQ_Q2_0; canon: list of uint8 [rows, cols/QK, 18];
         shapes: list of (name, rows, cols); x: list of float32 [cols] (or one
-        concatenated float32 array)."""
+        concatenated float32 array); f16_scale: quantize with f16-valued
+        scales (bq_quantize_act_q8_f16, the q8_0 flavour)."""
         import torch
 
-        self.fmt, self.qa = fmt, qa
+        self.fmt, self.qa, self.f16_scale = fmt, qa, f16_scale
         self.shapes = [(str(n), int(r), int(c)) for n, r, c in shapes]
         for _, _, cols in self.shapes:
             if cols % qa or cols % BLOCK_LEN[fmt]:
@@ -56,7 +59,7 @@ class StagedSweep:
 
     # ------------------------------------------------------------- running
     def quantize(self, stream=None):
-        bq_quantize_act_q8(self.xd, self.qa, self.q, self.d, stream)
+        (bq_quantize_act_q8_f16 if self.f16_scale else bq_quantize_act_q8)(self.xd, self.qa, self.q, self.d, stream)
 
     def sweep(self, stream=None):
         bq_token_sweep(self.plan, stream)

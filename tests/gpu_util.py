@@ -60,14 +60,14 @@ class SweepWorkload:
     """Seeded products (the 253 of one decode token, or any list of shapes)
     staged on the GPU, one float32 N(0, 1) activation vector per product."""
 
-    def __init__(self, fmt: int, shapes, seed: int, qa: int = 128):
+    def __init__(self, fmt: int, shapes, seed: int, qa: int = 128, f16_scale: bool = False):
         from ternary_quantized_gemv_amd.staging import StagedSweep
         shapes = list(shapes)
         canon = [synth.blocks(fmt, r, c, seed, i) for i, (_, r, c) in enumerate(shapes)]
         x = [synth.activation(c, seed, 1000 + i) for i, (_, _, c) in enumerate(shapes)]
-        self.s = StagedSweep(fmt, canon, shapes, x, qa)
+        self.s = StagedSweep(fmt, canon, shapes, x, qa, f16_scale=f16_scale)
         s = self.s
-        self.fmt, self.shapes, self.qa = fmt, shapes, qa
+        self.fmt, self.shapes, self.qa, self.f16_scale = fmt, shapes, qa, f16_scale
         self.canon, self.weights, self.entries = s.canon, s.weights, s.entries
         self.koff, self.yoff, self.x = s.koff, s.yoff, s.x
         self.q, self.d, self.y = s.q, s.d, s.y

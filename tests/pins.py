@@ -10,6 +10,15 @@ What pins what:
                  rounded first product, the fused inner and outer steps, the
                  final tree, the lane grouping, the int8 wrap, the Q2_0 code map
   f16            every one of the 65,536 f16 patterns against numpy's widening
+  f16 narrowing  f32 -> f16 against numpy's narrowing (nearest, ties to even):
+                 every f16 value, every midpoint between neighbours, both
+                 sides of each midpoint, random values over all exponents
+  quantizer_f16  f16-scale flavour: d is the f16 nearest to amax/127 (exact
+                 rationals), quants nearest to x/d, ties away, the clamp at
+                 subnormal scales, zero blocks, d = 0 when amax/127 narrows to 0
+  f16_merge      with f16-valued scales one per block, d1*s is exact, so the
+                 sub-blocks of a block can be taken in any order without
+                 changing a bit (and with f32 scales they cannot)
   quantizer      ties, amax -> 127, zero blocks, the correctly rounded scale,
                  nearest-integer property checked in exact rationals, 2x scaling
   exact_q1/q2    power-of-two scales make every float step exact, so the output
@@ -75,6 +84,34 @@ def check_f16(o):
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _f16_grid_values():
+    """Every finite f16 value, as f32."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16).astype(np.float32)
+    return v[np.isfinite(v)]
+
+
+def check_f16_narrowing(o):
+    fin = _f16_grid_values()
+    pos = np.unique(fin[fin >= 0])                       # 0 .. 65504, ascending
+    mids = ((pos[:-1].astype(np.float64) + pos[1:]) / 2).astype(np.float32)  # exact in f32
+    assert np.array_equal(mids.astype(np.float64), (pos[:-1].astype(np.float64) + pos[1:]) / 2)
+    up = np.nextafter(mids, np.float32(np.inf))
+    down = np.nextafter(mids, np.float32(-np.inf))
+    g = np.random.default_rng(5)
+    rnd = (g.uniform(1, 2, 20000) * 2.0 ** g.integers(-30, 17, 20000)).astype(np.float32)
+    tail = np.array([65504, 65519, 65519.996, 65520, 65536, 1e9, np.inf, 2.0 ** -25, 2.0 ** -26,
+                     np.float32(2.0 ** -25) * np.float32(1.0000001)], np.float32)
+    v = np.concatenate([fin, mids, up, down, rnd, -rnd, tail, -tail])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = o.f32_to_f16(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(v[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
+    nan = o.f32_to_f16(np.array([np.nan], np.float32))[0]
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
 
 
 # ------------------------------------------------------------------ quantizer
@@ -273,6 +310,78 @@ def check_scaling(o, fmt, rows=30, cols=512, qa=128, seed=18):
                      o.matvec(fmt, w, rows, cols, q, d, qa)[0] * np.float32(2.0))
 
 
+def _f16_neighbours(d: float):
+    """The f16 values just below and above (or equal to) the positive value d."""
+    fin = np.unique(_f16_grid_values())
+    i = np.searchsorted(fin, d)
+    return [float(fin[j]) for j in (i - 1, i, i + 1) if 0 <= j < fin.size]
+
+
+def check_quantizer_f16(o, seed: int = 11):
+    # ties and exact scales carry over: amax = 127 gives d = 1, an f16 value
+    x = np.zeros(128, np.float32)
+    x[:6] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5]
+    q, d, c = o.quantize_q8(x, 128, f16_scale=True)
+    assert d[0] == 1.0 and c == 0 and q[:6].tolist() == [127, 3, -3, 1, -1, 2]
+    # realistic blocks, a tiny block (subnormal f16 scale, clamp binds) and a zero block
+    x = np.concatenate([synth.activation(2048, seed, 0), synth.layer_shaped(Q1_0, 1, 1024, seed, 1)[1],
+                        synth.activation(32, seed, 2) * np.float32(1e-6), np.zeros(32, np.float32),
+                        np.full(32, 1e-9, np.float32)])
+    qa = 32
+    q, d, clamped = o.quantize_q8(x, qa, f16_scale=True)
+    assert q.min() >= -127 and q.max() <= 127
+    for b in range(x.size // qa):
+        xb = x[b * qa:(b + 1) * qa]
+        amax = Fraction(float(np.abs(xb).max()))
+        # d is an f16 value, and the nearest one to the correctly rounded amax / 127
+        assert o.f32_to_f16(d[b:b + 1]).view(np.float16).astype(np.float32)[0] == d[b]
+        d32 = np.float32(np.abs(xb).max()) / np.float32(127.0)
+        assert _correctly_rounded_div(np.abs(xb).max(), 127.0, d32)
+        near = min(_f16_neighbours(float(d32)), key=lambda v: (abs(Fraction(v) - Fraction(float(d32)))))
+        assert abs(Fraction(float(d[b])) - Fraction(float(d32))) == abs(Fraction(near) - Fraction(float(d32))), b
+        if d[b] == 0:
+            assert not q[b * qa:(b + 1) * qa].any()
+            continue
+        db = Fraction(float(d[b]))
+        for k in range(qa):
+            r = Fraction(float(xb[k])) / db
+            if abs(r) > 127 + Fraction(1, 2):
+                assert abs(int(q[b * qa + k])) == 127 and (int(q[b * qa + k]) > 0) == (r > 0), (b, k)
+                continue
+            dist = abs(r - int(q[b * qa + k]))
+            assert dist <= Fraction(1, 2) + Fraction(1, 1 << 17), (b, k)
+    assert clamped > 0          # the 1e-6 block: d is an f16 subnormal, too coarse for 127 steps
+    assert d[-1] == 0.0 and d[-2] == 0.0   # 1e-9 / 127 narrows to 0; the zero block
+
+
+def _permute_sub_blocks(w: np.ndarray, x: np.ndarray, perm):
+    """Q1_0 rows (canonical blocks) and an activation with the four 32-weight
+    sub-blocks of every block taken in the order perm."""
+    w2 = w.copy()
+    pay = w[:, :, 2:].reshape(w.shape[0], w.shape[1], 4, 4)   # sub-block j = payload bytes 4j..4j+3
+    w2[:, :, 2:] = pay[:, :, perm, :].reshape(w.shape[0], w.shape[1], 16)
+    xb = x.reshape(-1, 4, 32)[:, perm, :].reshape(-1)
+    return w2, xb
+
+
+def check_f16_merge(o, seed: int = 12):
+    rows, nb = 64, 16
+    cols = nb * 128
+    w = synth.q1_0_blocks(rows, cols, seed, 0)
+    x = synth.activation(cols, seed, 1)
+    perm = [2, 0, 3, 1]
+    w2, x2 = _permute_sub_blocks(w, x, perm)
+    # f16-valued scales, one per 128 values: every partial sum d1*(s0+..+sj) is exact
+    q, d, _ = o.quantize_q8(x, 128, f16_scale=True)
+    q2, d2, _ = o.quantize_q8(x2, 128, f16_scale=True)
+    assert same_bits(d, d2)
+    assert same_bits(o.matvec(Q1_0, w, rows, cols, q, d, 128), o.matvec(Q1_0, w2, rows, cols, q2, d2, 128))
+    # with f32 scales the inner chain rounds, and the order shows in some rows
+    q, d, _ = o.quantize_q8(x, 128)
+    q2, d2, _ = o.quantize_q8(x2, 128)
+    assert not same_bits(o.matvec(Q1_0, w, rows, cols, q, d, 128), o.matvec(Q1_0, w2, rows, cols, q2, d2, 128))
+
+
 def check_cover(o):
     for t in (1, 2, 3, 5):
         for rows in (0, 1, 15, 16, 17, 100, 1000):
@@ -288,6 +397,9 @@ ALL_CHECKS = [
     ("quantizer_zero_block", check_quantizer_zero_block),
     ("quantizer_properties", check_quantizer_properties),
     ("quantizer_scaling", check_quantizer_scaling),
+    ("f16_narrowing", check_f16_narrowing),
+    ("quantizer_f16", check_quantizer_f16),
+    ("f16_merge", check_f16_merge),
     ("exact_q1", lambda o: check_exact(o, Q1_0)),
     ("exact_q2", lambda o: check_exact(o, Q2_0)),
     ("exact_q1_qa128", lambda o: check_exact(o, Q1_0, rows=64, cols=128, qa=128)),

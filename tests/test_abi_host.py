@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert bq.bq_abi_version() == 2
+    assert bq.bq_abi_version() == 3
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
@@ -90,6 +90,12 @@ def test_gpu_entry_points_validate_before_launch():
     assert lib.bq_quantize_act_q8(None, 256, 32, x, x, None) == bq.BQ_EARG
     assert lib.bq_quantize_act_q8(ctypes.c_void_p(0x1004), 256, 32, x, x, None) == bq.BQ_EALIGN
     assert lib.bq_quantize_act_q8(x, 0, 32, x, x, None) == bq.BQ_OK  # empty input: nothing to do
+    assert lib.bq_quantize_act_q8_f16(x, 256, 33, x, x, None) == bq.BQ_EARG
+    assert "bq_quantize_act_q8_f16" in bq.bq_last_error() and "qa" in bq.bq_last_error()
+    assert lib.bq_quantize_act_q8_f16(x, 100, 32, x, x, None) == bq.BQ_EARG
+    assert lib.bq_quantize_act_q8_f16(x, 256, 32, None, x, None) == bq.BQ_EARG
+    assert lib.bq_quantize_act_q8_f16(ctypes.c_void_p(0x1008), 256, 32, x, x, None) == bq.BQ_EALIGN
+    assert lib.bq_quantize_act_q8_f16(x, 0, 32, x, x, None) == bq.BQ_OK
 
     w = bq.bq_weights(1, 0, 64, 256, 0x1000, 0x2000)
     a = bq.bq_act(0x3000, 0x4000, 256, 128, 1, 256, 2)

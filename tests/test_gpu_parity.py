@@ -220,16 +220,16 @@ def test_small_batch_full_size(fmt, rows):
 
 
 # ------------------------------------------------------------ token sweeps
-def _check_sweep(fmt, shapes, seed):
+def _check_sweep(fmt, shapes, seed, qa=128, f16_scale=False):
     t = torch()
-    log(f"sweep fmt={fmt}: staging {len(shapes)} products")
-    wl = SweepWorkload(fmt, shapes, seed)
+    log(f"sweep fmt={fmt} qa={qa} f16_scale={f16_scale}: staging {len(shapes)} products")
+    wl = SweepWorkload(fmt, shapes, seed, qa, f16_scale)
     try:
         wl.run()
         t.cuda.synchronize()
         y = wl.y.cpu().numpy()
         q_gpu, d_gpu = wl.q.cpu().numpy(), wl.d.cpu().numpy()
-        q_ref, d_ref, _ = oracle.quantize_q8(wl.x, wl.qa)
+        q_ref, d_ref, _ = oracle.quantize_q8(wl.x, wl.qa, f16_scale)
         assert np.array_equal(q_gpu, q_ref) and same_bits(d_gpu, d_ref)
         bad = 0
         for i, (name, rows, cols) in enumerate(shapes):

@@ -34,6 +34,12 @@ MUTANTS = [
     ("quant_divisor_128", "float db = amax / 127.0f;", "float db = amax / 128.0f;"),
     ("quant_multiply_by_reciprocal", "float r = roundf(xb[i] / db);", "float r = roundf(xb[i] * (1.0f / db));"),
     ("f16_subnormal_wrong", "v = ldexpf((float)m, -24);", "v = ldexpf((float)m, -25);"),
+    ("f16_narrow_truncates", "float m = rintf(ldexpf(a, 11 - e));", "float m = floorf(ldexpf(a, 11 - e));"),
+    ("f16_narrow_ties_away", "float m = rintf(ldexpf(a, 11 - e));", "float m = roundf(ldexpf(a, 11 - e));"),
+    ("f16_narrow_subnormal_grid", "return sign | (uint16_t)rintf(ldexpf(a, 24));",
+     "return sign | (uint16_t)rintf(ldexpf(a, 23));"),
+    ("f16_narrow_overflow_early", "if (a >= 65520.0f)", "if (a >= 65504.0f)"),
+    ("quant_f16_scale_ignored", "db = oracle_f16_to_f32(oracle_f32_to_f16(db)); /* reading R6 */", "db = db;"),
     ("f16_bias_wrong", "v = ldexpf((float)(1024 + m), e - 25);", "v = ldexpf((float)(1024 + m), e - 24);"),
     ("acc_starts_at_minus_zero_sign_flip", "acc[L] = 0.0f;\n    for (int64_t b = 0; b < nb; ++b) {\n        const uint8_t *blk = blocks + b * ORACLE_BLOCK_BYTES;\n        float d0 = oracle_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));\n        const uint8_t *qs = blk + 2;\n        float ab[8];\n        for (int j = 0; j < 4; ++j) {",
      "acc[L] = 0.0f;\n    for (int64_t b = 0; b < nb; ++b) {\n        const uint8_t *blk = blocks + b * ORACLE_BLOCK_BYTES;\n        float d0 = -oracle_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));\n        const uint8_t *qs = blk + 2;\n        float ab[8];\n        for (int j = 0; j < 4; ++j) {"),
