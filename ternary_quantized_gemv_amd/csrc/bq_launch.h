@@ -6,6 +6,19 @@
 
 namespace bq {
 
+// The products of one decode-group launch (bq_group.hip): they share the f32
+// activation x, which every workgroup quantizes for itself.  Product i owns
+// workgroups wg_end[i-1] .. wg_end[i] - 1 (wg_end[-1] = 0); q and d of p[i]
+// are unused.
+constexpr int kGroupMax = 4;
+struct GroupArgs {
+    GemvDesc p[kGroupMax];
+    int32_t wg_end[kGroupMax];
+    const float *x;
+    int32_t nprod;
+    int32_t pad;
+};
+
 // Kernel launchers (host side).  Each validates nothing: the entry points in
 // bq_api.cpp check every argument first.  They return hipGetLastError().
 //

@@ -1,6 +1,7 @@
 // bq_types.h -- internal to libbq: types and sizes shared by the kernel
 // sources (bq_sweep.hip, bq_cols.hip, bq_group.hip, bq_quantize.hip) and the C ABI entry
-// points (bq_api.cpp).  The launchers are declared in bq_launch.h.
+// points (bq_api.cpp).  The launchers, and the argument block of the decode
+// group kernels, are declared in bq_launch.h.
 //
 // Every output row is computed in the dot-product order of bankML's GPU page
 // ("gpu/ -- the video-card component", section "kernels.rs -- the Q1_0
@@ -61,17 +62,5 @@ struct WorkItem {
 };
 constexpr int kSplit = 4;                     // wavefronts per tile of split_kernel
 constexpr int kSplitTiles = kWaves / kSplit;  // tiles per split_kernel workgroup
-
-// The products of one group_kernel launch: they share the f32 activation x,
-// which every workgroup quantizes for itself.  Product i owns workgroups
-// wg_end[i-1] .. wg_end[i] - 1 (wg_end[-1] = 0); q and d of p[i] are unused.
-constexpr int kGroupMax = 4;
-struct GroupArgs {
-    GemvDesc p[kGroupMax];
-    int32_t wg_end[kGroupMax];
-    const float *x;
-    int32_t nprod;
-    int32_t pad;
-};
 
 }  // namespace bq
