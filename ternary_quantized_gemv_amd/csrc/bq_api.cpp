@@ -28,10 +28,15 @@ namespace bq {
 //   parallelism wins.
 constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
-// bq_group_matvec: groups of at most kWideMaxTiles tiles give each tile a
-// workgroup of sixteen wavefronts (wide_kernel), larger groups put two tiles
-// in a workgroup of eight (group_kernel): once the GPU is full, fewer table
-// builds win over more wavefronts per tile.
+// bq_group_matvec (measured on MI355X): groups of at most kHalfMaxTiles
+// tiles give each half tile a workgroup of sixteen wavefronts (wide_kernel),
+// so that they spread over more compute units; larger groups give each
+// sixteen-wavefront workgroup two tiles in turn (one table build serves
+// both), except single-chunk rows of groups beyond kWideMaxTiles, which run
+// two tiles per workgroup of eight wavefronts (group_kernel): there the GPU
+// is full anyway and the shorter phases of the wide shape do not pay for
+// its barriers.
+constexpr int kHalfMaxTiles = 128;
 constexpr int kWideMaxTiles = 512;
 
 // ------------------------------------------------------------ validation
@@ -214,21 +219,24 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
     }
     if (w[0].cols % qa)
         return set_error(BQ_EARG, "%s: cols %lld not a multiple of qa %d", fn, (long long)w[0].cols, (int)qa);
-    const int tpw = tiles > kWideMaxTiles ? 2 : 0;  // 0: one tile per wide workgroup
-    const int per_wg = tpw ? tpw : 1;
+    const bool one_chunk = w[0].cols / block_len(fmt) <= kChunkBlocks;
+    const GroupShape shape = tiles <= kHalfMaxTiles                 ? kShapeHalf
+                             : tiles <= kWideMaxTiles || !one_chunk ? kShapeWide2
+                                                                    : kShapePair;
     int64_t wgs = 0;
     for (int i = 0; i < count; ++i) {
         bq_act none;
         memset(&none, 0, sizeof none);
         args.p[i] = make_desc(&w[i], &none, y[i]);
-        wgs += (tiles_of(w[i].rows) + per_wg - 1) / per_wg;
+        const int64_t t = tiles_of(w[i].rows);
+        wgs += shape == kShapeHalf ? 2 * t : (t + 1) / 2;  // kShapeWide2, kShapePair: two tiles each
         if (wgs >= (int64_t(1) << 31))
             return set_error(BQ_EARG, "%s: too many rows", fn);
         args.wg_end[i] = (int32_t)wgs;
     }
     args.x = x;
     args.nprod = count;
-    return hip_check(fn, launch_group(fmt, qa, tpw, args, static_cast<hipStream_t>(s)));
+    return hip_check(fn, launch_group(fmt, qa, shape, args, static_cast<hipStream_t>(s)));
 }
 
 BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan)

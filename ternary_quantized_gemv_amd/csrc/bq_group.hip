@@ -217,15 +217,19 @@ __global__ __launch_bounds__(TPW * kSplit * 64) void group_kernel(GroupArgs a)
 }
 
 // ------------------------------------------------------------- wide tiles
-// One 64-row tile per workgroup of kWideWaves wavefronts, for groups whose
-// tiles are fewer than the GPU's compute units' worth of work.  A chunk runs
-// in three phases separated by barriers:
+// One 64-row tile (RW = 64), or half of one (RW = 32), per workgroup of
+// kWideWaves wavefronts, for groups with few tiles: the GPU has more compute
+// units than such a group has tiles, so a tile's work is spread over all
+// sixteen wavefronts of a CU, and with RW = 32 over two CUs.  A chunk runs in
+// three phases separated by barriers:
 //   A  every thread quantizes its share of the chunk's activation into the
-//      LDS table (build_x);
+//      LDS table (build_slot);
 //   B  wavefront w computes ab, the sub-block chain of all eight lane groups,
-//      of its two blocks 2w and 2w+1 for its 64 rows and puts them in LDS;
-//   C  wavefronts 0..7 (lane group L = w, row = lane) extend the block chain
-//      acc = fma(d0, ab, acc) over the chunk's blocks in order.
+//      of blocks 2w and 2w+1 for the workgroup's rows (RW = 64: one row per
+//      lane, both blocks in turn; RW = 32: lanes 0-31 take block 2w and
+//      lanes 32-63 block 2w+1 of the same 32 rows) and puts them in LDS;
+//   C  8 * RW / 64 wavefronts, one lane per (lane group, row), extend the
+//      block chain acc = fma(d0, ab, acc) over the chunk's blocks in order.
 // ab values are exact functions of one block, so computing them in parallel
 // changes nothing; the only sequential step, C, runs in block order as the
 // dot-product order prescribes.  The next chunk's activation, payload and
@@ -326,12 +330,13 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     }
 }
 
-// ab of the eight lane groups of chunk block B (payload v) for the calling lane's row.
+// ab of the eight lane groups of chunk block B (payload v, activation scales
+// d1) for the calling lane's row.  hoff is a per-lane byte offset into the
+// table (a further block for the upper half-wave when RW = 32, else 0).
 template <int FMT, int B>
-__device__ __forceinline__ void block_ab(const float *__restrict__ T, const float *__restrict__ D1, u32x4 v,
+__device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, uint32_t hoff,
                                          float ab[8])
 {
-    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1 + 4 * B);
     if (FMT == BQ_Q1_0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -339,7 +344,7 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, const floa
             const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
 #pragma unroll
             for (int L = 0; L < 8; ++L) {
-                const float t = tab(T, B * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1));
+                const float t = tab(T, B * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1) + hoff);
                 ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
             }
         }
@@ -353,7 +358,7 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, const floa
             for (int beta = 0; beta < 4; ++beta) {
                 const int L = 4 * (m & 1) + beta;
                 const int slot = B * kSlotsPerBlock + m * 8 + 2 * beta;
-                const float sv = tab(T, slot, nib4(wa, beta)) + tab(T, slot + 1, nib4(wb, beta));
+                const float sv = tab(T, slot, nib4(wa, beta) + hoff) + tab(T, slot + 1, nib4(wb, beta) + hoff);
                 ab[L] = j == 0 ? d1[0] * sv : __builtin_fmaf(d1[1], sv, ab[L]);
             }
         }
@@ -361,30 +366,44 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, const floa
 }
 
 // Phase B for the wavefront whose blocks are W2 and W2 + 1.
-template <int FMT, int W2>
+template <int FMT, int W2, int RW>
 __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float *__restrict__ D1,
-                                        float (*AB)[8][64], const u32x4 (&v)[2], int nbc, int lane)
+                                        float (*AB)[8][RW], const u32x4 (&v)[2], int nbc, int lane)
 {
     float ab[8];
-    if (W2 < nbc) {
-        block_ab<FMT, W2>(T, D1, v[0], ab);
+    if (RW == 64) {
+        if (W2 < nbc) {
+            block_ab<FMT, W2>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2), v[0], 0u, ab);
 #pragma unroll
-        for (int L = 0; L < 8; ++L)
-            AB[W2][L][lane] = ab[L];
-    }
-    if (W2 + 1 < nbc) {
-        block_ab<FMT, W2 + 1>(T, D1, v[1], ab);
+            for (int L = 0; L < 8; ++L)
+                AB[W2][L][lane] = ab[L];
+        }
+        if (W2 + 1 < nbc) {
+            block_ab<FMT, W2 + 1>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2 + 4), v[1], 0u, ab);
 #pragma unroll
-        for (int L = 0; L < 8; ++L)
-            AB[W2 + 1][L][lane] = ab[L];
+            for (int L = 0; L < 8; ++L)
+                AB[W2 + 1][L][lane] = ab[L];
+        }
+    } else {
+        const int h = lane / RW, r = lane % RW;
+        if (W2 + h < nbc) {
+            const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
+            block_ab<FMT, W2>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (W2 + h)), v[0], hoff, ab);
+#pragma unroll
+            for (int L = 0; L < 8; ++L)
+                AB[W2 + h][L][r] = ab[L];
+        }
     }
 }
 
-template <int FMT, int QA>
+template <int FMT, int QA, int RW, int TPW>
 __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
 {
+    static_assert(RW == 64 || TPW == 1, "several tiles per workgroup only with whole tiles");
+    constexpr int kParts = kTileRows / RW;  // workgroups per tile (RW = 32: two)
+    constexpr int kChainWaves = 8 * RW / 64;
     __shared__ float T[kTableFloats];
-    __shared__ float AB[kChunkBlocks][8][64];
+    __shared__ float AB[kChunkBlocks][8][RW];
     __shared__ float D1[kScaleFloats];
     const int wg = blockIdx.x;
     GemvDesc g = a.p[0];
@@ -395,35 +414,49 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             g = a.p[i];
             wg0 = a.wg_end[i - 1];
         }
-    const int tile = wg - wg0;
+    const int tiles = (g.rows + kTileRows - 1) / kTileRows;
+    const int tile0 = (wg - wg0) / kParts * TPW, part = (wg - wg0) % kParts;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)tile * g.nb * kTileRows);
-    const rsrc_t sp = rsrc_of(g.scales + (int64_t)tile * g.ng * kTileRows);
-    const uint32_t lo = (uint32_t)lane * 16;
+    const int h = lane / RW, r = lane % RW;  // half-wave and row of this lane (h = 0 when RW = 64)
+    const uint32_t lo = (uint32_t)(part * RW + r) * 16;
     const int nb = g.nb, ng = g.ng;
+    // a tile past the product's last one re-reads the last tile and stores nothing
+    auto wtile = [&](int t) { return rsrc_of(g.bits + (int64_t)min(tile0 + t, tiles - 1) * g.nb * kTileRows); };
+    auto stile = [&](int t) { return rsrc_of(g.scales + (int64_t)min(tile0 + t, tiles - 1) * g.ng * kTileRows); };
 
     // Requests in the order of use (vector memory counts complete in order);
     // all unconditional, clamped to the row's last block / scale group.
     XSlot<FMT> xs;
     u32x4 v[2], sc[kChunkBlocks / kGroup];
-    auto request = [&](int cb) {
+    auto request = [&](int t, int cb) {
+        const rsrc_t wp = wtile(t);
+        if (RW == 64) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            v[i] = bload(wp, lo, (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
+            for (int i = 0; i < 2; ++i)
+                v[i] = bload(wp, lo, (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
+        } else {
+            v[0] = bload(wp, lo + (uint32_t)min(cb + 2 * wave + h, nb - 1) * kStep, 0);
+        }
     };
-    auto request_scales = [&](int cb) {
+    auto request_scales = [&](int t, int cb) {
+        const rsrc_t sp = stile(t);
 #pragma unroll
         for (int j = 0; j < kChunkBlocks / kGroup; ++j)
             sc[j] = bload(sp, lo, (uint32_t)min(cb / kGroup + j, ng - 1) * kStep);
     };
     load_slot<FMT>(xs, a.x, 0, min(kChunkBlocks, nb));
     __builtin_amdgcn_sched_barrier(0);
-    request(0);
+    request(0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    request_scales(0);
+    request_scales(0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    float acc = 0.0f;  // wavefronts 0..7: lane group `wave` of row `lane`
+    // chain wavefronts: one lane per (lane group L, row r), one accumulator per tile
+    const int L = (wave * 64 + lane) / RW;
+    float acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        acc[t] = 0.0f;
     for (int cb = 0; cb < nb; cb += kChunkBlocks) {
         const int nbc = min(kChunkBlocks, nb - cb);
         const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;  // the last chunk re-reads itself
@@ -431,79 +464,89 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         build_slot<FMT, QA>(T, D1, xs, nbc);
         __syncthreads();
         load_slot<FMT>(xs, a.x, nx, min(kChunkBlocks, nb - nx));
-        // B (wavefront-uniform dispatch, so that every table offset is a constant)
-        switch (wave) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            // the unit after (tile t, this chunk): the next tile, or the first tile of the next chunk
+            const int tn = t + 1 < TPW ? t + 1 : 0, cn = t + 1 < TPW ? cb : nx;
+            // B (wavefront-uniform dispatch, so that every table offset is a constant)
+            switch (wave) {
 #define BQ_PHASE_B(w) \
-    case w: phase_b<FMT, 2 * (w)>(T, D1, AB, v, nbc, lane); break;
-            BQ_PHASE_B(0) BQ_PHASE_B(1) BQ_PHASE_B(2) BQ_PHASE_B(3) BQ_PHASE_B(4) BQ_PHASE_B(5)
-            BQ_PHASE_B(6) BQ_PHASE_B(7) BQ_PHASE_B(8) BQ_PHASE_B(9) BQ_PHASE_B(10) BQ_PHASE_B(11)
-            BQ_PHASE_B(12) BQ_PHASE_B(13) BQ_PHASE_B(14) BQ_PHASE_B(15)
+    case w: phase_b<FMT, 2 * (w), RW>(T, D1, AB, v, nbc, lane); break;
+                BQ_PHASE_B(0) BQ_PHASE_B(1) BQ_PHASE_B(2) BQ_PHASE_B(3) BQ_PHASE_B(4) BQ_PHASE_B(5)
+                BQ_PHASE_B(6) BQ_PHASE_B(7) BQ_PHASE_B(8) BQ_PHASE_B(9) BQ_PHASE_B(10) BQ_PHASE_B(11)
+                BQ_PHASE_B(12) BQ_PHASE_B(13) BQ_PHASE_B(14) BQ_PHASE_B(15)
 #undef BQ_PHASE_B
-        default: break;
-        }
-        request(nx);
-        __syncthreads();
-        // C
-        if (wave < 8) {
-            // all reads first, then the chain; blocks past a short last chunk
-            // leave acc unchanged (a select, so the reads need no branches)
-            float abv[kChunkBlocks];
-#pragma unroll
-            for (int b = 0; b < kChunkBlocks; ++b)
-                abv[b] = AB[b][wave][lane];
-#pragma unroll
-            for (int b = 0; b < kChunkBlocks; ++b) {
-                const float next = __builtin_fmaf(scale_of(sc[b / kGroup], b), abv[b], acc);
-                acc = b < nbc ? next : acc;
+            default: break;
             }
+            request(tn, cn);
+            __syncthreads();
+            // C
+            if (wave < kChainWaves) {
+                // all reads first, then the chain; blocks past a short last chunk
+                // leave acc unchanged (a select, so the reads need no branches)
+                float abv[kChunkBlocks];
+#pragma unroll
+                for (int b = 0; b < kChunkBlocks; ++b)
+                    abv[b] = AB[b][L][r];
+#pragma unroll
+                for (int b = 0; b < kChunkBlocks; ++b) {
+                    const float next = __builtin_fmaf(scale_of(sc[b / kGroup], b), abv[b], acc[t]);
+                    acc[t] = b < nbc ? next : acc[t];
+                }
+            }
+            request_scales(tn, cn);
+            if (t + 1 < TPW)
+                __syncthreads();  // this phase C reads AB before the next tile's phase B writes it
+            // after the last tile: the next chunk's phase A writes only T and D1,
+            // and its barrier orders this phase C before the next phase B
         }
-        request_scales(nx);
-        // the next chunk's phase A writes only T and D1, which phase C does not read;
-        // its barrier orders this phase C before the next phase B writes AB
     }
-    __syncthreads();
-    if (wave < 8)
-        AB[0][wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        const int row = tile * kTileRows + lane;
-        const float y = ((AB[0][0][lane] + AB[0][4][lane]) + (AB[0][2][lane] + AB[0][6][lane])) +
-                        ((AB[0][1][lane] + AB[0][5][lane]) + (AB[0][3][lane] + AB[0][7][lane]));
-        if (row < g.rows)
-            g.y[row] = y;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        __syncthreads();
+        if (wave < kChainWaves)
+            AB[0][L][r] = acc[t];
+        __syncthreads();
+        if (wave == 0 && lane < RW && tile0 + t < tiles) {
+            const int row = (tile0 + t) * kTileRows + part * RW + lane;
+            const float y = ((AB[0][0][lane] + AB[0][4][lane]) + (AB[0][2][lane] + AB[0][6][lane])) +
+                            ((AB[0][1][lane] + AB[0][5][lane]) + (AB[0][3][lane] + AB[0][7][lane]));
+            if (row < g.rows)
+                g.y[row] = y;
+        }
     }
 }
 
-template <int FMT>
+template <int FMT, int RW, int TPW>
 static void wide_qa(int qa, const GroupArgs &a, hipStream_t st)
 {
     const dim3 grid(a.wg_end[a.nprod - 1]), block(kWideThreads);
     switch (qa) {
-    case 32: hipLaunchKernelGGL((wide_kernel<FMT, 32>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((wide_kernel<FMT, 64>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((wide_kernel<FMT, 128>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((wide_kernel<FMT, 32, RW, TPW>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((wide_kernel<FMT, 64, RW, TPW>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((wide_kernel<FMT, 128, RW, TPW>), grid, block, 0, st, a); break;
     }
 }
 
-template <int FMT, int TPW>
+template <int FMT>
 static void group_qa(int qa, const GroupArgs &a, hipStream_t st)
 {
-    const dim3 grid(a.wg_end[a.nprod - 1]), block(TPW * kSplit * 64);
+    const dim3 grid(a.wg_end[a.nprod - 1]), block(2 * kSplit * 64);
     switch (qa) {
-    case 32: hipLaunchKernelGGL((group_kernel<FMT, 32, TPW>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((group_kernel<FMT, 64, TPW>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((group_kernel<FMT, 128, TPW>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((group_kernel<FMT, 32, 2>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((group_kernel<FMT, 64, 2>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((group_kernel<FMT, 128, 2>), grid, block, 0, st, a); break;
     }
 }
 
-hipError_t launch_group(int fmt, int qa, int tpw, const GroupArgs &a, hipStream_t st)
+hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, hipStream_t st)
 {
-    if (tpw == 0)
-        fmt == BQ_Q1_0 ? wide_qa<BQ_Q1_0>(qa, a, st) : wide_qa<BQ_Q2_0>(qa, a, st);
-    else if (fmt == BQ_Q1_0)
-        tpw == 2 ? group_qa<BQ_Q1_0, 2>(qa, a, st) : group_qa<BQ_Q1_0, 1>(qa, a, st);
-    else
-        tpw == 2 ? group_qa<BQ_Q2_0, 2>(qa, a, st) : group_qa<BQ_Q2_0, 1>(qa, a, st);
+    const bool q1 = fmt == BQ_Q1_0;
+    switch (shape) {
+    case kShapeHalf: q1 ? wide_qa<BQ_Q1_0, 32, 1>(qa, a, st) : wide_qa<BQ_Q2_0, 32, 1>(qa, a, st); break;
+    case kShapeWide2: q1 ? wide_qa<BQ_Q1_0, 64, 2>(qa, a, st) : wide_qa<BQ_Q2_0, 64, 2>(qa, a, st); break;
+    default: q1 ? group_qa<BQ_Q1_0>(qa, a, st) : group_qa<BQ_Q2_0>(qa, a, st); break;
+    }
     return hipGetLastError();
 }
 

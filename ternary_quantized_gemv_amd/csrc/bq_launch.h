@@ -35,9 +35,13 @@ hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_
 hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
                        hipStream_t st);
 // launch_group: a group of products sharing one f32 activation, quantized
-// inside the kernel; tpw = 0: one tile per sixteen-wavefront workgroup, else
-// tpw tiles (1 or 2) per workgroup of four wavefronts per tile (bq_group.hip).
-hipError_t launch_group(int fmt, int qa, int tpw, const GroupArgs &a, hipStream_t st);
+// inside the kernel (bq_group.hip), in one of three workgroup shapes:
+enum GroupShape {
+    kShapeHalf = 0,   // half a tile (32 rows) per sixteen-wavefront workgroup
+    kShapeWide2 = 1,  // two tiles per sixteen-wavefront workgroup, one after the other
+    kShapePair = 2,   // two tiles per workgroup, four wavefronts per tile
+};
+hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, hipStream_t st);
 // launch_quantize: n values in blocks of qa, f32 or f16-valued scales (bq_quantize.hip).
 hipError_t launch_quantize(const float *x, int64_t n, int qa, bool f16_scale, int8_t *q, float *d, hipStream_t st);
 

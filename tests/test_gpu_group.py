@@ -2,8 +2,10 @@
 activation that the kernel quantizes itself.  Every output must equal the
 oracle's quantize_q8 followed by its matvec, bit for bit: ragged rows, one to
 four products, one to several table chunks and a short last chunk, every qa,
-activations with zero blocks, exact ties and subnormal scales, and the
-two-tiles-per-workgroup layout used by groups of more than 512 tiles."""
+activations with zero blocks, exact ties and subnormal scales, and each
+workgroup shape: half a tile (groups of at most 128 tiles), two tiles in
+turn per sixteen-wavefront workgroup, two tiles per eight-wavefront workgroup
+(groups of more than 512 tiles with one table chunk), with odd tile counts."""
 import numpy as np
 import pytest
 
@@ -48,8 +50,12 @@ CASES = [
     (2, [300, 64], 64, 128, "normal"),        # two table chunks
     (2, [129], 37, 64, "layer"),              # 32 + 5 blocks
     (2, [12288, 12288], 64, 128, "normal"),   # 384 tiles
-    (1, [20000, 16000, 700, 5], 2, 128, "normal"),  # 575 tiles: two per workgroup, odd counts
-    (2, [40000, 3], 4, 64, "special"),              # 626 tiles: two per workgroup
+    (1, [8000, 300], 40, 64, "special"),      # 130 tiles: one per workgroup, 32 + 8 blocks
+    (2, [9000], 37, 32, "normal"),            # 141 tiles, 32 + 5 blocks
+    (1, [20000, 16000, 700, 5], 2, 128, "normal"),  # 575 tiles, one chunk: two tiles per 8-wavefront workgroup
+    (2, [40000, 3], 4, 64, "special"),              # 626 tiles, one chunk
+    (1, [40000, 100], 40, 128, "normal"),           # 627 tiles, two chunks: two tiles per wide workgroup
+    (2, [7000, 1100, 300], 70, 32, "special"),      # 133 tiles, three chunks, odd tile counts
 ]
 
 
