@@ -15,6 +15,34 @@
 
 namespace bq {
 
+// The quantizer's rule (quant_of) for the values of one activation block
+// with scale db, through a reciprocal.  p = x * rcp(db) is within 2^-15 of
+// x / db (|x| <= 127.0001 db, v_rcp_f32 is accurate to 1 ulp), and the
+// correctly rounded x / db within 2^-18 of it, so both round to the same
+// integer unless p lies within 2^-14 of a half-integer.  Those values, and
+// scales too small for a safe reciprocal (or zero), take the correctly
+// rounded division.  Zero comes out as +0, as quant_of's integer does.
+template <int V>
+__device__ __forceinline__ void quant_block(const float (&x)[V], float db, float (&q)[V])
+{
+    const float rdb = __builtin_amdgcn_rcpf(db);
+    bool slow = !(db >= 0x1p-120f);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const float p = x[i] * rdb;
+        const float a = fabsf(p);
+        const float fl = floorf(a);
+        const float dist = a - fl - 0.5f;  // exact wherever it decides
+        slow |= fabsf(dist) <= 0x1p-14f;
+        q[i] = __builtin_copysignf(dist >= 0.0f ? fl + 1.0f : fl, p) + 0.0f;
+    }
+    if (slow) {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            q[i] = (float)quant_of(x[i], db);
+    }
+}
+
 // The f32 activation values of one table chunk held by one thread: NT
 // threads take 8 consecutive values each per step.
 template <int FMT, int NT>
@@ -287,9 +315,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
         return;
     const float db = m / 127.0f;
     float f[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-        f[i] = (float)quant_of(xs.v[i], db);
+    quant_block<V>(xs.v, db, f);
     f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
     if constexpr (FMT == BQ_Q1_0) {
         // entry 4h + e: +-q0 +-q1 by bits 0, 1 of e, +-q2 +-q3 by bits 0, 1 of h
@@ -299,13 +325,14 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
             lo[e] = ((e & 1) ? f[0] : -f[0]) + ((e & 2) ? f[1] : -f[1]);
             hi[e] = ((e & 1) ? f[2] : -f[2]) + ((e & 2) ? f[3] : -f[3]);
         }
-        const bool first = ((t >> 3) & 3) == 0;
+        // times d1 on a block's first sub-block, times 1 (exact) elsewhere
+        const float s1 = ((t >> 3) & 3) == 0 ? db : 1.0f;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = first ? db * (lo[e] + hi[h]) : lo[e] + hi[h];
+                v[e] = s1 * (lo[e] + hi[h]);
             dst[h] = v;
         }
         if ((t & 7) == 0)

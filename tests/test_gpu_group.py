@@ -2,7 +2,9 @@
 activation that the kernel quantizes itself.  Every output must equal the
 oracle's quantize_q8 followed by its matvec, bit for bit: ragged rows, one to
 four products, one to several table chunks and a short last chunk, every qa,
-activations with zero blocks, exact ties and subnormal scales, and each
+activations with zero blocks, exact ties, values within a few ulps of a
+rounding boundary (where the kernels' reciprocal shortcut must hand over to
+the exact division) and subnormal scales, and each
 workgroup shape: half a tile (groups of at most 128 tiles), two tiles in
 turn per sixteen-wavefront workgroup, two tiles per eight-wavefront workgroup
 (groups of more than 512 tiles with one table chunk), with odd tile counts."""
@@ -19,9 +21,29 @@ pytestmark = pytest.mark.gpu
 THREADS = 16
 
 
+def near_ties(cols, qa, seed):
+    """Blocks whose values sit within a few ulps of (k + 1/2) * d, with d not a
+    power of two: x / d lands next to, or on, a rounding boundary."""
+    g = np.random.default_rng(seed)
+    x = np.empty(cols, np.float32)
+    for b in range(cols // qa):
+        dt = np.float32(g.uniform(0.01, 3.0))
+        k = g.integers(-127, 127, qa)
+        v = ((k + 0.5) * np.float64(dt)).astype(np.float32)
+        for _ in range(3):  # up to three ulps either way
+            step = g.integers(-1, 2, qa)
+            v = np.where(step > 0, np.nextafter(v, np.float32(np.inf)),
+                         np.where(step < 0, np.nextafter(v, np.float32(-np.inf)), v)).astype(np.float32)
+        v[0] = np.float32(127) * dt * (1 if k[0] >= 0 else -1)  # the block maximum: d = fl(amax / 127)
+        x[b * qa:(b + 1) * qa] = v
+    return x
+
+
 def group_input(fmt, cols, qa, regime, seed):
     if regime == "layer":
         return synth.layer_shaped(fmt, 1, cols, seed, qa)[1].astype(np.float32)
+    if regime == "nearties":
+        return near_ties(cols, qa, seed)
     x = synth.activation(cols, seed, qa)
     if regime == "special":
         nblk = cols // qa
@@ -42,6 +64,9 @@ def group_input(fmt, cols, qa, regime, seed):
 # fmt, rows of each product, blocks per row, qa, regime
 CASES = [
     (1, [1], 1, 128, "normal"),
+    (1, [300, 64], 33, 32, "nearties"),
+    (2, [129, 1000], 40, 128, "nearties"),
+    (1, [9000], 32, 64, "nearties"),          # two tiles per wide workgroup
     (1, [1, 63, 65, 130], 3, 32, "special"),
     (1, [300, 64], 96, 128, "normal"),        # three table chunks
     (1, [200], 40, 64, "special"),            # a short last chunk (32 + 8 blocks)
