@@ -30,12 +30,11 @@ constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
 // bq_group_matvec (measured on MI355X): groups of at most kHalfMaxTiles
 // tiles give each half tile a workgroup of sixteen wavefronts (wide_kernel),
-// so that they spread over more compute units; larger groups give each
-// sixteen-wavefront workgroup two tiles in turn (one table build serves
-// both), except single-chunk rows of groups beyond kWideMaxTiles, which run
-// two tiles per workgroup of eight wavefronts (group_kernel): there the GPU
-// is full anyway and the shorter phases of the wide shape do not pay for
-// its barriers.
+// so that they spread over more compute units; groups of at most
+// kWideMaxTiles give each sixteen-wavefront workgroup two tiles in turn (one
+// table build serves both); larger groups fill the GPU with one row per lane
+// and eight tiles per workgroup (rows_kernel), where the wide shapes' extra
+// LDS traffic and barriers no longer buy parallelism.
 constexpr int kHalfMaxTiles = 128;
 constexpr int kWideMaxTiles = 512;
 
@@ -219,17 +218,14 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
     }
     if (w[0].cols % qa)
         return set_error(BQ_EARG, "%s: cols %lld not a multiple of qa %d", fn, (long long)w[0].cols, (int)qa);
-    const bool one_chunk = w[0].cols / block_len(fmt) <= kChunkBlocks;
-    const GroupShape shape = tiles <= kHalfMaxTiles                 ? kShapeHalf
-                             : tiles <= kWideMaxTiles || !one_chunk ? kShapeWide2
-                                                                    : kShapePair;
+    const GroupShape shape = tiles <= kHalfMaxTiles ? kShapeHalf : tiles <= kWideMaxTiles ? kShapeWide2 : kShapeRows;
     int64_t wgs = 0;
     for (int i = 0; i < count; ++i) {
         bq_act none;
         memset(&none, 0, sizeof none);
         args.p[i] = make_desc(&w[i], &none, y[i]);
         const int64_t t = tiles_of(w[i].rows);
-        wgs += shape == kShapeHalf ? 2 * t : (t + 1) / 2;  // kShapeWide2, kShapePair: two tiles each
+        wgs += shape == kShapeHalf ? 2 * t : shape == kShapeRows ? (t + 7) / 8 : (t + 1) / 2;
         if (wgs >= (int64_t(1) << 31))
             return set_error(BQ_EARG, "%s: too many rows", fn);
         args.wg_end[i] = (int32_t)wgs;

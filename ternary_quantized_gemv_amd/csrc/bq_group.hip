@@ -3,12 +3,13 @@
 // section "Limitations": Q/K/V, and gate/up, submitted together with one wait
 // per group) run from an f32 vector that each workgroup quantizes itself
 // while it fills its LDS table, so a group needs no separate quantizer launch
-// and the int8 vector never goes to memory.
+// and the int8 vector never goes to memory.  Bits are those of
+// bq_quantize_act_q8 followed by bq_q1_0_matvec / bq_q2_0_matvec.
 //
-// The block arithmetic is split_kernel's (bq_split.h): four wavefronts per
-// 64-row tile, one tile (or two, for groups with many tiles) per workgroup,
-// so the few hundred tiles of a decode group spread over the whole GPU.  Bits are those
-// of bq_quantize_act_q8 followed by bq_q1_0_matvec / bq_q2_0_matvec.
+// Two kernels: wide_kernel spreads the tiles of a small group over whole
+// compute units (sixteen wavefronts on half a tile, or on two tiles in
+// turn), rows_kernel walks large groups one row per lane as the token sweep
+// does.
 #include "bq_device.h"
 #include "bq_launch.h"
 #include "bq_split.h"
@@ -43,206 +44,7 @@ __device__ __forceinline__ void quant_block(const float (&x)[V], float db, float
     }
 }
 
-// The f32 activation values of one table chunk held by one thread: NT
-// threads take 8 consecutive values each per step.
-template <int FMT, int NT>
-struct XChunk {
-    static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
-    static constexpr int kSteps = (kChunkBlocks * BL + NT * 8 - 1) / (NT * 8);
-    f32x4 v[2 * kSteps];
-};
-
-// Load the values of chunk blocks cb .. cb + nbc - 1.  Every load is issued
-// (past the chunk's end a thread re-reads the chunk's last 8 values and
-// drops them), so the loads count the same on every path.
-template <int FMT, int NT>
-__device__ __forceinline__ void load_x(XChunk<FMT, NT> &xc, const float *__restrict__ x, int cb, int nbc)
-{
-    constexpr int BL = XChunk<FMT, NT>::BL;
-    const int nvals = nbc * BL;
-    const float *xp = x + (int64_t)cb * BL;
-#pragma unroll
-    for (int s = 0; s < XChunk<FMT, NT>::kSteps; ++s) {
-        const int v0 = min(s * NT * 8 + (int)threadIdx.x * 8, nvals - 8);
-        xc.v[2 * s] = *reinterpret_cast<const f32x4 *>(xp + v0);
-        xc.v[2 * s + 1] = *reinterpret_cast<const f32x4 *>(xp + v0 + 4);
-    }
-}
-
-// Fill the table (and D1) of a chunk of nbc blocks from the values in xc.
-// The QA / 8 threads of one activation block combine their |x| maxima with
-// butterfly shuffles (max is exact in any order), take d = amax / 127 and the
-// quants by the quantizer's rule (quant_of), and write the 16-entry tables of
-// the nibble slots their 8 values cover.  Quants lie in [-127, 127], so the
-// Q1_0 negation needs no -128 case.
-template <int FMT, int QA, int NT>
-__device__ __forceinline__ void build_x(float *T, float *D1, const XChunk<FMT, NT> &xc, int nbc)
-{
-    constexpr int kLanes = QA / 8;
-    const int nvals = nbc * XChunk<FMT, NT>::BL;
-#pragma unroll
-    for (int s = 0; s < XChunk<FMT, NT>::kSteps; ++s) {
-        const int v0 = s * NT * 8 + (int)threadIdx.x * 8;
-        const bool ok = v0 < nvals;  // whole activation blocks are in or out
-        const f32x4 a = xc.v[2 * s], b = xc.v[2 * s + 1];
-        float m = fmaxf(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))),
-                        fmaxf(fmaxf(fabsf(b[0]), fabsf(b[1])), fmaxf(fabsf(b[2]), fabsf(b[3]))));
-#pragma unroll
-        for (int off = 1; off < kLanes; off <<= 1)
-            m = fmaxf(m, __shfl_xor(m, off, 64));
-        if (!ok)
-            continue;
-        const float db = m / 127.0f;
-        int qv[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qv[e] = quant_of(a[e], db);
-            qv[e + 4] = quant_of(b[e], db);
-        }
-        if (FMT == BQ_Q1_0) {
-            // slot t: values 4t .. 4t+3; entry 4h + e = sum of +-q_i by bit i
-            // of the nibble, times d1 on a block's first sub-block
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int t = v0 / 4 + u;
-                const int *qs = qv + 4 * u;
-                const bool first = ((t >> 3) & 3) == 0;
-                f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const int hi = ((h & 1) ? qs[2] : -qs[2]) + ((h & 2) ? qs[3] : -qs[3]);
-                    f32x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int lo = ((e & 1) ? qs[0] : -qs[0]) + ((e & 2) ? qs[1] : -qs[1]);
-                        const float sf = (float)(lo + hi);
-                        v[e] = first ? db * sf : sf;
-                    }
-                    dst[h] = v;
-                }
-            }
-            if ((v0 & 31) == 0)
-                D1[v0 / 32] = db;
-        } else {
-            // slot t: values 2t, 2t+1; entry 4h + e = (e-1) q_2t + (h-1) q_2t+1
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int t = v0 / 2 + u;
-                const int q0 = qv[2 * u], q1 = qv[2 * u + 1];
-                f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    f32x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = (float)((e - 1) * q0 + (h - 1) * q1);
-                    dst[h] = v;
-                }
-            }
-            if ((v0 & 31) == 0) {
-                // d1 of sub-block j of block b at D1[4b + j], j = 0, 1; 2 and 3 unused
-                const int sb = v0 / 32;
-                D1[4 * (sb >> 1) + (sb & 1)] = db;
-                if ((sb & 1) == 0)
-                    D1[4 * (sb >> 1) + 2] = D1[4 * (sb >> 1) + 3] = 0.0f;
-            }
-        }
-    }
-}
-
-// One workgroup: TPW tiles of one product, four wavefronts per tile
-// (wavefront k: lane groups k and k + 4, as split_kernel).  Each wavefront
-// keeps kDepth blocks of its tile's payload (16 bytes per lane each) in
-// flight in a register ring: the first ones are requested with the
-// activation, before the table is built, and each block walked requests the
-// block kDepth ahead (across chunk ends), while the next chunk's activation
-// is requested as soon as the current table is built.
-constexpr int kDepth = 16;      // payload blocks in flight per wavefront
-constexpr int kScaleSlots = 4;  // scale groups held (the current one, two ahead, one spare)
-static_assert(kChunkBlocks % kDepth == 0 && kDepth % kGroup == 0, "ring slots must be static");
-
-template <int FMT, int QA, int TPW>
-__global__ __launch_bounds__(TPW * kSplit * 64) void group_kernel(GroupArgs a)
-{
-    constexpr int NT = TPW * kSplit * 64;
-    __shared__ float T[kTableFloats];
-    __shared__ float D1[kScaleFloats];
-    __shared__ float P[TPW][kSplit][64];
-    // the product of this workgroup (wave-uniform selects, no indexed copy)
-    const int wg = blockIdx.x;
-    GemvDesc g = a.p[0];
-    int wg0 = 0;
-#pragma unroll
-    for (int i = 1; i < kGroupMax; ++i)
-        if (i < a.nprod && wg >= a.wg_end[i - 1]) {
-            g = a.p[i];
-            wg0 = a.wg_end[i - 1];
-        }
-    const int tiles = (g.rows + kTileRows - 1) / kTileRows;
-    const int tile0 = (wg - wg0) * TPW;
-    const int ntiles = min(TPW, tiles - tile0);
-
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int tl = wave / kSplit, k = wave % kSplit;
-    const int tile = tile0 + tl;
-    const bool live = tl < ntiles;
-    // a wavefront past the last tile reads the first tile and stores nothing
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)(live ? tile : tile0) * g.nb * kTileRows);
-    const rsrc_t sp = rsrc_of(g.scales + (int64_t)(live ? tile : tile0) * g.ng * kTileRows);
-    const uint32_t lo = (uint32_t)lane * 16;
-    const uint32_t sh = FMT == BQ_Q1_0 ? 8u * (k >> 1) + 4u * (k & 1) : 8u * k;
-    const int nb = g.nb, ng = g.ng;
-
-    // Requests go out in the order of use (vector memory counts complete in
-    // order): the chunk's activation, then per block its payload, preceded
-    // by the scale group it opens.  Every request is unconditional (past the
-    // row's end a wavefront re-reads its last block or chunk and drops it),
-    // so the counts are the same on every path.
-    XChunk<FMT, NT> xc;
-    u32x4 p[kDepth], sc[kScaleSlots];
-    // (scheduling barriers keep the compiler from reordering these requests)
-    load_x<FMT, NT>(xc, a.x, 0, min(kChunkBlocks, nb));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < kDepth; ++b) {
-        if (b % kGroup == 0)
-            sc[(b / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
-        p[b] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    float acc0 = 0.0f, acc1 = 0.0f;
-    for (int cb = 0; cb < nb; cb += kChunkBlocks) {
-        const int nbc = min(kChunkBlocks, nb - cb);
-        if (cb > 0)
-            __syncthreads();  // every wavefront is done with the previous table
-        build_x<FMT, QA, NT>(T, D1, xc, nbc);
-        __syncthreads();
-        // the next chunk's activation (the last chunk re-reads itself)
-        const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;
-        load_x<FMT, NT>(xc, a.x, nx, min(kChunkBlocks, nb - nx));
-#pragma unroll
-        for (int i = 0; i < kChunkBlocks; ++i) {
-            if (i < nbc)
-                split_block<FMT>(T, D1, i, p[i % kDepth], scale_of(sc[(i / kGroup) % kScaleSlots], i), k, sh, acc0,
-                                 acc1);
-            // block i + kDepth of the row takes the register block i leaves
-            const int b = cb + i + kDepth;
-            if ((i + kDepth) % kGroup == 0)
-                sc[((i + kDepth) / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
-            p[i % kDepth] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
-        }
-    }
-
-    P[tl][k][lane] = acc0 + acc1;  // p_k = a_k + a_(k+4)
-    __syncthreads();
-    if (k == 0 && live) {
-        const int row = tile * kTileRows + lane;
-        const float y = (P[tl][0][lane] + P[tl][2][lane]) + (P[tl][1][lane] + P[tl][3][lane]);
-        if (row < g.rows)
-            g.y[row] = y;
-    }
-}
+constexpr int kScaleSlots = 4;  // scale groups held in a ring (the current one, the next, spares)
 
 // ------------------------------------------------------------- wide tiles
 // One 64-row tile (RW = 64), or half of one (RW = 32), per workgroup of
@@ -276,11 +78,11 @@ struct XSlot {
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restrict__ x, int cb, int nbc)
+__device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restrict__ x, int cb, int nbc, int t)
 {
     constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64, V = XSlot<FMT>::V;
     // past the chunk's end a thread re-reads the chunk's last slot (and drops it)
-    const int v0 = min((int)threadIdx.x * V, nbc * BL - V);
+    const int v0 = min(t * V, nbc * BL - V);
     const float *xp = x + (int64_t)cb * BL + v0;
     if constexpr (FMT == BQ_Q1_0) {
         const f32x4 t = *reinterpret_cast<const f32x4 *>(xp);
@@ -300,10 +102,9 @@ __device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restric
 // converted quants; on a Q1_0 block's first sub-block they are multiplied by
 // d1 (one rounding, as the order prescribes).
 template <int FMT, int QA>
-__device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT> &xs, int nbc)
+__device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT> &xs, int nbc, int t)
 {
     constexpr int V = XSlot<FMT>::V, kLanes = QA / V;
-    const int t = threadIdx.x;
     float m = fabsf(xs.v[0]);
 #pragma unroll
     for (int i = 1; i < V; ++i)
@@ -358,10 +159,11 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
 }
 
 // ab of the eight lane groups of chunk block B (payload v, activation scales
-// d1) for the calling lane's row.  hoff is a per-lane byte offset into the
+// d1) for the calling lane's row.  B is a constant at every call (a template
+// argument or an unrolled loop index), so each table offset is an immediate.  hoff is a per-lane byte offset into the
 // table (a further block for the upper half-wave when RW = 32, else 0).
-template <int FMT, int B>
-__device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, uint32_t hoff,
+template <int FMT>
+__device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, int B, uint32_t hoff,
                                          float ab[8])
 {
     if (FMT == BQ_Q1_0) {
@@ -400,13 +202,13 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
     float ab[8];
     if (RW == 64) {
         if (W2 < nbc) {
-            block_ab<FMT, W2>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2), v[0], 0u, ab);
+            block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2), v[0], W2, 0u, ab);
 #pragma unroll
             for (int L = 0; L < 8; ++L)
                 AB[W2][L][lane] = ab[L];
         }
         if (W2 + 1 < nbc) {
-            block_ab<FMT, W2 + 1>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2 + 4), v[1], 0u, ab);
+            block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2 + 4), v[1], W2 + 1, 0u, ab);
 #pragma unroll
             for (int L = 0; L < 8; ++L)
                 AB[W2 + 1][L][lane] = ab[L];
@@ -415,7 +217,7 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
         const int h = lane / RW, r = lane % RW;
         if (W2 + h < nbc) {
             const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
-            block_ab<FMT, W2>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (W2 + h)), v[0], hoff, ab);
+            block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (W2 + h)), v[0], W2, hoff, ab);
 #pragma unroll
             for (int L = 0; L < 8; ++L)
                 AB[W2 + h][L][r] = ab[L];
@@ -471,7 +273,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         for (int j = 0; j < kChunkBlocks / kGroup; ++j)
             sc[j] = bload(sp, lo, (uint32_t)min(cb / kGroup + j, ng - 1) * kStep);
     };
-    load_slot<FMT>(xs, a.x, 0, min(kChunkBlocks, nb));
+    const int slot = threadIdx.x;
+    load_slot<FMT>(xs, a.x, 0, min(kChunkBlocks, nb), slot);
     __builtin_amdgcn_sched_barrier(0);
     request(0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -488,9 +291,9 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         const int nbc = min(kChunkBlocks, nb - cb);
         const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;  // the last chunk re-reads itself
         // A
-        build_slot<FMT, QA>(T, D1, xs, nbc);
+        build_slot<FMT, QA>(T, D1, xs, nbc, slot);
         __syncthreads();
-        load_slot<FMT>(xs, a.x, nx, min(kChunkBlocks, nb - nx));
+        load_slot<FMT>(xs, a.x, nx, min(kChunkBlocks, nb - nx), slot);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             // the unit after (tile t, this chunk): the next tile, or the first tile of the next chunk
@@ -544,6 +347,118 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     }
 }
 
+// -------------------------------------------------------------- row tiles
+// Large groups (the LM head): one row per lane and one tile per wavefront,
+// eight tiles per workgroup, walked as the token sweep walks them -- every
+// lane carries the eight lane accumulators of its row through all blocks in
+// order.  The workgroup builds each chunk's table from x (two slots per
+// thread) once for its eight tiles; payload requests run kRowsDepth blocks
+// ahead across chunk ends.
+constexpr int kRowsWaves = 8;
+constexpr int kRowsThreads = kRowsWaves * 64;
+constexpr int kRowsDepth = 4;
+static_assert(kChunkBlocks * kSlotsPerBlock == 2 * kRowsThreads, "two table slots per thread");
+
+template <int FMT, int QA>
+__global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
+{
+    __shared__ float T[kTableFloats];
+    __shared__ float D1[kScaleFloats];
+    const int wg = blockIdx.x;
+    GemvDesc g = a.p[0];
+    int wg0 = 0;
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < a.nprod && wg >= a.wg_end[i - 1]) {
+            g = a.p[i];
+            wg0 = a.wg_end[i - 1];
+        }
+    const int tiles = (g.rows + kTileRows - 1) / kTileRows;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int tile = (wg - wg0) * kRowsWaves + wave;
+    // a wavefront past the product's last tile re-reads it and stores nothing
+    const int tl = min(tile, tiles - 1);
+    const rsrc_t wp = rsrc_of(g.bits + (int64_t)tl * g.nb * kTileRows);
+    const rsrc_t sp = rsrc_of(g.scales + (int64_t)tl * g.ng * kTileRows);
+    const uint32_t lo = (uint32_t)lane * 16;
+    const int nb = g.nb, ng = g.ng;
+    const int s0 = threadIdx.x, s1 = threadIdx.x + kRowsThreads;
+
+    // Requests in the order of use, all unconditional and clamped to the row.
+    XSlot<FMT> x0, x1;
+    u32x4 p[kRowsDepth], sc[kScaleSlots];
+    load_slot<FMT>(x0, a.x, 0, min(kChunkBlocks, nb), s0);
+    load_slot<FMT>(x1, a.x, 0, min(kChunkBlocks, nb), s1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < kRowsDepth; ++b) {
+        if (b % kGroup == 0)
+            sc[(b / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
+        p[b] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    float acc[8];
+#pragma unroll
+    for (int L = 0; L < 8; ++L)
+        acc[L] = 0.0f;
+    // block i of the chunk at cb: the chain step, then the request kRowsDepth ahead
+    auto step = [&](int cb, int i) {
+        float ab[8];
+        block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * i), p[i % kRowsDepth], i, 0u, ab);
+        float d0 = scale_of(sc[(i / kGroup) % kScaleSlots], i);
+        asm volatile("" : "+v"(d0));  // widen once, then full-rate fmas
+#pragma unroll
+        for (int L = 0; L < 8; ++L)
+            acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
+    };
+    auto ahead = [&](int cb, int i) {
+        const int b = cb + i + kRowsDepth;
+        if ((i + kRowsDepth) % kGroup == 0)
+            sc[((i + kRowsDepth) / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
+        p[i % kRowsDepth] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
+    };
+    for (int cb = 0; cb < nb; cb += kChunkBlocks) {
+        const int nbc = min(kChunkBlocks, nb - cb);
+        const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;  // the last chunk re-reads itself
+        if (cb > 0)
+            __syncthreads();  // every wavefront is done with the previous table
+        build_slot<FMT, QA>(T, D1, x0, nbc, s0);
+        build_slot<FMT, QA>(T, D1, x1, nbc, s1);
+        __syncthreads();
+        load_slot<FMT>(x0, a.x, nx, min(kChunkBlocks, nb - nx), s0);
+        load_slot<FMT>(x1, a.x, nx, min(kChunkBlocks, nb - nx), s1);
+        if (nbc == kChunkBlocks) {
+#pragma unroll
+            for (int i = 0; i < kChunkBlocks; ++i) {
+                step(cb, i);
+                ahead(cb, i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kChunkBlocks; ++i) {
+                if (i < nbc)
+                    step(cb, i);
+                ahead(cb, i);
+            }
+        }
+    }
+    const int row = tile * kTileRows + lane;
+    if (tile < tiles && row < g.rows)
+        g.y[row] = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
+}
+
+template <int FMT>
+static void rows_qa(int qa, const GroupArgs &a, hipStream_t st)
+{
+    const dim3 grid(a.wg_end[a.nprod - 1]), block(kRowsThreads);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((rows_kernel<FMT, 32>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((rows_kernel<FMT, 64>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((rows_kernel<FMT, 128>), grid, block, 0, st, a); break;
+    }
+}
+
 template <int FMT, int RW, int TPW>
 static void wide_qa(int qa, const GroupArgs &a, hipStream_t st)
 {
@@ -555,24 +470,13 @@ static void wide_qa(int qa, const GroupArgs &a, hipStream_t st)
     }
 }
 
-template <int FMT>
-static void group_qa(int qa, const GroupArgs &a, hipStream_t st)
-{
-    const dim3 grid(a.wg_end[a.nprod - 1]), block(2 * kSplit * 64);
-    switch (qa) {
-    case 32: hipLaunchKernelGGL((group_kernel<FMT, 32, 2>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((group_kernel<FMT, 64, 2>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((group_kernel<FMT, 128, 2>), grid, block, 0, st, a); break;
-    }
-}
-
 hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, hipStream_t st)
 {
     const bool q1 = fmt == BQ_Q1_0;
     switch (shape) {
     case kShapeHalf: q1 ? wide_qa<BQ_Q1_0, 32, 1>(qa, a, st) : wide_qa<BQ_Q2_0, 32, 1>(qa, a, st); break;
     case kShapeWide2: q1 ? wide_qa<BQ_Q1_0, 64, 2>(qa, a, st) : wide_qa<BQ_Q2_0, 64, 2>(qa, a, st); break;
-    default: q1 ? group_qa<BQ_Q1_0>(qa, a, st) : group_qa<BQ_Q2_0>(qa, a, st); break;
+    default: q1 ? rows_qa<BQ_Q1_0>(qa, a, st) : rows_qa<BQ_Q2_0>(qa, a, st); break;
     }
     return hipGetLastError();
 }

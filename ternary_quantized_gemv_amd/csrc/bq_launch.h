@@ -39,7 +39,7 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 enum GroupShape {
     kShapeHalf = 0,   // half a tile (32 rows) per sixteen-wavefront workgroup
     kShapeWide2 = 1,  // two tiles per sixteen-wavefront workgroup, one after the other
-    kShapePair = 2,   // two tiles per workgroup, four wavefronts per tile
+    kShapeRows = 2,   // eight tiles per workgroup, one per wavefront, one row per lane
 };
 hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, hipStream_t st);
 // launch_quantize: n values in blocks of qa, f32 or f16-valued scales (bq_quantize.hip).

@@ -6,8 +6,8 @@ activations with zero blocks, exact ties, values within a few ulps of a
 rounding boundary (where the kernels' reciprocal shortcut must hand over to
 the exact division) and subnormal scales, and each
 workgroup shape: half a tile (groups of at most 128 tiles), two tiles in
-turn per sixteen-wavefront workgroup, two tiles per eight-wavefront workgroup
-(groups of more than 512 tiles with one table chunk), with odd tile counts."""
+turn per sixteen-wavefront workgroup (up to 512), and one row per lane with
+eight tiles per workgroup (more), with odd tile counts."""
 import numpy as np
 import pytest
 
@@ -77,9 +77,10 @@ CASES = [
     (2, [12288, 12288], 64, 128, "normal"),   # 384 tiles
     (1, [8000, 300], 40, 64, "special"),      # 130 tiles: one per workgroup, 32 + 8 blocks
     (2, [9000], 37, 32, "normal"),            # 141 tiles, 32 + 5 blocks
-    (1, [20000, 16000, 700, 5], 2, 128, "normal"),  # 575 tiles, one chunk: two tiles per 8-wavefront workgroup
-    (2, [40000, 3], 4, 64, "special"),              # 626 tiles, one chunk
-    (1, [40000, 100], 40, 128, "normal"),           # 627 tiles, two chunks: two tiles per wide workgroup
+    (1, [20000, 16000, 700, 5], 2, 128, "normal"),  # 575 tiles: one row per lane, partial workgroups
+    (2, [40000, 3], 4, 64, "special"),              # 626 tiles
+    (1, [40000, 100], 40, 128, "normal"),           # 627 tiles, 32 + 8 blocks
+    (2, [33000], 70, 64, "nearties"),               # 516 tiles, three chunks
     (2, [7000, 1100, 300], 70, 32, "special"),      # 133 tiles, three chunks, odd tile counts
 ]
 
