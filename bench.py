@@ -8,6 +8,8 @@ Weights are packed and copied to the GPU once, before timing; inputs are
 seeded synthetic data with the workload's shapes and distributions.
 
 Prints ONE JSON line.  python bench.py [--steps K] [--warmup W] [--fmt q1_0|q2_0]
+The line also reports, as context, the same token run as a dependency-ordered
+decode (field decode_chain; --no-chain skips it).
 [--act q8_128|q8_0]: q8_0 quantizes with qa 32 and f16-valued scales (the
 pages' activation flavour) instead of qa 128 with f32 scales.
 
@@ -217,17 +219,11 @@ def bench_batch(args):
                       "results": rows_out}), flush=True)
 
 
-def bench_chain(args):
+def chain_timing(fmt, canon, shapes, x0, fused: bool, K: int, W: int):
+    """The dependency-ordered decode token (staging.StagedChain): ms per token
+    launched eagerly and replayed from a captured graph, and the outputs."""
     import torch
-    import synth
-    import ternary_quantized_gemv_amd as bq
     from ternary_quantized_gemv_amd.staging import StagedChain
-
-    fmt = bq.BQ_Q1_0 if args.fmt == "q1_0" else bq.BQ_Q2_0
-    shapes = synth.decode_sweep_shapes()
-    canon = [synth.blocks(fmt, r, c, args.seed, i) for i, (_, r, c) in enumerate(shapes)]
-    x0 = synth.activation(shapes[0][2], args.seed, 999)
-    K, W = max(20, args.steps // 4), max(5, args.warmup // 10)
 
     def per_token(fn):
         for _ in range(W):
@@ -241,8 +237,8 @@ def bench_chain(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    def measure(fused):
-        ch = StagedChain(fmt, canon, shapes, x0, fused=fused)
+    ch = StagedChain(fmt, canon, shapes, x0, fused=fused)
+    try:
         eager_ms = per_token(ch.run)
         ref = ch.y.cpu().numpy()
         side = torch.cuda.Stream()
@@ -261,11 +257,22 @@ def bench_chain(args):
                "graph_GB_s": round(ch.token_bytes() / (graph_ms * 1e-3) / 1e9, 1),
                "graph_replay_equals_eager": same}
         del graph
+    finally:
         ch.close()
-        return out, ref
+    return out, ref
 
-    fused, y_fused = measure(True)
-    split, y_split = measure(False)
+
+def bench_chain(args):
+    import synth
+    import ternary_quantized_gemv_amd as bq
+
+    fmt = bq.BQ_Q1_0 if args.fmt == "q1_0" else bq.BQ_Q2_0
+    shapes = synth.decode_sweep_shapes()
+    canon = [synth.blocks(fmt, r, c, args.seed, i) for i, (_, r, c) in enumerate(shapes)]
+    x0 = synth.activation(shapes[0][2], args.seed, 999)
+    K, W = max(20, args.steps // 4), max(5, args.warmup // 10)
+    fused, y_fused = chain_timing(fmt, canon, shapes, x0, True, K, W)
+    split, y_split = chain_timing(fmt, canon, shapes, x0, False, K, W)
     name = "Q1_0" if fmt == bq.BQ_Q1_0 else "Q2_0"
     print(json.dumps({"metric": f"ms per token for the {name} decode token as 145 dependent groups",
                       "value": fused["graph_ms_per_token"], "unit": "ms", "higher_is_better": False,
@@ -291,6 +298,7 @@ def main():
                     help="sweep activations: qa 128 with f32 scales, or qa 32 with f16-valued scales")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-chain", action="store_true", help="skip the decode-chain context field")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -366,6 +374,18 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(sw, y_gpu, args.cpu_budget, cpu_threads())
 
+    # context, not the headline: the same products as a dependency-ordered
+    # decode (145 groups, each the quantized output of the one before)
+    chain = None
+    if not args.no_chain and not q8_0:
+        try:
+            out, _ = chain_timing(fmt, canon, shapes, x[0], True, 40, 10)
+            chain = {"ms_per_token": out["graph_ms_per_token"], "eager_ms_per_token": out["eager_ms_per_token"],
+                     "launches_per_token": out["launches_per_token"],
+                     "how": "bench.py --workload chain: one fused quantize+product launch per group, graph replay"}
+        except Exception as e:  # the headline line must print regardless
+            chain = {"error": f"{type(e).__name__}: {e}"}
+
     fmt_name = "Q1_0" if fmt == bq.BQ_Q1_0 else "Q2_0"
     out = {
         "metric": f"achieved HBM GB/s (% of peak) and ms/token for 253-matmul {fmt_name} sweep",
@@ -408,6 +428,7 @@ def main():
             "algorithmic_bytes_per_launch": sw.sweep_bytes(),
         },
         "cpu_baseline": cpu,
+        "decode_chain": chain,
     }
     sw.close()
     print(json.dumps(out), flush=True)
