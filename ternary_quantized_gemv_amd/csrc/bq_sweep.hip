@@ -332,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(GemvDesc g, int64_t ld_
 }
 
 template <int FMT, int QA>
-__global__ __launch_bounds__(kThreads) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int tiles)
+__global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d,
+                                                                          int tiles)
 {
     __shared__ float T[kTableFloats];
     __shared__ float D1[kScaleFloats];
@@ -344,8 +345,13 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(GemvDesc g, int64_t ld
     run_item<FMT, QA>(g, tile0, min(kWaves, tiles - tile0), T, D1);
 }
 
+// With activation blocks shorter than 128 values the chunk's activation
+// scales come from LDS, and the compiler would keep more of them in flight
+// than four wavefronts per SIMD (two workgroups per CU) leave room for; the
+// second bound holds those instantiations to 128 registers.  The qa-128
+// code is unaffected.
 template <int FMT, int QA>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(const GemvDesc *__restrict__ descs,
+__global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void sweep_kernel(const GemvDesc *__restrict__ descs,
                                                          const WorkItem *__restrict__ items)
 {
     __shared__ float T[kTableFloats];
