@@ -115,18 +115,32 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
 
 def timed_calls(fn, reps: int) -> float:
     """Mean microseconds per call of fn(i) over reps back-to-back calls on the
-    current stream (HIP events around the batch)."""
+    current stream: the calls are captured once in a graph and the replay is
+    timed with HIP events, so the figure is the GPU's time per call (kernel
+    plus the launch gap between kernels), not the host's launch rate."""
     import torch
 
     for i in range(3):
         fn(i)
     torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(reps):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(reps):
-        fn(i)
+    graph.replay()
     e1.record()
     torch.cuda.synchronize()
+    del graph
     return e0.elapsed_time(e1) * 1e3 / reps
 
 

@@ -17,26 +17,21 @@
 
 namespace bq {
 
-// Kernel choice for bq_q1_0_matvec / bq_q2_0_matvec (measured on MI355X):
-// * single-column products of at most kSplitMaxTiles 64-row tiles run four
-//   wavefronts per tile (launch_split), larger ones one row per lane;
-// * several columns run those kernels once per column (one grid row each),
-//   except at least kColsMinCols columns on a matrix of more than
-//   kSplitMaxTiles tiles, which run four columns per workgroup from
-//   interleaved tables (launch_cols): there the per-column kernels re-stream
-//   the weights once per column, while on smaller matrices their extra
-//   parallelism wins.
+// Kernel choice (measured on MI355X).  bq_group_matvec, and single-column
+// bq_q1_0_matvec / bq_q2_0_matvec: group_shape() picks the finest workgroup
+// shape whose workgroups fit one round of the 256 compute units -- half a
+// tile, one tile or two tiles per sixteen-wavefront workgroup (wide_kernel,
+// a tile's blocks spread over the whole CU) up to 512 tiles, beyond that one
+// row per lane with eight tiles per workgroup (rows_kernel for groups;
+// matvec_kernel, the sweep's walk, for single products).  Several columns:
+// four wavefronts per tile, one grid row per column (launch_split), up to
+// kSplitMaxTiles tiles, above that four columns per workgroup from
+// interleaved tables (launch_cols) for at least kColsMinCols columns, else
+// one row per lane per column: there the per-column kernels re-stream the
+// weights once per column, while on smaller matrices their extra parallelism
+// wins.
 constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
-// bq_group_matvec (measured on MI355X): groups of at most kHalfMaxTiles
-// tiles give each half tile a workgroup of sixteen wavefronts (wide_kernel),
-// so that they spread over more compute units; groups of at most
-// kWideMaxTiles give each sixteen-wavefront workgroup two tiles in turn (one
-// table build serves both); larger groups fill the GPU with one row per lane
-// and eight tiles per workgroup (rows_kernel), where the wide shapes' extra
-// LDS traffic and barriers no longer buy parallelism.
-constexpr int kHalfMaxTiles = 128;
-constexpr int kWideMaxTiles = 512;
 
 // ------------------------------------------------------------ validation
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -122,7 +117,17 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
     const int tiles = (int)tiles_of(w->rows);
     hipStream_t st = static_cast<hipStream_t>(s);
     hipError_t e;
-    if (a->ncols >= kColsMinCols && tiles > kSplitMaxTiles)
+    if (a->ncols == 1 && group_shape(tiles) != kShapeRows) {
+        GroupArgs args;
+        memset(&args, 0, sizeof args);
+        const GroupShape shape = group_shape(tiles);
+        args.p[0] = g;
+        args.wg_end[0] = (int32_t)group_workgroups(shape, tiles);
+        args.nprod = 1;
+        args.ld_q = a->ld_q;
+        args.ld_d = a->ld_d;
+        e = launch_wide_q8(FMT, a->qa, shape, args, a->ncols, st);
+    } else if (a->ncols >= kColsMinCols && tiles > kSplitMaxTiles)
         e = launch_cols(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
     else if (tiles <= kSplitMaxTiles)
         e = launch_split(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
@@ -218,14 +223,13 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
     }
     if (w[0].cols % qa)
         return set_error(BQ_EARG, "%s: cols %lld not a multiple of qa %d", fn, (long long)w[0].cols, (int)qa);
-    const GroupShape shape = tiles <= kHalfMaxTiles ? kShapeHalf : tiles <= kWideMaxTiles ? kShapeWide2 : kShapeRows;
+    const GroupShape shape = group_shape(tiles);
     int64_t wgs = 0;
     for (int i = 0; i < count; ++i) {
         bq_act none;
         memset(&none, 0, sizeof none);
         args.p[i] = make_desc(&w[i], &none, y[i]);
-        const int64_t t = tiles_of(w[i].rows);
-        wgs += shape == kShapeHalf ? 2 * t : shape == kShapeRows ? (t + 7) / 8 : (t + 1) / 2;
+        wgs += group_workgroups(shape, tiles_of(w[i].rows));
         if (wgs >= (int64_t(1) << 31))
             return set_error(BQ_EARG, "%s: too many rows", fn);
         args.wg_end[i] = (int32_t)wgs;

@@ -12,7 +12,6 @@
 // does.
 #include "bq_device.h"
 #include "bq_launch.h"
-#include "bq_split.h"
 
 namespace bq {
 
@@ -158,6 +157,74 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     }
 }
 
+// Phase A from an activation that is already quantized (the single-product
+// entry points on small matrices): thread t reads its slot's quants (Q1_0:
+// 4, Q2_0: 2) and the scale of their activation block, and writes the same
+// table build_table_q1 / build_table_q2 would (Q1_0 negation keeps -128).
+struct QSlot {
+    uint32_t w;
+    float d;
+};
+
+template <int FMT, int QA>
+__device__ __forceinline__ void load_qslot(QSlot &qs, const int8_t *__restrict__ q, const float *__restrict__ d,
+                                           int cb, int nbc, int t)
+{
+    constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64, V = FMT == BQ_Q1_0 ? 4 : 2;
+    // past the chunk's end a thread re-reads the chunk's last slot (and drops it)
+    const int64_t e = (int64_t)cb * BL + min(t * V, nbc * BL - V);
+    if constexpr (FMT == BQ_Q1_0)
+        qs.w = *reinterpret_cast<const uint32_t *>(q + e);
+    else
+        qs.w = *reinterpret_cast<const uint16_t *>(q + e);
+    qs.d = d[e / QA];
+}
+
+template <int FMT>
+__device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs, int nbc, int t)
+{
+    if (t >= nbc * kSlotsPerBlock)
+        return;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+    if constexpr (FMT == BQ_Q1_0) {
+        int p1[4], p0[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int v = (int8_t)(qs.w >> (8 * i));
+            p1[i] = v;
+            p0[i] = v == -128 ? -128 : -v;
+        }
+        const float s1 = ((t >> 3) & 3) == 0 ? qs.d : 1.0f;  // d1 on a block's first sub-block
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = s1 * (float)(((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]) + hi);
+            dst[h] = v;
+        }
+        if ((t & 7) == 0)
+            D1[t / 8] = qs.d;
+    } else {
+        const int q0 = (int8_t)(qs.w & 0xFF), q1 = (int8_t)(qs.w >> 8);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = (float)((e - 1) * q0 + (h - 1) * q1);
+            dst[h] = v;
+        }
+        if ((t & 15) == 0) {
+            const int sb = t / 16;
+            D1[4 * (sb >> 1) + (sb & 1)] = qs.d;
+            if ((sb & 1) == 0)
+                D1[4 * (sb >> 1) + 2] = D1[4 * (sb >> 1) + 3] = 0.0f;
+        }
+    }
+}
+
 // ab of the eight lane groups of chunk block B (payload v, activation scales
 // d1) for the calling lane's row.  B is a constant at every call (a template
 // argument or an unrolled loop index), so each table offset is an immediate.  hoff is a per-lane byte offset into the
@@ -225,7 +292,7 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
     }
 }
 
-template <int FMT, int QA, int RW, int TPW>
+template <int FMT, int QA, int RW, int TPW, bool Q8>
 __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
 {
     static_assert(RW == 64 || TPW == 1, "several tiles per workgroup only with whole tiles");
@@ -243,6 +310,12 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             g = a.p[i];
             wg0 = a.wg_end[i - 1];
         }
+    if (Q8) {  // grid row c: activation column c
+        const int c = blockIdx.y;
+        g.q += c * a.ld_q;
+        g.d += c * a.ld_d;
+        g.y += (int64_t)c * g.rows;
+    }
     const int tiles = (g.rows + kTileRows - 1) / kTileRows;
     const int tile0 = (wg - wg0) / kParts * TPW, part = (wg - wg0) % kParts;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -256,7 +329,20 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     // Requests in the order of use (vector memory counts complete in order);
     // all unconditional, clamped to the row's last block / scale group.
     XSlot<FMT> xs;
-    u32x4 v[2], sc[kChunkBlocks / kGroup];
+    QSlot qs;
+    auto load_a = [&](int cb, int nbc, int t) {
+        if constexpr (Q8)
+            load_qslot<FMT, QA>(qs, g.q, g.d, cb, nbc, t);
+        else
+            load_slot<FMT>(xs, a.x, cb, nbc, t);
+    };
+    auto build_a = [&](int nbc, int t) {
+        if constexpr (Q8)
+            build_qslot<FMT>(T, D1, qs, nbc, t);
+        else
+            build_slot<FMT, QA>(T, D1, xs, nbc, t);
+    };
+    u32x4 v[2], sc[kChunkBlocks / kScalesPerGroup];
     auto request = [&](int t, int cb) {
         const rsrc_t wp = wtile(t);
         if (RW == 64) {
@@ -270,11 +356,11 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     auto request_scales = [&](int t, int cb) {
         const rsrc_t sp = stile(t);
 #pragma unroll
-        for (int j = 0; j < kChunkBlocks / kGroup; ++j)
-            sc[j] = bload(sp, lo, (uint32_t)min(cb / kGroup + j, ng - 1) * kStep);
+        for (int j = 0; j < kChunkBlocks / kScalesPerGroup; ++j)
+            sc[j] = bload(sp, lo, (uint32_t)min(cb / kScalesPerGroup + j, ng - 1) * kStep);
     };
     const int slot = threadIdx.x;
-    load_slot<FMT>(xs, a.x, 0, min(kChunkBlocks, nb), slot);
+    load_a(0, min(kChunkBlocks, nb), slot);
     __builtin_amdgcn_sched_barrier(0);
     request(0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -291,9 +377,9 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         const int nbc = min(kChunkBlocks, nb - cb);
         const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;  // the last chunk re-reads itself
         // A
-        build_slot<FMT, QA>(T, D1, xs, nbc, slot);
+        build_a(nbc, slot);
         __syncthreads();
-        load_slot<FMT>(xs, a.x, nx, min(kChunkBlocks, nb - nx), slot);
+        load_a(nx, min(kChunkBlocks, nb - nx), slot);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             // the unit after (tile t, this chunk): the next tile, or the first tile of the next chunk
@@ -320,7 +406,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
                     abv[b] = AB[b][L][r];
 #pragma unroll
                 for (int b = 0; b < kChunkBlocks; ++b) {
-                    const float next = __builtin_fmaf(scale_of(sc[b / kGroup], b), abv[b], acc[t]);
+                    const float next = __builtin_fmaf(scale_of(sc[b / kScalesPerGroup], b), abv[b], acc[t]);
                     acc[t] = b < nbc ? next : acc[t];
                 }
             }
@@ -392,8 +478,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < kRowsDepth; ++b) {
-        if (b % kGroup == 0)
-            sc[(b / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
+        if (b % kScalesPerGroup == 0)
+            sc[(b / kScalesPerGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kScalesPerGroup, ng - 1) * kStep);
         p[b] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -406,7 +492,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
     auto step = [&](int cb, int i) {
         float ab[8];
         block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * i), p[i % kRowsDepth], i, 0u, ab);
-        float d0 = scale_of(sc[(i / kGroup) % kScaleSlots], i);
+        float d0 = scale_of(sc[(i / kScalesPerGroup) % kScaleSlots], i);
         asm volatile("" : "+v"(d0));  // widen once, then full-rate fmas
 #pragma unroll
         for (int L = 0; L < 8; ++L)
@@ -414,8 +500,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
     };
     auto ahead = [&](int cb, int i) {
         const int b = cb + i + kRowsDepth;
-        if ((i + kRowsDepth) % kGroup == 0)
-            sc[((i + kRowsDepth) / kGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kGroup, ng - 1) * kStep);
+        if ((i + kRowsDepth) % kScalesPerGroup == 0)
+            sc[((i + kRowsDepth) / kScalesPerGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kScalesPerGroup, ng - 1) * kStep);
         p[i % kRowsDepth] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
     };
     for (int cb = 0; cb < nb; cb += kChunkBlocks) {
@@ -459,14 +545,14 @@ static void rows_qa(int qa, const GroupArgs &a, hipStream_t st)
     }
 }
 
-template <int FMT, int RW, int TPW>
-static void wide_qa(int qa, const GroupArgs &a, hipStream_t st)
+template <int FMT, int RW, int TPW, bool Q8>
+static void wide_qa(int qa, const GroupArgs &a, int ncols, hipStream_t st)
 {
-    const dim3 grid(a.wg_end[a.nprod - 1]), block(kWideThreads);
+    const dim3 grid(a.wg_end[a.nprod - 1], ncols), block(kWideThreads);
     switch (qa) {
-    case 32: hipLaunchKernelGGL((wide_kernel<FMT, 32, RW, TPW>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((wide_kernel<FMT, 64, RW, TPW>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((wide_kernel<FMT, 128, RW, TPW>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((wide_kernel<FMT, 32, RW, TPW, Q8>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((wide_kernel<FMT, 64, RW, TPW, Q8>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((wide_kernel<FMT, 128, RW, TPW, Q8>), grid, block, 0, st, a); break;
     }
 }
 
@@ -474,10 +560,23 @@ hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, h
 {
     const bool q1 = fmt == BQ_Q1_0;
     switch (shape) {
-    case kShapeHalf: q1 ? wide_qa<BQ_Q1_0, 32, 1>(qa, a, st) : wide_qa<BQ_Q2_0, 32, 1>(qa, a, st); break;
-    case kShapeWide2: q1 ? wide_qa<BQ_Q1_0, 64, 2>(qa, a, st) : wide_qa<BQ_Q2_0, 64, 2>(qa, a, st); break;
+    case kShapeHalf: q1 ? wide_qa<BQ_Q1_0, 32, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 32, 1, false>(qa, a, 1, st); break;
+    case kShapeWide: q1 ? wide_qa<BQ_Q1_0, 64, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 64, 1, false>(qa, a, 1, st); break;
+    case kShapeWide2: q1 ? wide_qa<BQ_Q1_0, 64, 2, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 64, 2, false>(qa, a, 1, st); break;
     default: q1 ? rows_qa<BQ_Q1_0>(qa, a, st) : rows_qa<BQ_Q2_0>(qa, a, st); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_q8(int fmt, int qa, GroupShape shape, const GroupArgs &a, int ncols, hipStream_t st)
+{
+    const bool q1 = fmt == BQ_Q1_0;
+    if (shape == kShapeHalf)
+        q1 ? wide_qa<BQ_Q1_0, 32, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 32, 1, true>(qa, a, ncols, st);
+    else if (shape == kShapeWide)
+        q1 ? wide_qa<BQ_Q1_0, 64, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 64, 1, true>(qa, a, ncols, st);
+    else
+        q1 ? wide_qa<BQ_Q1_0, 64, 2, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 64, 2, true>(qa, a, ncols, st);
     return hipGetLastError();
 }
 

@@ -1,7 +1,6 @@
-// bq_split.h -- internal to libbq: the four-wavefronts-per-tile walk shared
-// by split_kernel (bq_sweep.hip) and the fused group kernel (bq_group.hip).
-// The caller passes the function that fills the LDS table of a chunk, so the
-// two kernels differ only in where the activation comes from.
+// bq_split.h -- internal to libbq: the four-wavefronts-per-tile walk of
+// split_kernel (bq_sweep.hip).  The caller passes the function that fills the
+// LDS table of a chunk.
 #pragma once
 
 #include "bq_device.h"

@@ -5,9 +5,10 @@ four products, one to several table chunks and a short last chunk, every qa,
 activations with zero blocks, exact ties, values within a few ulps of a
 rounding boundary (where the kernels' reciprocal shortcut must hand over to
 the exact division) and subnormal scales, and each
-workgroup shape: half a tile (groups of at most 128 tiles), two tiles in
-turn per sixteen-wavefront workgroup (up to 512), and one row per lane with
-eight tiles per workgroup (more), with odd tile counts."""
+workgroup shape: half a tile (groups of at most 128 tiles), one tile (up to
+256) or two tiles in turn (up to 512) per sixteen-wavefront workgroup, and
+one row per lane with eight tiles per workgroup (more), with odd tile
+counts."""
 import numpy as np
 import pytest
 
@@ -77,6 +78,7 @@ CASES = [
     (2, [12288, 12288], 64, 128, "normal"),   # 384 tiles
     (1, [8000, 300], 40, 64, "special"),      # 130 tiles: one per workgroup, 32 + 8 blocks
     (2, [9000], 37, 32, "normal"),            # 141 tiles, 32 + 5 blocks
+    (1, [20000], 3, 64, "special"),           # 313 tiles: two tiles per wide workgroup
     (1, [20000, 16000, 700, 5], 2, 128, "normal"),  # 575 tiles: one row per lane, partial workgroups
     (2, [40000, 3], 4, 64, "special"),              # 626 tiles
     (1, [40000, 100], 40, 128, "normal"),           # 627 tiles, 32 + 8 blocks
