@@ -46,17 +46,19 @@ __device__ __forceinline__ void quant_block(const float (&x)[V], float db, float
 constexpr int kScaleSlots = 4;  // scale groups held in a ring (the current one, the next, spares)
 
 // ------------------------------------------------------------- wide tiles
-// One 64-row tile (RW = 64), or half of one (RW = 32), per workgroup of
-// kWideWaves wavefronts, for groups with few tiles: the GPU has more compute
-// units than such a group has tiles, so a tile's work is spread over all
-// sixteen wavefronts of a CU, and with RW = 32 over two CUs.  A chunk runs in
+// One or two 64-row tiles (RW = 64), or a half or quarter of one (RW = 32,
+// 16), per workgroup of kWideWaves wavefronts, for groups with few tiles:
+// the GPU has more compute units than such a group has tiles, so a tile's
+// work is spread over all sixteen wavefronts of a CU, and with RW < 64 over
+// several CUs.  A chunk runs in
 // three phases separated by barriers:
 //   A  every thread quantizes its share of the chunk's activation into the
 //      LDS table (build_slot);
 //   B  wavefront w computes ab, the sub-block chain of all eight lane groups,
-//      of blocks 2w and 2w+1 for the workgroup's rows (RW = 64: one row per
-//      lane, both blocks in turn; RW = 32: lanes 0-31 take block 2w and
-//      lanes 32-63 block 2w+1 of the same 32 rows) and puts them in LDS;
+//      of its blocks for the workgroup's rows (RW = 64: blocks 2w and 2w+1,
+//      one row per lane, in turn; RW = 32: lanes 0-31 take block 2w and
+//      lanes 32-63 block 2w+1 of the same 32 rows; RW = 16: wavefronts 0-7
+//      take blocks 4w .. 4w+3, sixteen lanes each) and puts them in LDS;
 //   C  8 * RW / 64 wavefronts, one lane per (lane group, row), extend the
 //      block chain acc = fma(d0, ab, acc) over the chunk's blocks in order.
 // ab values are exact functions of one block, so computing them in parallel
@@ -65,7 +67,7 @@ constexpr int kScaleSlots = 4;  // scale groups held in a ring (the current one,
 // scales are requested as soon as the registers they replace are consumed.
 constexpr int kWideWaves = 16;
 constexpr int kWideThreads = kWideWaves * 64;
-static_assert(kChunkBlocks == 2 * kWideWaves, "two blocks per wavefront and chunk");
+static_assert(kChunkBlocks == 2 * kWideWaves, "two blocks per wavefront and chunk (four for RW = 16)");
 
 // Phase A of the wide kernel: thread t owns nibble slot t of the chunk
 // (Q1_0: values 4t .. 4t+3; Q2_0: values 2t, 2t+1), so all sixteen
@@ -261,33 +263,39 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, 
     }
 }
 
-// Phase B for the wavefront whose blocks are W2 and W2 + 1.
-template <int FMT, int W2, int RW>
+// Phase B for the wavefront whose first block is WB: with RW = 64 its lanes
+// (rows) take blocks WB and WB + 1 in turn; with RW = 32 or 16 the lanes
+// split into 64 / RW groups of RW rows, group h taking block WB + h.
+template <int FMT, int WB, int RW>
 __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float *__restrict__ D1,
                                         float (*AB)[8][RW], const u32x4 (&v)[2], int nbc, int lane)
 {
-    float ab[8];
-    if (RW == 64) {
-        if (W2 < nbc) {
-            block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2), v[0], W2, 0u, ab);
-#pragma unroll
-            for (int L = 0; L < 8; ++L)
-                AB[W2][L][lane] = ab[L];
-        }
-        if (W2 + 1 < nbc) {
-            block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * W2 + 4), v[1], W2 + 1, 0u, ab);
-#pragma unroll
-            for (int L = 0; L < 8; ++L)
-                AB[W2 + 1][L][lane] = ab[L];
-        }
+    if constexpr (WB >= kChunkBlocks) {
+        return;  // RW = 16: wavefronts 8-15 have no block
     } else {
-        const int h = lane / RW, r = lane % RW;
-        if (W2 + h < nbc) {
-            const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
-            block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (W2 + h)), v[0], W2, hoff, ab);
+        float ab[8];
+        if (RW == 64) {
+            if (WB < nbc) {
+                block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB), v[0], WB, 0u, ab);
 #pragma unroll
-            for (int L = 0; L < 8; ++L)
-                AB[W2 + h][L][r] = ab[L];
+                for (int L = 0; L < 8; ++L)
+                    AB[WB][L][lane] = ab[L];
+            }
+            if (WB + 1 < nbc) {
+                block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB + 4), v[1], WB + 1, 0u, ab);
+#pragma unroll
+                for (int L = 0; L < 8; ++L)
+                    AB[WB + 1][L][lane] = ab[L];
+            }
+        } else {
+            const int h = lane / RW, r = lane % RW;
+            if (WB + h < nbc) {
+                const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
+                block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB, hoff, ab);
+#pragma unroll
+                for (int L = 0; L < 8; ++L)
+                    AB[WB + h][L][r] = ab[L];
+            }
         }
     }
 }
@@ -296,8 +304,9 @@ template <int FMT, int QA, int RW, int TPW, bool Q8>
 __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
 {
     static_assert(RW == 64 || TPW == 1, "several tiles per workgroup only with whole tiles");
-    constexpr int kParts = kTileRows / RW;  // workgroups per tile (RW = 32: two)
+    constexpr int kParts = kTileRows / RW;           // workgroups per tile
     constexpr int kChainWaves = 8 * RW / 64;
+    constexpr int kBPW = RW == 64 ? 2 : 64 / RW;     // first block of wavefront w: kBPW * w
     __shared__ float T[kTableFloats];
     __shared__ float AB[kChunkBlocks][8][RW];
     __shared__ float D1[kScaleFloats];
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             for (int i = 0; i < 2; ++i)
                 v[i] = bload(wp, lo, (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
         } else {
-            v[0] = bload(wp, lo + (uint32_t)min(cb + 2 * wave + h, nb - 1) * kStep, 0);
+            v[0] = bload(wp, lo + (uint32_t)min(cb + kBPW * wave + h, nb - 1) * kStep, 0);
         }
     };
     auto request_scales = [&](int t, int cb) {
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             // B (wavefront-uniform dispatch, so that every table offset is a constant)
             switch (wave) {
 #define BQ_PHASE_B(w) \
-    case w: phase_b<FMT, 2 * (w), RW>(T, D1, AB, v, nbc, lane); break;
+    case w: phase_b<FMT, kBPW * (w), RW>(T, D1, AB, v, nbc, lane); break;
                 BQ_PHASE_B(0) BQ_PHASE_B(1) BQ_PHASE_B(2) BQ_PHASE_B(3) BQ_PHASE_B(4) BQ_PHASE_B(5)
                 BQ_PHASE_B(6) BQ_PHASE_B(7) BQ_PHASE_B(8) BQ_PHASE_B(9) BQ_PHASE_B(10) BQ_PHASE_B(11)
                 BQ_PHASE_B(12) BQ_PHASE_B(13) BQ_PHASE_B(14) BQ_PHASE_B(15)
@@ -560,6 +569,7 @@ hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, h
 {
     const bool q1 = fmt == BQ_Q1_0;
     switch (shape) {
+    case kShapeQuarter: q1 ? wide_qa<BQ_Q1_0, 16, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 16, 1, false>(qa, a, 1, st); break;
     case kShapeHalf: q1 ? wide_qa<BQ_Q1_0, 32, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 32, 1, false>(qa, a, 1, st); break;
     case kShapeWide: q1 ? wide_qa<BQ_Q1_0, 64, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 64, 1, false>(qa, a, 1, st); break;
     case kShapeWide2: q1 ? wide_qa<BQ_Q1_0, 64, 2, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 64, 2, false>(qa, a, 1, st); break;
@@ -571,7 +581,9 @@ hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, h
 hipError_t launch_wide_q8(int fmt, int qa, GroupShape shape, const GroupArgs &a, int ncols, hipStream_t st)
 {
     const bool q1 = fmt == BQ_Q1_0;
-    if (shape == kShapeHalf)
+    if (shape == kShapeQuarter)
+        q1 ? wide_qa<BQ_Q1_0, 16, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 16, 1, true>(qa, a, ncols, st);
+    else if (shape == kShapeHalf)
         q1 ? wide_qa<BQ_Q1_0, 32, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 32, 1, true>(qa, a, ncols, st);
     else if (shape == kShapeWide)
         q1 ? wide_qa<BQ_Q1_0, 64, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 64, 1, true>(qa, a, ncols, st);

@@ -38,24 +38,31 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // launch_group: a group of products sharing one f32 activation, quantized
 // inside the kernel (bq_group.hip), in one of three workgroup shapes:
 enum GroupShape {
-    kShapeHalf = 0,   // half a tile (32 rows) per sixteen-wavefront workgroup
-    kShapeWide = 1,   // one tile per sixteen-wavefront workgroup
-    kShapeWide2 = 2,  // two tiles per sixteen-wavefront workgroup, one after the other
-    kShapeRows = 3,   // eight tiles per workgroup, one per wavefront, one row per lane
+    kShapeQuarter = 0,  // a quarter tile (16 rows) per sixteen-wavefront workgroup
+    kShapeHalf = 1,     // half a tile (32 rows) per sixteen-wavefront workgroup
+    kShapeWide = 2,     // one tile per sixteen-wavefront workgroup
+    kShapeWide2 = 3,    // two tiles per sixteen-wavefront workgroup, one after the other
+    kShapeRows = 4,     // eight tiles per workgroup, one per wavefront, one row per lane
 };
 // The finest shape whose workgroups fit one round of the GPU's 256 compute
 // units (one sixteen-wavefront workgroup each), and its workgroup count.
 inline GroupShape group_shape(int64_t tiles)
 {
-    return tiles <= 128 ? kShapeHalf : tiles <= 256 ? kShapeWide : tiles <= 512 ? kShapeWide2 : kShapeRows;
+    return tiles <= 64 ? kShapeQuarter : tiles <= 128 ? kShapeHalf : tiles <= 256 ? kShapeWide
+           : tiles <= 512 ? kShapeWide2 : kShapeRows;
 }
 inline int64_t group_workgroups(GroupShape shape, int64_t tiles)
 {
-    return shape == kShapeHalf ? 2 * tiles : shape == kShapeWide ? tiles : shape == kShapeWide2 ? (tiles + 1) / 2
-                                                                                                 : (tiles + 7) / 8;
+    switch (shape) {
+    case kShapeQuarter: return 4 * tiles;
+    case kShapeHalf: return 2 * tiles;
+    case kShapeWide: return tiles;
+    case kShapeWide2: return (tiles + 1) / 2;
+    default: return (tiles + 7) / 8;
+    }
 }
 hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, hipStream_t st);
-// launch_wide_q8: the wide shapes (kShapeHalf, kShapeWide, kShapeWide2) for one product
+// launch_wide_q8: the wide shapes (kShapeQuarter .. kShapeWide2) for one product
 // whose activation is already quantized (p[0].q, p[0].d), ncols columns.
 hipError_t launch_wide_q8(int fmt, int qa, GroupShape shape, const GroupArgs &a, int ncols, hipStream_t st);
 // launch_quantize: n values in blocks of qa, f32 or f16-valued scales (bq_quantize.hip).

@@ -5,8 +5,9 @@ four products, one to several table chunks and a short last chunk, every qa,
 activations with zero blocks, exact ties, values within a few ulps of a
 rounding boundary (where the kernels' reciprocal shortcut must hand over to
 the exact division) and subnormal scales, and each
-workgroup shape: half a tile (groups of at most 128 tiles), one tile (up to
-256) or two tiles in turn (up to 512) per sixteen-wavefront workgroup, and
+workgroup shape: a quarter tile (groups of at most 64 tiles), half a tile
+(up to 128), one tile (up to 256) or two tiles in turn (up to 512) per
+sixteen-wavefront workgroup, and
 one row per lane with eight tiles per workgroup (more), with odd tile
 counts."""
 import numpy as np

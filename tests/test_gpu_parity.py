@@ -190,8 +190,8 @@ def test_small_batch_tall(fmt, rows, cols, ncols, qa, regime):
 FULL = [
     (Q1, 4096, 4096), (Q1, 12288, 4096), (Q1, 4096, 12288), (Q1, 151936, 4096),
     (Q2, 4096, 4096), (Q2, 1024, 4096), (Q2, 12288, 4096), (Q2, 4096, 12288),
-    # 313 and 700 tiles: two tiles per wide workgroup; the four-wavefront split
-    (Q1, 20000, 4096), (Q2, 20000, 2048), (Q1, 44800, 1024),
+    # 100, 313 and 700 tiles: half a tile and two tiles per wide workgroup; the four-wavefront split
+    (Q1, 6400, 2048), (Q2, 6390, 4096), (Q1, 20000, 4096), (Q2, 20000, 2048), (Q1, 44800, 1024),
 ]
 
 
