@@ -15,6 +15,35 @@
 
 namespace bq {
 
+// Maximum over aligned groups of N lanes (exact in any order).  Within a
+// 16-lane row the partners come through DPP (quad permutations, then the
+// half-row and row mirrors, each of which maps a group onto its neighbour),
+// across rows through ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float m)
+{
+    const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), CTRL, 0xF, 0xF, false);
+    return fmaxf(m, __builtin_bit_cast(float, o));
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float m)
+{
+    if constexpr (N >= 2)
+        m = dpp_max<0xB1>(m);  // quad_perm [1,0,3,2]
+    if constexpr (N >= 4)
+        m = dpp_max<0x4E>(m);  // quad_perm [2,3,0,1]
+    if constexpr (N >= 8)
+        m = dpp_max<0x141>(m);  // row_half_mirror
+    if constexpr (N >= 16)
+        m = dpp_max<0x140>(m);  // row_mirror
+    if constexpr (N >= 32)
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+    if constexpr (N >= 64)
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+    return m;
+}
+
 // The quantizer's rule (quant_of) for the values of one activation block
 // with scale db, through a reciprocal.  p = x * rcp(db) is within 2^-15 of
 // x / db (|x| <= 127.0001 db, v_rcp_f32 is accurate to 1 ulp), and the
@@ -97,8 +126,8 @@ __device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restric
     }
 }
 
-// The quantizer's per-block maximum (butterfly over the QA / V threads of an
-// activation block; max is exact in any order), its quants, and the slot's
+// The quantizer's per-block maximum (over the QA / V threads of an
+// activation block, group_max), its quants, and the slot's
 // 16-entry table.  Entries are sums of quants, exact in f32, formed from
 // converted quants; on a Q1_0 block's first sub-block they are multiplied by
 // d1 (one rounding, as the order prescribes).
@@ -110,9 +139,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
 #pragma unroll
     for (int i = 1; i < V; ++i)
         m = fmaxf(m, fabsf(xs.v[i]));
-#pragma unroll
-    for (int off = 1; off < kLanes; off <<= 1)
-        m = fmaxf(m, __shfl_xor(m, off, 64));
+    m = group_max<kLanes>(m);
     if (t >= nbc * kSlotsPerBlock)
         return;
     const float db = m / 127.0f;
