@@ -7,9 +7,10 @@
 // bq_quantize_act_q8 followed by bq_q1_0_matvec / bq_q2_0_matvec.
 //
 // Two kernels: wide_kernel spreads the tiles of a small group over whole
-// compute units (sixteen wavefronts on half a tile, or on two tiles in
-// turn), rows_kernel walks large groups one row per lane as the token sweep
-// does.
+// compute units (sixteen wavefronts on a quarter, a half, one or two tiles;
+// the single-product entry points use it too, reading their quantized
+// activation), rows_kernel walks large groups one row per lane as the token
+// sweep does.
 #include "bq_device.h"
 #include "bq_launch.h"
 
