@@ -22,6 +22,9 @@ namespace bq {
 
 constexpr int kColsNC = 4;     // activation columns per workgroup
 constexpr int kColsChunk = 4;  // blocks per table chunk
+// the walk steps through a chunk four blocks at a time with a four-block
+// payload ring, so a full chunk must be a multiple of four blocks
+static_assert(kColsChunk % 4 == 0, "chunk of whole ring turns");
 constexpr int kColsWaves = 4;  // wavefronts (tiles) per workgroup
 constexpr int kColsSlotBytes = 16 * kColsNC * 4;
 constexpr int kColsD1 = kColsChunk * 4 * kColsNC;  // activation scales per chunk [sub-block][column]
