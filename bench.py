@@ -8,6 +8,11 @@ Weights are packed and copied to the GPU once, before timing; inputs are
 seeded synthetic data with the workload's shapes and distributions.
 
 Prints ONE JSON line.  python bench.py [--steps K] [--warmup W] [--fmt q1_0|q2_0]
+Beside GB/s it gives us per matmul and ms per token, each with its HBM
+roofline time and fraction, the streaming-read floor measured live on the same
+GPU (k_floor, bq_read_floor over 1 GiB) and every fraction against it, the
+oracle on the host's cores with a bit-for-bit check of the GPU's outputs (and
+their largest relative error), and the pages' laptop CPU figures as context.
 The line also reports, as context, the same token run as a dependency-ordered
 decode (field decode_chain; --no-chain skips it).
 [--act q8_128|q8_0]: q8_0 quantizes with qa 32 and f16-valued scales (the
@@ -87,6 +92,7 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
     done_bytes = 0
     secs = 0.0
     mismatched = 0
+    max_rel = 0.0
     n = 0
     for i, (name, rows, cols) in enumerate(sw.shapes):
         k0, k1 = int(sw.koff[i]), int(sw.koff[i + 1])
@@ -97,6 +103,9 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
         done_bytes += sw.canon[i].size + cols + 4 * (cols // sw.qa) + 4 * rows
         yg = y_gpu[int(sw.yoff[i]):int(sw.yoff[i + 1])]
         mismatched += int(np.count_nonzero(yg.view(np.uint32) != y.view(np.uint32)))
+        ref = np.abs(y.astype(np.float64))
+        err = np.abs(yg.astype(np.float64) - y.astype(np.float64))
+        max_rel = max(max_rel, float(np.max(np.where(ref > 0, err / np.where(ref > 0, ref, 1.0), err), initial=0.0)))
         n += 1
         if secs >= budget_s:
             break
@@ -110,6 +119,7 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
         "ms_per_token_equiv": round(sw.sweep_bytes() / (done_bytes / secs) * 1e3, 1),
         "gpu_outputs_checked": int(sum(r for _, r, _ in sw.shapes[:n])),
         "gpu_outputs_mismatched": mismatched,
+        "gpu_max_rel_err": max_rel,
     }
 
 
@@ -144,6 +154,32 @@ def timed_calls(fn, reps: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+def read_floor(gib: float = 1.0, reps: int = 20) -> dict:
+    """The streaming-read floor of this GPU, measured live: bq_read_floor over
+    a buffer four times the last-level cache, median of reps event-timed
+    launches after a warm-up."""
+    import torch
+    import ternary_quantized_gemv_amd as bq
+
+    nbytes = int(gib * (1 << 30))
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(bq.BQ_FLOOR_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        bq.bq_read_floor(buf, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        bq.bq_read_floor(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    del buf, sink
+    torch.cuda.empty_cache()
+    gbs = nbytes / us / 1e3
+    return {"value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "how": f"bq_read_floor: one streaming read of {gib:g} GiB, median of {reps} launches"}
+
+
 def weight_copies(bq, fmt, rows, cols, seed, total=1.1e9, cap=512):
     """Device copies of one packed matrix, enough to total about 1.1 GB, so a
     timed batch that cycles through them streams from HBM (the 256 MB
@@ -176,6 +212,7 @@ def bench_gemv(args):
     shapes = [(bq.BQ_Q1_0, 4096, 4096), (bq.BQ_Q1_0, 12288, 4096), (bq.BQ_Q1_0, 4096, 12288),
               (bq.BQ_Q1_0, 151936, 4096), (bq.BQ_Q2_0, 4096, 4096), (bq.BQ_Q2_0, 1024, 4096),
               (bq.BQ_Q2_0, 12288, 4096), (bq.BQ_Q2_0, 4096, 12288)]
+    floor = read_floor()
     rows_out = []
     for fmt, rows, cols in shapes:
         ws, wbytes = weight_copies(bq, fmt, rows, cols, args.seed)
@@ -188,6 +225,7 @@ def bench_gemv(args):
         name = "Q1_0" if fmt == bq.BQ_Q1_0 else "Q2_0"
         rows_out.append({"fmt": name, "shape": f"{rows}x{cols}", "us_per_product": round(us, 2),
                          "algorithmic_bytes": nbytes, "GB_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "frac_of_floor": round(gbs / floor["value"], 4),
                          "ms_per_token_equiv": round(TOKEN_BYTES[name] / (gbs * 1e9) * 1e3, 3),
                          "weight_copies": len(ws)})
         log(f"gemv {name} {rows}x{cols}: {us:.2f} us, {gbs:.0f} GB/s")
@@ -198,7 +236,7 @@ def bench_gemv(args):
                       "dtype": "int8xQ->f32", "data": "synthetic (seeded)",
                       "config": {"workload": "single Q1_0 / Q2_0 products, one activation vector, qa 128; "
                                              "each timed batch cycles through ~1.1 GB of weight copies"},
-                      "results": rows_out}), flush=True)
+                      "k_floor": floor, "results": rows_out}), flush=True)
 
 
 def bench_batch(args):
@@ -384,6 +422,9 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device-to-device copies done")
 
+    floor = read_floor()
+    log(f"streaming-read floor {floor['value']:.0f} GB/s")
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(sw, y_gpu, args.cpu_budget, cpu_threads())
@@ -438,10 +479,28 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_of_floor": round(achieved / floor["value"], 4),
             "traffic": None if q8_0 else measured_traffic(fmt_name),
             "algorithmic_bytes_per_launch": sw.sweep_bytes(),
         },
+        "per_matmul": {
+            "us": round(ms_per_step * 1e3 / len(shapes), 4),
+            "roofline_us": round(step_bytes / len(shapes) / (HBM_PEAK_GBS * 1e3), 4),
+            "frac": round(value / HBM_PEAK_GBS, 4),
+        },
+        "per_token": {
+            "ms": round(ms_per_step, 5),
+            "roofline_ms": round(step_bytes / (HBM_PEAK_GBS * 1e6), 5),
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "frac_of_floor": round(value / floor["value"], 4),
+        },
+        "k_floor": floor,
         "cpu_baseline": cpu,
+        "pages_cpu_context": {
+            "memory_floor_GB_s": [14.9, 17.2],
+            "ternary_token_s_at_3_threads": [0.23, 0.25],
+            "machine": "the pages' laptop CPU (other hardware; context, not the target)",
+        },
         "decode_chain": chain,
     }
     sw.close()

@@ -190,6 +190,19 @@ int bq_token_sweep(const bq_sweep *plan, bq_stream s);
 /* Release a plan (NULL is allowed).  Synchronises the device first. */
 void bq_sweep_destroy(bq_sweep *plan);
 
+/* The streaming-read floor, a measurement aid and not a step of the
+ * product (bankML "par.rs -- the persistent thread pool and row scheduler",
+ * sections "How it is verified" and "Advantages and efficiency": the memory
+ * floor a token's weight stream is compared against).  Reads every byte of
+ * p (device, 16-byte aligned, bytes a positive multiple of 16) once with
+ * plain 16-byte loads from a fixed grid and writes BQ_FLOOR_SINK_WORDS
+ * uint32 to sink (device, 4-byte aligned): the XOR of all of them equals
+ * the XOR of all 32-bit words of the buffer.  Time it with events to get
+ * the read bandwidth a kernel can reach on this GPU.  Allocates nothing.
+ * Asynchronous on s. */
+#define BQ_FLOOR_SINK_WORDS 8192
+int bq_read_floor(const void *p, int64_t bytes, uint32_t *sink, bq_stream s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,13 +21,14 @@ LIB_PATH = os.path.join(_HERE, "libbq.so")
 BQ_Q1_0 = 1
 BQ_Q2_0 = 2
 BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
+BQ_FLOOR_SINK_WORDS = 8192
 BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
 BLOCK_BYTES = 18
 
 EXPORTS = (
     "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
     "bq_quantize_act_q8", "bq_quantize_act_q8_f16", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
-    "bq_sweep_create", "bq_token_sweep", "bq_sweep_destroy",
+    "bq_sweep_create", "bq_token_sweep", "bq_sweep_destroy", "bq_read_floor",
 )
 
 
@@ -103,6 +104,8 @@ def _load() -> ctypes.CDLL:
     lib.bq_token_sweep.argtypes = [vp, vp]
     lib.bq_sweep_destroy.restype = None
     lib.bq_sweep_destroy.argtypes = [vp]
+    lib.bq_read_floor.restype = ctypes.c_int
+    lib.bq_read_floor.argtypes = [vp, i64, vp, vp]
     return lib
 
 
@@ -179,6 +182,16 @@ def bq_quantize_act_q8_f16(x, qa: int, q, d, stream=None) -> None:
     """As bq_quantize_act_q8, with the scales narrowed to f16 values."""
     n = x.numel()
     _check(lib.bq_quantize_act_q8_f16(_dev(x, "x"), n, qa, _dev(q, "q"), _dev(d, "d"), _stream(stream)))
+
+
+def bq_read_floor(buf, sink, stream=None) -> None:
+    """Streaming read of every byte of the device tensor buf (the read
+    bandwidth floor); sink is a device tensor of BQ_FLOOR_SINK_WORDS int32
+    whose XOR equals the XOR of buf's 32-bit words."""
+    if sink.numel() * sink.element_size() < 4 * BQ_FLOOR_SINK_WORDS:
+        raise ValueError(f"bq_read_floor: sink holds fewer than {BQ_FLOOR_SINK_WORDS} words")
+    _check(lib.bq_read_floor(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
+                             _stream(stream)))
 
 
 class Weights:

@@ -176,6 +176,19 @@ BQ_EXPORT int bq_quantize_act_q8_f16(const float *x, int64_t n, int32_t qa, int8
     return quantize_entry("bq_quantize_act_q8_f16", x, n, qa, true, q, d, s);
 }
 
+BQ_EXPORT int bq_read_floor(const void *p, int64_t bytes, uint32_t *sink, bq_stream s)
+{
+    const char *fn = "bq_read_floor";
+    static_assert(kFloorSinkWords == BQ_FLOOR_SINK_WORDS, "sink size of the header");
+    if (!p || !sink)
+        return set_error(BQ_EARG, "%s: null pointer", fn);
+    if (bytes <= 0 || bytes % 16)
+        return set_error(BQ_EARG, "%s: bytes %lld is not a positive multiple of 16", fn, (long long)bytes);
+    if (!aligned(p, 16) || !aligned(sink, 4))
+        return set_error(BQ_EALIGN, "%s: p must be 16-byte aligned, sink 4-byte aligned", fn);
+    return hip_check(fn, launch_floor(p, bytes, sink, static_cast<hipStream_t>(s)));
+}
+
 BQ_EXPORT int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
 {
     return launch_matvec<BQ_Q1_0>("bq_q1_0_matvec", w, a, y, s);

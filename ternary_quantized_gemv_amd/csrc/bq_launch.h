@@ -65,6 +65,11 @@ hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, h
 // launch_wide_q8: the wide shapes (kShapeQuarter .. kShapeWide2) for one product
 // whose activation is already quantized (p[0].q, p[0].d), ncols columns.
 hipError_t launch_wide_q8(int fmt, int qa, GroupShape shape, const GroupArgs &a, int ncols, hipStream_t st);
+// launch_floor: the streaming read of bytes (a multiple of 16) at p, one
+// sink word per wavefront of a fixed grid (bq_floor.hip).
+constexpr int kFloorGrid = 1024;
+constexpr int kFloorSinkWords = 8192;
+hipError_t launch_floor(const void *p, int64_t bytes, uint32_t *sink, hipStream_t st);
 // launch_quantize: n values in blocks of qa, f32 or f16-valued scales (bq_quantize.hip).
 hipError_t launch_quantize(const float *x, int64_t n, int qa, bool f16_scale, int8_t *q, float *d, hipStream_t st);
 

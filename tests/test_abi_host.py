@@ -160,6 +160,19 @@ def test_group_validates_before_launch():
     assert lib.bq_group_matvec(w, 1, x, 128, y, None) == bq.BQ_EARG
 
 
+def test_read_floor_validates_before_launch():
+    """bq_read_floor refuses bad buffers on the host (no GPU is touched)."""
+    lib = bq.lib
+    p, sink = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    assert lib.bq_read_floor(None, 1024, sink, None) == bq.BQ_EARG
+    assert lib.bq_read_floor(p, 1024, None, None) == bq.BQ_EARG
+    assert lib.bq_read_floor(p, 0, sink, None) == bq.BQ_EARG and "bytes" in bq.bq_last_error()
+    assert lib.bq_read_floor(p, 1000, sink, None) == bq.BQ_EARG
+    assert lib.bq_read_floor(ctypes.c_void_p(0x10008), 1024, sink, None) == bq.BQ_EALIGN
+    assert lib.bq_read_floor(p, 1024, ctypes.c_void_p(0x20002), None) == bq.BQ_EALIGN
+    assert "bq_read_floor" in bq.bq_last_error()
+
+
 def test_host_tensors_are_refused():
     torch = pytest.importorskip("torch")
     x = torch.zeros(256)
