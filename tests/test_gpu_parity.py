@@ -192,6 +192,9 @@ FULL = [
     (Q2, 4096, 4096), (Q2, 1024, 4096), (Q2, 12288, 4096), (Q2, 4096, 12288),
     # 100, 313 and 700 tiles: half a tile and two tiles per wide workgroup; the four-wavefront split
     (Q1, 6400, 2048), (Q2, 6390, 4096), (Q1, 20000, 4096), (Q2, 20000, 2048), (Q1, 44800, 1024),
+    # one row per lane with fewer than eight tiles per workgroup: 2374 tiles (five per workgroup),
+    # 2051 ragged tiles (five, the last workgroup one), 2188 tiles of two table chunks each
+    (Q2, 151936, 4096), (Q1, 131201, 1024), (Q2, 140001, 4096),
 ]
 
 
