@@ -122,7 +122,7 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
         memset(&args, 0, sizeof args);
         const GroupShape shape = group_shape(tiles);
         args.p[0] = g;
-        args.wg_end[0] = (int32_t)group_workgroups(shape, tiles);
+        args.wg_end[0] = (int32_t)group_workgroups(shape, tiles, 0);
         args.nprod = 1;
         args.ld_q = a->ld_q;
         args.ld_d = a->ld_d;
@@ -237,12 +237,13 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
     if (w[0].cols % qa)
         return set_error(BQ_EARG, "%s: cols %lld not a multiple of qa %d", fn, (long long)w[0].cols, (int)qa);
     const GroupShape shape = group_shape(tiles);
+    args.rows_tpw = rows_tiles_per_workgroup(tiles, kRowsWaves);
     int64_t wgs = 0;
     for (int i = 0; i < count; ++i) {
         bq_act none;
         memset(&none, 0, sizeof none);
         args.p[i] = make_desc(&w[i], &none, y[i]);
-        wgs += group_workgroups(shape, tiles_of(w[i].rows));
+        wgs += group_workgroups(shape, tiles_of(w[i].rows), args.rows_tpw);
         if (wgs >= (int64_t(1) << 31))
             return set_error(BQ_EARG, "%s: too many rows", fn);
         args.wg_end[i] = (int32_t)wgs;

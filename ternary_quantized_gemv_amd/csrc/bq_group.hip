@@ -472,12 +472,11 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
 
 // -------------------------------------------------------------- row tiles
 // Large groups (the LM head): one row per lane and one tile per wavefront,
-// eight tiles per workgroup, walked as the token sweep walks them -- every
-// lane carries the eight lane accumulators of its row through all blocks in
-// order.  The workgroup builds each chunk's table from x (two slots per
-// thread) once for its eight tiles; payload requests run kRowsDepth blocks
-// ahead across chunk ends.
-constexpr int kRowsWaves = 8;
+// a.rows_tpw (at most eight) tiles per workgroup, walked as the token sweep
+// walks them -- every lane carries the eight lane accumulators of its row
+// through all blocks in order.  The workgroup builds each chunk's table from
+// x (two slots per thread, every wavefront taking part) once for its tiles;
+// payload requests run kRowsDepth blocks ahead across chunk ends.
 constexpr int kRowsThreads = kRowsWaves * 64;
 constexpr int kRowsDepth = 4;
 static_assert(kChunkBlocks * kSlotsPerBlock == 2 * kRowsThreads, "two table slots per thread");
@@ -498,8 +497,10 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
         }
     const int tiles = (g.rows + kTileRows - 1) / kTileRows;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int tile = (wg - wg0) * kRowsWaves + wave;
-    // a wavefront past the product's last tile re-reads it and stores nothing
+    // wavefronts past rows_tpw only help build the tables; a wavefront past
+    // the product's last tile re-reads it and stores nothing
+    const bool busy = wave < a.rows_tpw;
+    const int tile = (wg - wg0) * a.rows_tpw + wave;
     const int tl = min(tile, tiles - 1);
     const rsrc_t wp = rsrc_of(g.bits + (int64_t)tl * g.nb * kTileRows);
     const rsrc_t sp = rsrc_of(g.scales + (int64_t)tl * g.ng * kTileRows);
@@ -513,12 +514,15 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
     load_slot<FMT>(x0, a.x, 0, min(kChunkBlocks, nb), s0);
     load_slot<FMT>(x1, a.x, 0, min(kChunkBlocks, nb), s1);
     __builtin_amdgcn_sched_barrier(0);
+    if (busy) {
 #pragma unroll
-    for (int b = 0; b < kRowsDepth; ++b) {
-        if (b % kScalesPerGroup == 0)
-            sc[(b / kScalesPerGroup) % kScaleSlots] = bload(sp, lo, (uint32_t)min(b / kScalesPerGroup, ng - 1) * kStep);
-        p[b] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int b = 0; b < kRowsDepth; ++b) {
+            if (b % kScalesPerGroup == 0)
+                sc[(b / kScalesPerGroup) % kScaleSlots] =
+                    bload(sp, lo, (uint32_t)min(b / kScalesPerGroup, ng - 1) * kStep);
+            p[b] = bload(wp, lo, (uint32_t)min(b, nb - 1) * kStep);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     float acc[8];
@@ -551,6 +555,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
         __syncthreads();
         load_slot<FMT>(x0, a.x, nx, min(kChunkBlocks, nb - nx), s0);
         load_slot<FMT>(x1, a.x, nx, min(kChunkBlocks, nb - nx), s1);
+        if (!busy)
+            continue;
         if (nbc == kChunkBlocks) {
 #pragma unroll
             for (int i = 0; i < kChunkBlocks; ++i) {
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
         }
     }
     const int row = tile * kTileRows + lane;
-    if (tile < tiles && row < g.rows)
+    if (busy && tile < tiles && row < g.rows)
         g.y[row] = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
 }
 

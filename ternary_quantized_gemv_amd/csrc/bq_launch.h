@@ -16,9 +16,27 @@ struct GroupArgs {
     int32_t wg_end[kGroupMax];
     const float *x;
     int32_t nprod;
-    int32_t pad;
+    int32_t rows_tpw;    // kShapeRows: row tiles per workgroup, one per wavefront (rows_tiles_per_workgroup)
     int64_t ld_q, ld_d;  // launch_wide_q8: activation columns (grid row c reads q + c ld_q, d + c ld_d)
 };
+
+// Row tiles per workgroup of the one-row-per-lane kernels (matvec_kernel,
+// rows_kernel: one tile per wavefront, at most `waves`), for `total` tiles
+// over all columns or products of one launch.  Up to 2048 tiles a full
+// workgroup each leaves at most one workgroup per compute unit.  Beyond
+// that, full workgroups would put two on some units and one on others, and
+// the doubly loaded units set the time; spreading the tiles over up to 512
+// workgroups (two per unit) of fewer busy wavefronts evens the load
+// (151936x4096 single product, 2374 tiles: five per workgroup, Q1_0 30.0 ->
+// 24.7 us, Q2_0 52-55 -> 43-45 us).  Past 4096 tiles every workgroup is full
+// again.
+inline int rows_tiles_per_workgroup(int64_t total, int waves)
+{
+    if (total <= 2048)
+        return waves;
+    const int64_t tpw = (total + 511) / 512;
+    return tpw > waves ? waves : (int)tpw;
+}
 
 // Kernel launchers (host side).  Each validates nothing: the entry points in
 // bq_api.cpp check every argument first.  They return hipGetLastError().
@@ -42,7 +60,7 @@ enum GroupShape {
     kShapeHalf = 1,     // half a tile (32 rows) per sixteen-wavefront workgroup
     kShapeWide = 2,     // one tile per sixteen-wavefront workgroup
     kShapeWide2 = 3,    // two tiles per sixteen-wavefront workgroup, one after the other
-    kShapeRows = 4,     // eight tiles per workgroup, one per wavefront, one row per lane
+    kShapeRows = 4,     // up to eight tiles per workgroup (GroupArgs::rows_tpw), one per wavefront, one row per lane
 };
 // The finest shape whose workgroups fit one round of the GPU's 256 compute
 // units (one sixteen-wavefront workgroup each), and its workgroup count.
@@ -51,16 +69,17 @@ inline GroupShape group_shape(int64_t tiles)
     return tiles <= 64 ? kShapeQuarter : tiles <= 128 ? kShapeHalf : tiles <= 256 ? kShapeWide
            : tiles <= 512 ? kShapeWide2 : kShapeRows;
 }
-inline int64_t group_workgroups(GroupShape shape, int64_t tiles)
+inline int64_t group_workgroups(GroupShape shape, int64_t tiles, int rows_tpw)
 {
     switch (shape) {
     case kShapeQuarter: return 4 * tiles;
     case kShapeHalf: return 2 * tiles;
     case kShapeWide: return tiles;
     case kShapeWide2: return (tiles + 1) / 2;
-    default: return (tiles + 7) / 8;
+    default: return (tiles + rows_tpw - 1) / rows_tpw;
     }
 }
+constexpr int kRowsWaves = 8;  // wavefronts of a kShapeRows workgroup
 hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, hipStream_t st);
 // launch_wide_q8: the wide shapes (kShapeQuarter .. kShapeWide2) for one product
 // whose activation is already quantized (p[0].q, p[0].d), ncols columns.

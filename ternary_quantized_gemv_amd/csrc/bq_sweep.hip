@@ -363,27 +363,10 @@ __global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void sweep_kernel(const
     run_item<FMT, QA>(g, it.tile0, it.ntiles, T, D1);
 }
 
-// Row tiles per matvec_kernel workgroup.  Up to 2048 tiles (all columns
-// together) eight per workgroup leave at most one workgroup per compute
-// unit.  Beyond that, eight per workgroup would put two full workgroups on
-// some units and one on others, and the doubly loaded units set the time;
-// spreading the tiles over up to 512 workgroups (two per unit) of fewer
-// busy wavefronts evens the load (151936x4096, 2374 tiles: five per
-// workgroup, Q1_0 30.0 -> 24.7 us, Q2_0 52-55 -> 43-45 us).  Past 4096
-// tiles every workgroup is full again.
-static int rows_tiles_per_workgroup(int tiles, int ncols)
-{
-    const int64_t total = (int64_t)tiles * ncols;
-    if (total <= 2048)
-        return kWaves;
-    const int64_t tpw = (total + 511) / 512;
-    return tpw > kWaves ? kWaves : (int)tpw;
-}
-
 template <int FMT>
 static hipError_t rows_fmt(int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols, hipStream_t st)
 {
-    const int tpw = rows_tiles_per_workgroup(tiles, ncols);
+    const int tpw = rows_tiles_per_workgroup((int64_t)tiles * ncols, kWaves);
     const dim3 grid((tiles + tpw - 1) / tpw, ncols);
     switch (qa) {
     case 32: hipLaunchKernelGGL((matvec_kernel<FMT, 32>), grid, dim3(kThreads), 0, st, g, ld_q, ld_d, tiles, tpw); break;

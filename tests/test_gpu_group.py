@@ -85,6 +85,9 @@ CASES = [
     (1, [40000, 100], 40, 128, "normal"),           # 627 tiles, 32 + 8 blocks
     (2, [33000], 70, 64, "nearties"),               # 516 tiles, three chunks
     (2, [7000, 1100, 300], 70, 32, "special"),      # 133 tiles, three chunks, odd tile counts
+    # more than 2048 tiles: fewer busy wavefronts per row-tile workgroup, the rest only build tables
+    (1, [100000, 40001, 3], 8, 128, "nearties"),     # 2190 tiles: five per workgroup, ragged last workgroups
+    (2, [131072, 2000], 40, 64, "special"),         # 2080 tiles: five per workgroup, 32 + 8 blocks
 ]
 
 
