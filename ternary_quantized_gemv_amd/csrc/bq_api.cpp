@@ -122,7 +122,7 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
         memset(&args, 0, sizeof args);
         const GroupShape shape = group_shape(tiles);
         args.p[0] = g;
-        args.wg_end[0] = (int32_t)group_workgroups(shape, tiles, 0);
+        args.wg_end[0] = (int32_t)group_workgroups(shape, tiles, kRowsWaves);  // a wide shape: rows_tpw unused
         args.nprod = 1;
         args.ld_q = a->ld_q;
         args.ld_d = a->ld_d;
