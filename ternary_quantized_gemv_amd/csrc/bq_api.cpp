@@ -17,19 +17,20 @@
 
 namespace bq {
 
-// Kernel choice (measured on MI355X).  bq_group_matvec, and single-column
-// bq_q1_0_matvec / bq_q2_0_matvec: group_shape() picks the finest workgroup
-// shape whose workgroups fit one round of the 256 compute units -- half a
+// Kernel choice (measured on MI355X).  bq_group_matvec, and
+// bq_q1_0_matvec / bq_q2_0_matvec counting the tiles of all activation
+// columns together: group_shape() picks the finest workgroup shape whose
+// workgroups fit one round of the 256 compute units -- a quarter, half a
 // tile, one tile or two tiles per sixteen-wavefront workgroup (wide_kernel,
-// a tile's blocks spread over the whole CU) up to 512 tiles, beyond that one
-// row per lane with eight tiles per workgroup (rows_kernel for groups;
-// matvec_kernel, the sweep's walk, for single products).  Several columns:
-// four wavefronts per tile, one grid row per column (launch_split), up to
-// kSplitMaxTiles tiles, above that four columns per workgroup from
-// interleaved tables (launch_cols) for at least kColsMinCols columns, else
-// one row per lane per column: there the per-column kernels re-stream the
-// weights once per column, while on smaller matrices their extra parallelism
-// wins.
+// a tile's blocks spread over the whole CU; one grid row per column) up to
+// 512 tiles, beyond that one row per lane with up to eight tiles per
+// workgroup (rows_kernel for groups; matvec_kernel, the sweep's walk, for
+// single products).  Several columns past 512 tiles in all: four wavefronts
+// per tile, one grid row per column (launch_split), up to kSplitMaxTiles
+// tiles per column, above that four columns per workgroup from interleaved
+// tables (launch_cols) for at least kColsMinCols columns, else one row per
+// lane per column: there the per-column kernels re-stream the weights once
+// per column, while on smaller matrices their extra parallelism wins.
 constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
 
@@ -117,10 +118,11 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
     const int tiles = (int)tiles_of(w->rows);
     hipStream_t st = static_cast<hipStream_t>(s);
     hipError_t e;
-    if (a->ncols == 1 && group_shape(tiles) != kShapeRows) {
+    if (group_shape((int64_t)tiles * a->ncols) != kShapeRows) {
+        // the shape is chosen for all columns together (grid row c = column c)
         GroupArgs args;
         memset(&args, 0, sizeof args);
-        const GroupShape shape = group_shape(tiles);
+        const GroupShape shape = group_shape((int64_t)tiles * a->ncols);
         args.p[0] = g;
         args.wg_end[0] = (int32_t)group_workgroups(shape, tiles, kRowsWaves);  // a wide shape: rows_tpw unused
         args.nprod = 1;

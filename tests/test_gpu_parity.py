@@ -125,6 +125,25 @@ def test_matvec_columns(fmt, ncols):
     assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, f"columns fmt={fmt} ncols={ncols}")
 
 
+# Several columns on the wide shapes, chosen for the tiles of all columns
+# together: quarter (2 x 30 tiles), half (3 x 32), one tile (5 x 47), two
+# tiles in turn (4 x 65, 4 x 128 = 512), then the split walk (3 x 200).
+WIDE_COLS = [
+    (Q1, 1900, 4096, 2, 128, "quant"), (Q2, 2000, 2048, 3, 64, "raw"), (Q1, 3000, 4096, 5, 32, "mixed"),
+    (Q2, 4100, 2048, 4, 128, "quant"), (Q1, 8192, 1024, 4, 64, "raw"), (Q2, 12800, 1024, 3, 128, "quant"),
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", WIDE_COLS,
+                         ids=[f"q{f}-{r}x{c}-n{n}-qa{a}-{g}" for f, r, c, n, a, g in WIDE_COLS])
+def test_columns_wide_shapes(fmt, rows, cols, ncols, qa, regime):
+    name = f"wide columns fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
+    log(name)
+    w, q, d = _batch_inputs(fmt, rows, cols, ncols, qa, regime)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
+
+
 def _batch_cases():
     out = []
     for fmt in (Q1, Q2):
@@ -154,8 +173,8 @@ def _batch_inputs(fmt, rows, cols, ncols, qa, regime):
 
 @pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", _batch_cases())
 def test_small_batch_parity(fmt, rows, cols, ncols, qa, regime):
-    """Several activation columns against one small matrix (the single-column
-    kernels, one grid row per column)."""
+    """Several activation columns against one small matrix (the wide shapes,
+    one grid row per column)."""
     name = f"batch fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
     log(name)
     w, q, d = _batch_inputs(fmt, rows, cols, ncols, qa, regime)
