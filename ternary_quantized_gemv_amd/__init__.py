@@ -22,6 +22,7 @@ BQ_Q1_0 = 1
 BQ_Q2_0 = 2
 BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
 BQ_FLOOR_SINK_WORDS = 8192
+BQ_ABI_VERSION = 4  # include/bq.h
 BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
 BLOCK_BYTES = 18
 
@@ -81,6 +82,9 @@ def _load() -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.bq_abi_version.restype = ctypes.c_int
     lib.bq_abi_version.argtypes = []
+    if lib.bq_abi_version() != BQ_ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.bq_abi_version()}, this binding {BQ_ABI_VERSION}: "
+                          "rebuild it with `python ternary_quantized_gemv_amd/build.py`")
     lib.bq_last_error.restype = ctypes.c_char_p
     lib.bq_last_error.argtypes = []
     lib.bq_packed_bytes.restype = ctypes.c_int
