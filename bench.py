@@ -13,8 +13,9 @@ roofline time and fraction, the streaming-read floor measured live on the same
 GPU (k_floor, bq_read_floor over 1 GiB) and every fraction against it, the
 oracle on the host's cores with a bit-for-bit check of the GPU's outputs (and
 their largest relative error), and the pages' laptop CPU figures as context.
-The line also reports, as context, the same token run as a dependency-ordered
-decode (field decode_chain; --no-chain skips it).
+The line also reports, as context, the same token in one launch that
+quantizes the f32 activations itself (field one_launch_token), and run as a
+dependency-ordered decode (field decode_chain; --no-chain skips it).
 [--act q8_128|q8_0]: q8_0 quantizes with qa 32 and f16-valued scales (the
 pages' activation flavour) instead of qa 128 with f32 scales.
 
@@ -416,6 +417,34 @@ def main():
     achieved = sw.sweep_bytes() / (sweep_ms * 1e-3) / 1e9
     y_gpu = sw.y.cpu().numpy()
 
+    # context, not the headline: the same token in ONE launch that quantizes
+    # the f32 activations itself (bq_sweep_create_x), checked against the
+    # two-launch outputs bit for bit
+    fused = None
+    if not q8_0:
+        sw.y.fill_(float("nan"))
+        for _ in range(args.warmup):
+            sw.sweep_fused()
+        torch.cuda.synchronize()
+        same = bool(np.array_equal(sw.y.cpu().numpy().view(np.uint32), y_gpu.view(np.uint32)))
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b, c in fev:
+            b.record(stream)
+            sw.sweep_fused()
+            c.record(stream)
+        torch.cuda.synchronize()
+        f_ms = (time.perf_counter() - t0) * 1e3 / K
+        f_kernel = float(np.mean([b.elapsed_time(c) for b, c in fev]))
+        fused = {"ms_per_step": round(f_ms, 5), "value": round(sw.fused_bytes() / (f_ms * 1e-3) / 1e9, 2),
+                 "kernel_ms": round(f_kernel, 5), "bytes_per_launch": sw.fused_bytes(),
+                 "kernel_GB_s": round(sw.fused_bytes() / (f_kernel * 1e-3) / 1e9, 2),
+                 "same_bits_as_two_launch": same,
+                 "how": "one bq_token_sweep launch of a bq_sweep_create_x plan (f32 activations quantized in the launch)"}
+        log(f"one-launch token: {f_ms * 1e3:.1f} us per step, kernel {f_kernel * 1e3:.1f} us, same bits: {same}")
+
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -503,6 +532,7 @@ def main():
             "ternary_token_s_at_3_threads": [0.23, 0.25],
             "machine": "the pages' laptop CPU (other hardware; context, not the target)",
         },
+        "one_launch_token": fused,
         "decode_chain": chain,
     }
     sw.close()

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 4
+#define BQ_ABI_VERSION 5
 
 /* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
  * then 16 payload bytes).
@@ -104,6 +104,14 @@ typedef struct bq_gemv {
     bq_act a; /* a.ncols must be 1 */
     float *y; /* device, 4-byte aligned: w.rows floats */
 } bq_gemv;
+
+/* One product of a sweep that quantizes in the launch: y = W q(x), with q
+ * the activation quantizer's output for the f32 vector x. */
+typedef struct bq_gemv_x {
+    bq_weights w;
+    const float *x; /* device, 16-byte aligned: w.cols floats */
+    float *y;       /* device, 4-byte aligned: w.rows floats */
+} bq_gemv_x;
 
 typedef struct bq_sweep bq_sweep; /* opaque plan */
 
@@ -182,6 +190,21 @@ int bq_group_matvec(const bq_weights *w, int32_t count, const float *x, int32_t 
  * allocation, freed by bq_sweep_destroy).  Must be called with the device of
  * the pointers current.  *plan receives the plan, or NULL on failure. */
 int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan);
+
+/* As bq_sweep_create, for products whose activations are f32 vectors that
+ * the launch itself quantizes: every workgroup quantizes the blocks of x it
+ * needs into on-chip memory, with bq_quantize_act_q8's rule and block length
+ * qa (32, 64 or 128; every w.cols a multiple of qa), before building its
+ * tables, so a decode token's products run from their f32 inputs in one
+ * launch and the int8 vectors never go to memory (bankML "par.rs -- the
+ * persistent thread pool and row scheduler", section "Summary": one token's
+ * 253 products; bankML "gpu/ -- the video-card component", section
+ * "kernels.rs -- the Q1_0 kernels": the activation is quantized per call).
+ * Each y equals what bq_quantize_act_q8 followed by bq_q1_0_matvec /
+ * bq_q2_0_matvec would give.  No y may overlap an x.  Allocation, errors and
+ * ownership as bq_sweep_create; run and release the plan with
+ * bq_token_sweep and bq_sweep_destroy. */
+int bq_sweep_create_x(const bq_gemv_x *list, int32_t count, int32_t qa, bq_sweep **plan);
 
 /* Enqueue the whole plan on s as one kernel launch.  Each entry's y equals
  * what bq_q1_0_matvec / bq_q2_0_matvec would write for it. */

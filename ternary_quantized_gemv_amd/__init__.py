@@ -22,14 +22,14 @@ BQ_Q1_0 = 1
 BQ_Q2_0 = 2
 BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
 BQ_FLOOR_SINK_WORDS = 8192
-BQ_ABI_VERSION = 4  # include/bq.h
+BQ_ABI_VERSION = 5  # include/bq.h
 BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
 BLOCK_BYTES = 18
 
 EXPORTS = (
     "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
     "bq_quantize_act_q8", "bq_quantize_act_q8_f16", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
-    "bq_sweep_create", "bq_token_sweep", "bq_sweep_destroy", "bq_read_floor",
+    "bq_sweep_create", "bq_sweep_create_x", "bq_token_sweep", "bq_sweep_destroy", "bq_read_floor",
 )
 
 
@@ -52,6 +52,10 @@ class bq_act(ctypes.Structure):
 
 class bq_gemv(ctypes.Structure):
     _fields_ = [("w", bq_weights), ("a", bq_act), ("y", ctypes.c_void_p)]
+
+
+class bq_gemv_x(ctypes.Structure):
+    _fields_ = [("w", bq_weights), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 def _hip_runtimes() -> set:
@@ -104,6 +108,8 @@ def _load() -> ctypes.CDLL:
     lib.bq_group_matvec.restype = ctypes.c_int
     lib.bq_group_matvec.argtypes = [ctypes.POINTER(bq_weights), i32, vp, i32, ctypes.POINTER(vp), vp]
     lib.bq_sweep_create.argtypes = [ctypes.POINTER(bq_gemv), i32, ctypes.POINTER(vp)]
+    lib.bq_sweep_create_x.restype = ctypes.c_int
+    lib.bq_sweep_create_x.argtypes = [ctypes.POINTER(bq_gemv_x), i32, i32, ctypes.POINTER(vp)]
     lib.bq_token_sweep.restype = ctypes.c_int
     lib.bq_token_sweep.argtypes = [vp, vp]
     lib.bq_sweep_destroy.restype = None
@@ -298,6 +304,21 @@ def bq_sweep_create(entries) -> Sweep:
         arr[i].y = _dev(y, "y")
     h = ctypes.c_void_p()
     _check(lib.bq_sweep_create(arr, len(entries), ctypes.byref(h)))
+    return Sweep(h.value, list(entries))
+
+
+def bq_sweep_create_x(entries, qa: int) -> Sweep:
+    """entries: [(Weights, x f32 tensor of length cols, y tensor)]; the launch
+    quantizes each x in blocks of qa."""
+    arr = (bq_gemv_x * len(entries))()
+    for i, (w, x, y) in enumerate(entries):
+        if x.numel() != w.cols:
+            raise ValueError(f"bq_sweep_create_x: entry {i}: x has {x.numel()} values, cols is {w.cols}")
+        arr[i].w = w.c()
+        arr[i].x = _dev(x, "x")
+        arr[i].y = _dev(y, "y")
+    h = ctypes.c_void_p()
+    _check(lib.bq_sweep_create_x(arr, len(entries), qa, ctypes.byref(h)))
     return Sweep(h.value, list(entries))
 
 

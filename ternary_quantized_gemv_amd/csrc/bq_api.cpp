@@ -145,6 +145,7 @@ using namespace bq;
 struct bq_sweep {
     int fmt;
     int qa;
+    bool quantize;  // f32 activations, quantized in the launch (bq_sweep_create_x)
     int nitems;
     int count;
     void *dev;  // descriptors, then work items
@@ -255,38 +256,17 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
     return hip_check(fn, launch_group(fmt, qa, shape, args, static_cast<hipStream_t>(s)));
 }
 
-BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan)
+// The work items of a plan over the products descs (validated), balanced
+// over the GPU, and the plan that owns their device copy.
+static int make_plan(const char *fn, std::vector<GemvDesc> &descs, int fmt, int qa, bool quantize, bq_sweep **plan)
 {
-    const char *fn = "bq_sweep_create";
-    if (!plan)
-        return set_error(BQ_EARG, "%s: null plan pointer", fn);
-    *plan = nullptr;
-    if (!list || count < 1)
-        return set_error(BQ_EARG, "%s: empty list", fn);
-    const int fmt = list[0].w.fmt, qa = list[0].a.qa;
-    std::vector<GemvDesc> descs((size_t)count);
     std::vector<WorkItem> items;
-    for (int i = 0; i < count; ++i) {
-        const bq_gemv &e = list[i];
-        char where[96];
-        snprintf(where, sizeof where, "%s: entry %d", fn, i);
-        if (e.w.fmt != fmt || e.a.qa != qa)
-            return set_error(BQ_EARG, "%s: every entry must share the format and qa of entry 0", where);
-        int rc = check_weights(where, &e.w, fmt);
-        if (!rc)
-            rc = check_act(where, &e.a, e.w.cols, 1);
-        if (rc)
-            return rc;
-        if (!e.y)
-            return set_error(BQ_EARG, "%s: null y", where);
-        if (!aligned(e.y, 4))
-            return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
-        descs[(size_t)i] = make_desc(&e.w, &e.a, e.y);
-        const int tiles = (int)tiles_of(e.w.rows);
-        const int per_item = descs[(size_t)i].nb <= kChunkBlocks ? kWaves * kMaxRounds : kWaves;
+    for (size_t i = 0; i < descs.size(); ++i) {
+        const int tiles = (int)tiles_of(descs[i].rows);
+        const int per_item = descs[i].nb <= kChunkBlocks ? kWaves * kMaxRounds : kWaves;
         for (int t = 0; t < tiles; t += per_item) {
             WorkItem it;
-            it.gemv = i;
+            it.gemv = (int32_t)i;
             it.tile0 = t;
             it.ntiles = std::min(per_item, tiles - t);
             it.pad = 0;
@@ -337,7 +317,8 @@ BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **pla
     }
     p->fmt = fmt;
     p->qa = qa;
-    p->count = count;
+    p->quantize = quantize;
+    p->count = (int)descs.size();
     p->nitems = (int)sorted.size();
     p->dev = dev;
     p->descs = static_cast<const GemvDesc *>(dev);
@@ -346,12 +327,77 @@ BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **pla
     return BQ_OK;
 }
 
+BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan)
+{
+    const char *fn = "bq_sweep_create";
+    if (!plan)
+        return set_error(BQ_EARG, "%s: null plan pointer", fn);
+    *plan = nullptr;
+    if (!list || count < 1)
+        return set_error(BQ_EARG, "%s: empty list", fn);
+    const int fmt = list[0].w.fmt, qa = list[0].a.qa;
+    std::vector<GemvDesc> descs((size_t)count);
+    for (int i = 0; i < count; ++i) {
+        const bq_gemv &e = list[i];
+        char where[96];
+        snprintf(where, sizeof where, "%s: entry %d", fn, i);
+        if (e.w.fmt != fmt || e.a.qa != qa)
+            return set_error(BQ_EARG, "%s: every entry must share the format and qa of entry 0", where);
+        int rc = check_weights(where, &e.w, fmt);
+        if (!rc)
+            rc = check_act(where, &e.a, e.w.cols, 1);
+        if (rc)
+            return rc;
+        if (!e.y)
+            return set_error(BQ_EARG, "%s: null y", where);
+        if (!aligned(e.y, 4))
+            return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
+        descs[(size_t)i] = make_desc(&e.w, &e.a, e.y);
+    }
+    return make_plan(fn, descs, fmt, qa, false, plan);
+}
+
+BQ_EXPORT int bq_sweep_create_x(const bq_gemv_x *list, int32_t count, int32_t qa, bq_sweep **plan)
+{
+    const char *fn = "bq_sweep_create_x";
+    if (!plan)
+        return set_error(BQ_EARG, "%s: null plan pointer", fn);
+    *plan = nullptr;
+    if (!list || count < 1)
+        return set_error(BQ_EARG, "%s: empty list", fn);
+    if (qa != 32 && qa != 64 && qa != 128)
+        return set_error(BQ_EARG, "%s: qa %d not in {32, 64, 128}", fn, (int)qa);
+    const int fmt = list[0].w.fmt;
+    std::vector<GemvDesc> descs((size_t)count);
+    for (int i = 0; i < count; ++i) {
+        const bq_gemv_x &e = list[i];
+        char where[96];
+        snprintf(where, sizeof where, "%s: entry %d", fn, i);
+        if (e.w.fmt != fmt)
+            return set_error(BQ_EARG, "%s: every entry must share the format of entry 0", where);
+        const int rc = check_weights(where, &e.w, fmt);
+        if (rc)
+            return rc;
+        if (e.w.cols % qa)
+            return set_error(BQ_EARG, "%s: cols %lld not a multiple of qa %d", where, (long long)e.w.cols, (int)qa);
+        if (!e.x || !e.y)
+            return set_error(BQ_EARG, "%s: null x or y", where);
+        if (!aligned(e.x, 16) || !aligned(e.y, 4))
+            return set_error(BQ_EALIGN, "%s: x must be 16-byte aligned, y 4-byte aligned", where);
+        bq_act none;
+        memset(&none, 0, sizeof none);
+        descs[(size_t)i] = make_desc(&e.w, &none, e.y);
+        descs[(size_t)i].x = e.x;
+    }
+    return make_plan(fn, descs, fmt, qa, true, plan);
+}
+
 BQ_EXPORT int bq_token_sweep(const bq_sweep *plan, bq_stream s)
 {
     const char *fn = "bq_token_sweep";
     if (!plan)
         return set_error(BQ_EARG, "%s: null plan", fn);
-    return hip_check(fn, launch_sweep(plan->fmt, plan->qa, (unsigned)plan->nitems, plan->descs, plan->items,
+    return hip_check(fn, launch_sweep(plan->fmt, plan->qa, plan->quantize, (unsigned)plan->nitems, plan->descs, plan->items,
                                       static_cast<hipStream_t>(s)));
 }
 

@@ -50,6 +50,76 @@ __device__ __forceinline__ int quant_of(float x, float db)
     return (int)r;
 }
 
+// The quantizer's rule (quant_of) for the values of one activation block
+// with scale db, through a reciprocal.  p = x * rcp(db) is within 2^-15 of
+// x / db (|x| <= 127.0001 db, v_rcp_f32 is accurate to 1 ulp), and the
+// correctly rounded x / db within 2^-18 of it, so both round to the same
+// integer unless p lies within 2^-14 of a half-integer.  Those values, and
+// scales too small for a safe reciprocal (or zero), take the correctly
+// rounded division.  Zero comes out as +0, as quant_of's integer does.
+template <int V>
+__device__ __forceinline__ void quant_block(const float (&x)[V], float db, float (&q)[V])
+{
+    const float rdb = __builtin_amdgcn_rcpf(db);
+    bool slow = !(db >= 0x1p-120f);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const float p = x[i] * rdb;
+        const float a = fabsf(p);
+        const float fl = floorf(a);
+        const float dist = a - fl - 0.5f;  // exact wherever it decides
+        slow |= fabsf(dist) <= 0x1p-14f;
+        q[i] = __builtin_copysignf(dist >= 0.0f ? fl + 1.0f : fl, p) + 0.0f;
+    }
+    if (slow) {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            q[i] = (float)quant_of(x[i], db);
+    }
+}
+
+// The activation quantizer's rule (quant_block: the bits of quant_of) applied to nvals values at x
+// (a whole number of activation blocks, 16-byte aligned), eight per thread,
+// into LDS: Qs[i] = the quant of x[i], Ds[i / QA] = the block's scale
+// amax / 127.  A block's QA / 8 threads are consecutive lanes of one
+// wavefront and combine their |x| maxima by butterfly shuffles (max is exact
+// in any order); threads past the values take part with zeros.
+template <int QA>
+__device__ __forceinline__ void quantize_chunk(int8_t *Qs, float *Ds, const float *x, int nvals)
+{
+    constexpr int TPB = QA / 8;
+    for (int t0 = 0; t0 < nvals / 8; t0 += (int)blockDim.x) {
+        const int t = t0 + (int)threadIdx.x;
+        const bool live = t < nvals / 8;
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, b = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (live) {
+            a = reinterpret_cast<const f32x4 *>(x)[2 * t];
+            b = reinterpret_cast<const f32x4 *>(x)[2 * t + 1];
+        }
+        float m = fmaxf(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))),
+                        fmaxf(fmaxf(fabsf(b[0]), fabsf(b[1])), fmaxf(fabsf(b[2]), fabsf(b[3]))));
+#pragma unroll
+        for (int off = 1; off < TPB; off <<= 1)
+            m = fmaxf(m, __shfl_xor(m, off, 64));
+        const float db = m / 127.0f;
+        if (live) {
+            const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            float qv[8];
+            quant_block<8>(v, db, qv);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo |= (uint32_t)((int)qv[e] & 0xFF) << (8 * e);
+                hi |= (uint32_t)((int)qv[4 + e] & 0xFF) << (8 * e);
+            }
+            reinterpret_cast<uint32_t *>(Qs)[2 * t] = lo;
+            reinterpret_cast<uint32_t *>(Qs)[2 * t + 1] = hi;
+            if (t % TPB == 0)
+                Ds[t / TPB] = db;
+        }
+    }
+}
+
 // --------------------------------------------------------------- tables
 // Each thread writes one quarter (4 entries, 16 bytes) of a slot's table per
 // step, so a wavefront's stores cover 1 KiB of consecutive LDS addresses.

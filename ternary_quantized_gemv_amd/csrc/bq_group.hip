@@ -45,34 +45,6 @@ __device__ __forceinline__ float group_max(float m)
     return m;
 }
 
-// The quantizer's rule (quant_of) for the values of one activation block
-// with scale db, through a reciprocal.  p = x * rcp(db) is within 2^-15 of
-// x / db (|x| <= 127.0001 db, v_rcp_f32 is accurate to 1 ulp), and the
-// correctly rounded x / db within 2^-18 of it, so both round to the same
-// integer unless p lies within 2^-14 of a half-integer.  Those values, and
-// scales too small for a safe reciprocal (or zero), take the correctly
-// rounded division.  Zero comes out as +0, as quant_of's integer does.
-template <int V>
-__device__ __forceinline__ void quant_block(const float (&x)[V], float db, float (&q)[V])
-{
-    const float rdb = __builtin_amdgcn_rcpf(db);
-    bool slow = !(db >= 0x1p-120f);
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const float p = x[i] * rdb;
-        const float a = fabsf(p);
-        const float fl = floorf(a);
-        const float dist = a - fl - 0.5f;  // exact wherever it decides
-        slow |= fabsf(dist) <= 0x1p-14f;
-        q[i] = __builtin_copysignf(dist >= 0.0f ? fl + 1.0f : fl, p) + 0.0f;
-    }
-    if (slow) {
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-            q[i] = (float)quant_of(x[i], db);
-    }
-}
-
 constexpr int kScaleSlots = 4;  // scale groups held in a ring (the current one, the next, spares)
 
 // ------------------------------------------------------------- wide tiles

@@ -44,8 +44,9 @@ inline int rows_tiles_per_workgroup(int64_t total, int waves)
 // launch_rows: one row per lane, one grid row per activation column (bq_sweep.hip).
 hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
                        hipStream_t st);
-// launch_sweep: the work items of a sweep plan (bq_sweep.hip).
-hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
+// launch_sweep: the work items of a sweep plan (bq_sweep.hip); quantize:
+// the descriptors carry f32 activations (GemvDesc::x), quantized in the launch.
+hipError_t launch_sweep(int fmt, int qa, bool quantize, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
                         hipStream_t st);
 // launch_split: four wavefronts per 64-row tile (bq_sweep.hip).
 hipError_t launch_split(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,

@@ -62,6 +62,19 @@ struct ChunkScales {
         }
     }
 
+    // the same from the chunk's scales in LDS (wave-uniform reads, then
+    // scalar registers)
+    __device__ __forceinline__ void load_lds(const float *d_chunk)
+    {
+        if (kScalar) {
+#pragma unroll
+            for (int i = 0; i < (kScalar ? ND : 1); ++i) {
+                dv[i] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, d_chunk[i])));
+                asm volatile("" : "+s"(dv[i]));
+            }
+        }
+    }
+
     __device__ __forceinline__ f32x4 get(const float *__restrict__ D1, int b) const
     {
         f32x4 r;
@@ -234,12 +247,38 @@ __device__ __forceinline__ void store_row(const GemvDesc &g, int tile, int lane,
         g.y[row] = y;
 }
 
+// The table (and D1) of the chunk of nbc blocks at value k0.  With X the
+// f32 activation g.x is first quantized into LDS (Qs, Ds: the quantizer's
+// bits, as bq_quantize_act_q8 would write them) and the table is built from
+// there; otherwise from the quants g.q, g.d in memory.
+template <int FMT, int QA, bool X>
+__device__ __forceinline__ void chunk_table(const GemvDesc &g, int k0, int nbc, float *T, float *D1, int8_t *Qs,
+                                            float *Ds)
+{
+    const int8_t *q = g.q;
+    const float *d = g.d;
+    int kq = k0;
+    if (X) {
+        quantize_chunk<QA>(Qs, Ds, g.x + k0, nbc * (FMT == BQ_Q1_0 ? 128 : 64));
+        __syncthreads();
+        q = Qs;
+        d = Ds;
+        kq = 0;
+    }
+    if (FMT == BQ_Q1_0)
+        build_table_q1<QA>(T, D1, q, d, kq, nbc);
+    else
+        build_table_q2<QA>(T, D1, q, d, kq, nbc);
+}
+
 // Rows [64*tile0, 64*(tile0+ntiles)) of one product; wavefront w takes tiles
 // tile0 + w, tile0 + w + kWaves, ...  Rows of at most one chunk share one
 // table for every tile of the item; longer rows (ntiles <= kWaves) walk the
-// chunks with a table rebuild between barriers.
-template <int FMT, int QA>
-__device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1)
+// chunks with a table rebuild between barriers.  X: the activation is f32
+// and quantized chunk by chunk into Qs, Ds (chunk_table).
+template <int FMT, int QA, bool X>
+__device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1, int8_t *Qs,
+                                         float *Ds)
 {
     // the wavefront index is wave-uniform: say so, so that tile addresses live in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -256,14 +295,15 @@ __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntile
         int tile = tile0 + wave;
         if (tile < tend && nbc == kChunkBlocks)
             prefetch_chunk(pf, wtile(tile, 0), stile(tile, 0), lo);
-        if (FMT == BQ_Q1_0)
-            build_table_q1<QA>(T, D1, g.q, g.d, 0, nbc);
-        else
-            build_table_q2<QA>(T, D1, g.q, g.d, 0, nbc);
+        chunk_table<FMT, QA, X>(g, 0, nbc, T, D1, Qs, Ds);
         __syncthreads();
         ChunkScales<FMT, QA> cs;
-        if (nbc == kChunkBlocks)
-            cs.load(g.d);
+        if (nbc == kChunkBlocks) {
+            if (X)
+                cs.load_lds(Ds);
+            else
+                cs.load(g.d);
+        }
         for (; tile < tend; tile += kWaves) {
 #pragma unroll
             for (int L = 0; L < 8; ++L)
@@ -291,15 +331,15 @@ __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntile
         const int k0 = (cb / kChunkBlocks) * per_chunk;
         if (cb > 0)
             __syncthreads();  // every wavefront is done with the previous table
-        if (FMT == BQ_Q1_0)
-            build_table_q1<QA>(T, D1, g.q, g.d, k0, nbc);
-        else
-            build_table_q2<QA>(T, D1, g.q, g.d, k0, nbc);
+        chunk_table<FMT, QA, X>(g, k0, nbc, T, D1, Qs, Ds);
         __syncthreads();
         if (active) {
             if (nbc == kChunkBlocks) {
                 ChunkScales<FMT, QA> cs;
-                cs.load(g.d + k0 / QA);
+                if (X)
+                    cs.load_lds(Ds);
+                else
+                    cs.load(g.d + k0 / QA);
                 const bool has_next = cb + 2 * kChunkBlocks <= g.nb;
                 run_full_chunk<FMT, QA>(T, D1, cs, wtile(tile, cb), stile(tile, cb), wtile(tile, cb + kChunkBlocks),
                                         stile(tile, cb + kChunkBlocks), has_next, lo, pf, acc);
@@ -344,7 +384,7 @@ __global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void matvec_kernel(Gemv
     g.d += c * ld_d;
     g.y += (int64_t)c * g.rows;
     const int tile0 = blockIdx.x * tpw;
-    run_item<FMT, QA>(g, tile0, min(tpw, tiles - tile0), T, D1);
+    run_item<FMT, QA, false>(g, tile0, min(tpw, tiles - tile0), T, D1, nullptr, nullptr);
 }
 
 // With activation blocks shorter than 128 values the chunk's activation
@@ -352,15 +392,21 @@ __global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void matvec_kernel(Gemv
 // than four wavefronts per SIMD (two workgroups per CU) leave room for; the
 // second bound holds those instantiations to 128 registers.  The qa-128
 // code is unaffected.
-template <int FMT, int QA>
-__global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void sweep_kernel(const GemvDesc *__restrict__ descs,
+// X: the products' activations are f32 and every workgroup quantizes the
+// chunks it needs (the quantizer's bits) into LDS before building its table;
+// the bound keeps those instantiations at four wavefronts per SIMD too.
+template <int FMT, int QA, bool X>
+__global__ __launch_bounds__(kThreads, QA < 128 || X ? 4 : 1) void sweep_kernel(const GemvDesc *__restrict__ descs,
                                                          const WorkItem *__restrict__ items)
 {
+    constexpr int kChunkValues = kChunkBlocks * (FMT == BQ_Q1_0 ? 128 : 64);
     __shared__ float T[kTableFloats];
     __shared__ float D1[kScaleFloats];
+    __shared__ __attribute__((aligned(16))) int8_t Qs[X ? kChunkValues : 16];
+    __shared__ float Ds[X ? kChunkValues / QA : 1];
     const WorkItem it = items[blockIdx.x];
     const GemvDesc g = descs[it.gemv];
-    run_item<FMT, QA>(g, it.tile0, it.ntiles, T, D1);
+    run_item<FMT, QA, X>(g, it.tile0, it.ntiles, T, D1, Qs, Ds);
 }
 
 template <int FMT>
@@ -383,23 +429,26 @@ hipError_t launch_rows(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
                           : rows_fmt<BQ_Q2_0>(qa, g, ld_q, ld_d, tiles, ncols, st);
 }
 
-template <int FMT>
+template <int FMT, bool X>
 static hipError_t sweep_fmt(int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items, hipStream_t st)
 {
     const dim3 grid(nitems);
     switch (qa) {
-    case 32: hipLaunchKernelGGL((sweep_kernel<FMT, 32>), grid, dim3(kThreads), 0, st, descs, items); break;
-    case 64: hipLaunchKernelGGL((sweep_kernel<FMT, 64>), grid, dim3(kThreads), 0, st, descs, items); break;
-    default: hipLaunchKernelGGL((sweep_kernel<FMT, 128>), grid, dim3(kThreads), 0, st, descs, items); break;
+    case 32: hipLaunchKernelGGL((sweep_kernel<FMT, 32, X>), grid, dim3(kThreads), 0, st, descs, items); break;
+    case 64: hipLaunchKernelGGL((sweep_kernel<FMT, 64, X>), grid, dim3(kThreads), 0, st, descs, items); break;
+    default: hipLaunchKernelGGL((sweep_kernel<FMT, 128, X>), grid, dim3(kThreads), 0, st, descs, items); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_sweep(int fmt, int qa, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
+hipError_t launch_sweep(int fmt, int qa, bool quantize, unsigned nitems, const GemvDesc *descs, const WorkItem *items,
                         hipStream_t st)
 {
-    return fmt == BQ_Q1_0 ? sweep_fmt<BQ_Q1_0>(qa, nitems, descs, items, st)
-                          : sweep_fmt<BQ_Q2_0>(qa, nitems, descs, items, st);
+    if (quantize)
+        return fmt == BQ_Q1_0 ? sweep_fmt<BQ_Q1_0, true>(qa, nitems, descs, items, st)
+                              : sweep_fmt<BQ_Q2_0, true>(qa, nitems, descs, items, st);
+    return fmt == BQ_Q1_0 ? sweep_fmt<BQ_Q1_0, false>(qa, nitems, descs, items, st)
+                          : sweep_fmt<BQ_Q2_0, false>(qa, nitems, descs, items, st);
 }
 
 template <int FMT>

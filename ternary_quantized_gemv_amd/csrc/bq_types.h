@@ -50,6 +50,7 @@ struct GemvDesc {
     int32_t nb;  // blocks per row
     int32_t ng;  // scale groups (of 8 blocks) per row
     int32_t pad;
+    const float *x;  // f32 activation, for sweeps that quantize it in the launch (q and d unused)
 };
 
 // A work item of a sweep: tiles tile0 .. tile0 + ntiles - 1 of product gemv;

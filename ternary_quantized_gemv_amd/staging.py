@@ -5,14 +5,15 @@ copies both planes to the device once, lays the float32 activation vectors end
 to end in one device buffer (so one bq_quantize_act_q8 call quantizes them
 all: quantization works block by block and every vector length is a multiple
 of qa), and builds one bq_sweep plan.  A token is then two launches: the
-quantizer over all activations and the sweep.
+quantizer over all activations and the sweep -- or one, sweep_fused(), whose
+plan (bq_sweep_create_x) quantizes the f32 vectors inside the launch.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from . import (Act, GroupCall, Weights, bq_quantize_act_q8, bq_quantize_act_q8_f16, bq_sweep_create,
-               bq_token_sweep, BLOCK_LEN)
+               bq_sweep_create_x, bq_token_sweep, BLOCK_LEN)
 
 
 class StagedSweep:
@@ -56,6 +57,7 @@ class StagedSweep:
             a = Act(self.q[k0:k1], self.d[k0 // qa:k1 // qa], cols, qa, 1)
             self.entries.append((self.weights[i], a, self.y[int(self.yoff[i]):int(self.yoff[i + 1])]))
         self.plan = bq_sweep_create(self.entries)
+        self.plan_x = None
 
     # ------------------------------------------------------------- running
     def quantize(self, stream=None):
@@ -68,11 +70,26 @@ class StagedSweep:
         self.quantize(stream)
         self.sweep(stream)
 
+    def sweep_fused(self, stream=None):
+        """The token in one launch from the f32 activations (f32 scales only):
+        the same bits in y as run()."""
+        if self.f16_scale:
+            raise ValueError("the in-launch quantizer writes f32 scales (the q8_0 flavour needs run())")
+        if self.plan_x is None:
+            ents = [(w, self.xd[int(self.koff[i]):int(self.koff[i + 1])], y) for i, (w, _, y) in enumerate(self.entries)]
+            self.plan_x = bq_sweep_create_x(ents, self.qa)
+        bq_token_sweep(self.plan_x, stream)
+
     # ----------------------------------------------------------- accounting
     def sweep_bytes(self) -> int:
         """Algorithmic bytes of one sweep launch: packed weights (18 bytes a
         block) + int8 quants + f32 activation scales read, f32 outputs written."""
         return self.weight_bytes + self.ktotal + 4 * (self.ktotal // self.qa) + 4 * self.rows_total
+
+    def fused_bytes(self) -> int:
+        """Algorithmic bytes of one sweep_fused launch: packed weights + the
+        f32 activations read, f32 outputs written."""
+        return self.weight_bytes + 4 * self.ktotal + 4 * self.rows_total
 
     def quantize_bytes(self) -> int:
         """Algorithmic bytes of the quantizer launch: f32 in, int8 + f32 scales out."""
@@ -83,6 +100,8 @@ class StagedSweep:
 
     def close(self):
         self.plan.destroy()
+        if self.plan_x is not None:
+            self.plan_x.destroy()
 
 
 # ------------------------------------------------------------------ chain

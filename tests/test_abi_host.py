@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 4
+    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 5
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
@@ -158,6 +158,33 @@ def test_group_validates_before_launch():
     assert lib.bq_group_matvec(w, 4, x, 128, y, None) == bq.BQ_EALIGN
     w[0].fmt = 3
     assert lib.bq_group_matvec(w, 1, x, 128, y, None) == bq.BQ_EARG
+
+
+def test_sweep_create_x_validates_before_launch():
+    """bq_sweep_create_x refuses bad entries on the host (no GPU is touched)."""
+    lib = bq.lib
+    plan = ctypes.c_void_p()
+    arr = (bq.bq_gemv_x * 2)()
+    for i in range(2):
+        arr[i].w = bq.bq_weights(1, 0, 64, 256, 0x1000 * (i + 1), 0x9000)
+        arr[i].x, arr[i].y = 0x40000 + 0x1000 * i, 0x60000 + 0x1000 * i
+    assert lib.bq_sweep_create_x(arr, 2, 128, None) == bq.BQ_EARG
+    assert lib.bq_sweep_create_x(None, 1, 128, ctypes.byref(plan)) == bq.BQ_EARG and not plan.value
+    assert lib.bq_sweep_create_x(arr, 0, 128, ctypes.byref(plan)) == bq.BQ_EARG
+    assert lib.bq_sweep_create_x(arr, 2, 96, ctypes.byref(plan)) == bq.BQ_EARG and "qa" in bq.bq_last_error()
+    arr[1].w.fmt = 2
+    assert lib.bq_sweep_create_x(arr, 2, 128, ctypes.byref(plan)) == bq.BQ_EARG and "entry 1" in bq.bq_last_error()
+    arr[0].w.fmt, arr[1].w.cols = 2, 192  # Q2_0 rows of three 64-weight blocks: not a multiple of qa 128
+    assert lib.bq_sweep_create_x(arr, 2, 128, ctypes.byref(plan)) == bq.BQ_EARG and "qa" in bq.bq_last_error()
+    arr[0].w.fmt = arr[1].w.fmt = 1
+    arr[1].w.cols = 256
+    arr[1].x = 0
+    assert lib.bq_sweep_create_x(arr, 2, 128, ctypes.byref(plan)) == bq.BQ_EARG
+    arr[1].x = 0x41004
+    assert lib.bq_sweep_create_x(arr, 2, 128, ctypes.byref(plan)) == bq.BQ_EALIGN
+    arr[1].x, arr[1].y = 0x41000, 0x61002
+    assert lib.bq_sweep_create_x(arr, 2, 128, ctypes.byref(plan)) == bq.BQ_EALIGN
+    assert "bq_sweep_create_x" in bq.bq_last_error() and not plan.value
 
 
 def test_read_floor_validates_before_launch():
