@@ -1,7 +1,8 @@
 // bq_sweep.hip -- the single-column kernels: one row per lane
 // (matvec_kernel, one grid row per activation column), four wavefronts per
 // 64-row tile (split_kernel, for matrices with few tiles), and the sweep of
-// many products in one launch (sweep_kernel, one row per lane).
+// many products in one launch (sweep_kernel, one row per lane; its X form
+// quantizes f32 activations chunk by chunk into LDS before each table build).
 //
 // How the work maps onto CDNA4
 // ----------------------------
