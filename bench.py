@@ -351,6 +351,7 @@ def main():
                     help="sweep activations: qa 128 with f32 scales, or qa 32 with f16-valued scales")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache sweep timing")
     ap.add_argument("--no-chain", action="store_true", help="skip the decode-chain context field")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
@@ -416,6 +417,24 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = sw.sweep_bytes() / (sweep_ms * 1e-3) / 1e9
     y_gpu = sw.y.cpu().numpy()
+    # the same sweep with the 256 MB last-level cache flushed before each launch
+    # (a streaming read of 512 MB between launches, outside the events; a read
+    # leaves no dirty lines to write back during the sweep): cold-cache time
+    cold_ms = None
+    if not args.no_cold:
+        scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+        sink = torch.empty(bq.BQ_FLOOR_SINK_WORDS, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for b, c in cev:
+            bq.bq_read_floor(scratch, sink)
+            b.record(stream)
+            sw.sweep()
+            c.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = float(np.mean([b.elapsed_time(c) for b, c in cev]))
+        del scratch, sink
+        log(f"sweep after a 512 MB cache flush: {cold_ms * 1e3:.1f} us (back to back {sweep_ms * 1e3:.1f} us)")
 
     # context, not the headline: the same token in ONE launch that quantizes
     # the f32 activations itself (bq_sweep_create_x), checked against the
@@ -502,6 +521,7 @@ def main():
             "sweep_ms": round(sweep_ms, 5),
             "sweep_ms_min": round(float(sweep_ms_all.min()), 5),
             "quantize_with_gaps_ms": round(quant_ms, 5),
+            "sweep_ms_cold_cache": None if cold_ms is None else round(cold_ms, 5),
         },
         "roofline": {
             "bound": "hbm",
