@@ -422,46 +422,52 @@ def main():
     # leaves no dirty lines to write back during the sweep): cold-cache time
     cold_ms = None
     if not args.no_cold:
-        scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
-        sink = torch.empty(bq.BQ_FLOOR_SINK_WORDS, dtype=torch.int32, device="cuda")
-        torch.cuda.synchronize()
-        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-        for b, c in cev:
-            bq.bq_read_floor(scratch, sink)
-            b.record(stream)
-            sw.sweep()
-            c.record(stream)
-        torch.cuda.synchronize()
-        cold_ms = float(np.mean([b.elapsed_time(c) for b, c in cev]))
-        del scratch, sink
-        log(f"sweep after a 512 MB cache flush: {cold_ms * 1e3:.1f} us (back to back {sweep_ms * 1e3:.1f} us)")
+        try:
+            scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+            sink = torch.empty(bq.BQ_FLOOR_SINK_WORDS, dtype=torch.int32, device="cuda")
+            torch.cuda.synchronize()
+            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for b, c in cev:
+                bq.bq_read_floor(scratch, sink)
+                b.record(stream)
+                sw.sweep()
+                c.record(stream)
+            torch.cuda.synchronize()
+            cold_ms = float(np.mean([b.elapsed_time(c) for b, c in cev]))
+            del scratch, sink
+            log(f"sweep after a 512 MB cache flush: {cold_ms * 1e3:.1f} us (back to back {sweep_ms * 1e3:.1f} us)")
+        except Exception as e:  # context only; the headline line must print regardless
+            log(f"cold-cache timing skipped: {type(e).__name__}: {e}")
 
     # context, not the headline: the same token in ONE launch that quantizes
     # the f32 activations itself (bq_sweep_create_x), checked against the
     # two-launch outputs bit for bit
     fused = None
     if not q8_0:
-        sw.y.fill_(float("nan"))
-        for _ in range(args.warmup):
-            sw.sweep_fused()
-        torch.cuda.synchronize()
-        same = bool(np.array_equal(sw.y.cpu().numpy().view(np.uint32), y_gpu.view(np.uint32)))
-        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for b, c in fev:
-            b.record(stream)
-            sw.sweep_fused()
-            c.record(stream)
-        torch.cuda.synchronize()
-        f_ms = (time.perf_counter() - t0) * 1e3 / K
-        f_kernel = float(np.mean([b.elapsed_time(c) for b, c in fev]))
-        fused = {"ms_per_step": round(f_ms, 5), "value": round(sw.fused_bytes() / (f_ms * 1e-3) / 1e9, 2),
-                 "kernel_ms": round(f_kernel, 5), "bytes_per_launch": sw.fused_bytes(),
-                 "kernel_GB_s": round(sw.fused_bytes() / (f_kernel * 1e-3) / 1e9, 2),
-                 "same_bits_as_two_launch": same,
-                 "how": "one bq_token_sweep launch of a bq_sweep_create_x plan (f32 activations quantized in the launch)"}
-        log(f"one-launch token: {f_ms * 1e3:.1f} us per step, kernel {f_kernel * 1e3:.1f} us, same bits: {same}")
+        try:
+            sw.y.fill_(float("nan"))
+            for _ in range(args.warmup):
+                sw.sweep_fused()
+            torch.cuda.synchronize()
+            same = bool(np.array_equal(sw.y.cpu().numpy().view(np.uint32), y_gpu.view(np.uint32)))
+            fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for b, c in fev:
+                b.record(stream)
+                sw.sweep_fused()
+                c.record(stream)
+            torch.cuda.synchronize()
+            f_ms = (time.perf_counter() - t0) * 1e3 / K
+            f_kernel = float(np.mean([b.elapsed_time(c) for b, c in fev]))
+            fused = {"ms_per_step": round(f_ms, 5), "value": round(sw.fused_bytes() / (f_ms * 1e-3) / 1e9, 2),
+                     "kernel_ms": round(f_kernel, 5), "bytes_per_launch": sw.fused_bytes(),
+                     "kernel_GB_s": round(sw.fused_bytes() / (f_kernel * 1e-3) / 1e9, 2),
+                     "same_bits_as_two_launch": same,
+                     "how": "one bq_token_sweep launch of a bq_sweep_create_x plan (f32 activations quantized in the launch)"}
+            log(f"one-launch token: {f_ms * 1e3:.1f} us per step, kernel {f_kernel * 1e3:.1f} us, same bits: {same}")
+        except Exception as e:  # the headline line must print regardless
+            fused = {"error": f"{type(e).__name__}: {e}"}
 
 
     if args.copy_calibration:
