@@ -258,7 +258,7 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
 
 // The work items of a plan over the products descs (validated), balanced
 // over the GPU, and the plan that owns their device copy.
-static int make_plan(const char *fn, std::vector<GemvDesc> &descs, int fmt, int qa, bool quantize, bq_sweep **plan)
+static int make_plan(const char *fn, const std::vector<GemvDesc> &descs, int fmt, int qa, bool quantize, bq_sweep **plan)
 {
     std::vector<WorkItem> items;
     for (size_t i = 0; i < descs.size(); ++i) {
