@@ -110,6 +110,19 @@ def q2_0_blocks(rows: int, cols: int, seed: int, *stream: int, sigma: float = 0.
     return _assemble(sc, payload, rows, nb)
 
 
+def q2_0_blocks_all_codes(rows: int, cols: int, seed: int, *stream: int, sigma: float = 0.02) -> np.ndarray:
+    """Canonical Q2_0 weights whose payload bytes are uniform over all 256
+    values, so the unused code 3 appears with probability 1/4 (a test regime
+    for its defined decoding, not a workload): uint8 [rows, cols/64, 18]."""
+    if cols % 64:
+        raise ValueError("Q2_0 needs cols % 64 == 0")
+    nb = cols // 64
+    g = rng(seed, 7, *stream)
+    sc = scales_f16(g, rows * nb, sigma)
+    payload = g.integers(0, 256, size=rows * nb * 16, dtype=np.uint8)
+    return _assemble(sc, payload, rows, nb)
+
+
 def blocks(fmt: int, rows: int, cols: int, seed: int, *stream: int, **kw) -> np.ndarray:
     return (q1_0_blocks if fmt == Q1_0 else q2_0_blocks)(rows, cols, seed, *stream, **kw)
 

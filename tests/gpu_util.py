@@ -13,6 +13,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def assert_parity(y_gpu, y_ref, what):
+    """The parity bar: every element bit-identical (float32 bit patterns,
+    so -0 differs from +0 and a NaN differs from every number).  The scaled
+    error max|gpu - oracle| / max|oracle| is logged beside it."""
+    y_gpu = np.asarray(y_gpu, np.float32)
+    y_ref = np.asarray(y_ref, np.float32)
+    assert y_gpu.shape == y_ref.shape, (what, y_gpu.shape, y_ref.shape)
+    bad = np.flatnonzero(y_gpu.view(np.uint32) != y_ref.view(np.uint32))
+    scale = float(np.max(np.abs(y_ref))) if y_ref.size else 0.0
+    scale = scale or 1.0
+    err = float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref))) / scale if y_ref.size else 0.0
+    log(f"{what}: {y_ref.size} outputs, {bad.size} differ, scaled error {err:.3g}")
+    assert bad.size == 0, (what, bad[:8], y_gpu.ravel()[bad[:4]], y_ref.ravel()[bad[:4]])
+
+
 def torch():
     import torch as t
     return t

@@ -179,9 +179,9 @@ def check_quantizer_scaling(o, seed: int = 8):
 
 
 # ------------------------------------------------------ exact special cases
-def _pow2_inputs(fmt, rows, cols, qa, seed):
+def _pow2_inputs(fmt, rows, cols, qa, seed, all_codes=False):
     g = synth.rng(seed, 9)
-    w = synth.blocks(fmt, rows, cols, seed, 10)
+    w = synth.q2_0_blocks_all_codes(rows, cols, seed, 10) if all_codes else synth.blocks(fmt, rows, cols, seed, 10)
     nb = cols // QK[fmt]
     e0 = g.integers(-1, 3, size=(rows, nb))
     w[:, :, 0:2] = np.exp2(e0).astype(np.float16).view(np.uint16).astype("<u2").view(np.uint8).reshape(rows, nb, 2)
@@ -213,8 +213,16 @@ def _exact_sum(fmt, w, q, d, qa, e0):
     return [math.fsum((prods[r] * scale[r]).tolist()) for r in range(rows)]
 
 
-def check_exact(o, fmt, rows=64, cols=512, qa=32, seed=11):
-    w, q, d, e0 = _pow2_inputs(fmt, rows, cols, qa, seed)
+def check_exact(o, fmt, rows=64, cols=512, qa=32, seed=11, all_codes=False):
+    """Power-of-two scales make every step exact, so y is the integer dot
+    product decoded another way (numpy.unpackbits / base-4 digits).  With
+    all_codes (Q2_0) a quarter of the codes are the unused code 3, which must
+    decode as c - 1 = +2 like the others."""
+    w, q, d, e0 = _pow2_inputs(fmt, rows, cols, qa, seed, all_codes)
+    if all_codes:
+        by = w[:, :, 2:]
+        n3 = sum(int(np.count_nonzero(((by >> (2 * i)) & 3) == 3)) for i in range(4))
+        assert n3 > rows * cols // 8, n3
     y = o.matvec(fmt, w, rows, cols, q, d, qa)[0]
     exact = _exact_sum(fmt, w, q, d, qa, e0)
     assert all(abs(v) < 2.0**20 for v in exact)
@@ -403,6 +411,7 @@ ALL_CHECKS = [
     ("exact_q1", lambda o: check_exact(o, Q1_0)),
     ("exact_q2", lambda o: check_exact(o, Q2_0)),
     ("exact_q1_qa128", lambda o: check_exact(o, Q1_0, rows=64, cols=128, qa=128)),
+    ("exact_q2_code3", lambda o: check_exact(o, Q2_0, rows=64, cols=512, qa=64, seed=19, all_codes=True)),
     ("bound_q1", lambda o: check_bound(o, Q1_0)),
     ("bound_q2", lambda o: check_bound(o, Q2_0)),
     ("bound_q1_layer", lambda o: check_bound(o, Q1_0, layer=True, qa=32)),

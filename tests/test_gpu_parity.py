@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import SweepWorkload, log, matvec_gpu, quantize_gpu, torch
+from gpu_util import SweepWorkload, assert_parity, log, matvec_gpu, quantize_gpu, torch
 from pins import load_witnesses, same_bits
 
 pytestmark = pytest.mark.gpu
@@ -27,17 +27,6 @@ def _gpu():
         pytest.fail("no GPU visible: the gpu tests need an MI355X")
     import ternary_quantized_gemv_amd  # noqa: F401  (fails loudly if libbq.so is missing)
     yield
-
-
-def assert_parity(y_gpu, y_ref, what):
-    y_gpu = np.asarray(y_gpu, np.float32)
-    y_ref = np.asarray(y_ref, np.float32)
-    assert y_gpu.shape == y_ref.shape
-    bad = np.flatnonzero(y_gpu.view(np.uint32) != y_ref.view(np.uint32))
-    scale = float(np.max(np.abs(y_ref))) or 1.0
-    err = float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref))) / scale if y_ref.size else 0.0
-    log(f"{what}: {y_ref.size} outputs, {bad.size} differ, scaled error {err:.3g}")
-    assert bad.size == 0, (what, bad[:8], y_gpu.ravel()[bad[:4]], y_ref.ravel()[bad[:4]])
 
 
 # --------------------------------------------------------------- witnesses
@@ -243,6 +232,62 @@ def test_small_batch_full_size(fmt, rows):
         assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
 
 
+# -------------------------------------- Q2_0 code 3: its defined decoding
+# Code 3 never occurs in ternary weights; the layout contract decodes it as
+# c - 1 = +2 on both sides.  Payload bytes uniform over all 256 values (a
+# quarter of the codes are 3), through every kernel path.
+CODE3 = [
+    (1024, 4096, 1, 128),    # 16 tiles: wide kernel, quarter tiles
+    (2000, 2048, 3, 64),     # 96 tiles over three columns: half tiles, one grid row per column
+    (44800, 1024, 1, 128),   # 700 tiles: four wavefronts per tile
+    (131201, 1024, 1, 32),   # 2051 tiles: one row per lane
+    (65600, 320, 5, 64),     # tall, five columns: interleaved four-column tables
+]
+
+
+@pytest.mark.parametrize("rows,cols,ncols,qa", CODE3, ids=[f"{r}x{c}-n{n}-qa{a}" for r, c, n, a in CODE3])
+def test_q2_code3_parity(rows, cols, ncols, qa):
+    name = f"Q2_0 code 3 {rows}x{cols} N={ncols} qa={qa}"
+    log(name)
+    w = synth.q2_0_blocks_all_codes(rows, cols, 91, rows, ncols)
+    qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 91, c), qa)[:2] for c in range(ncols)])
+    q, d = np.stack(qs), np.stack(ds)
+    y_ref = oracle.matvec(Q2, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(Q2, w, rows, cols, q, d, qa), y_ref, name)
+
+
+def test_q2_code3_sweeps_and_group():
+    """Code 3 through the token sweep (two launches and one launch) and a
+    fused decode group."""
+    import ternary_quantized_gemv_amd as bq
+    from ternary_quantized_gemv_amd.staging import StagedSweep
+    t = torch()
+    shapes = [("a", 100, 33 * 64), ("b", 700, 4096), ("c", 130, 96 * 64), ("d", 64, 64)]
+    canon = [synth.q2_0_blocks_all_codes(r, c, 92, i) for i, (_, r, c) in enumerate(shapes)]
+    x = [synth.activation(c, 92, 100 + i) for i, (_, _, c) in enumerate(shapes)]
+    sw = StagedSweep(Q2, canon, shapes, x, 64)
+    try:
+        q_ref, d_ref, _ = oracle.quantize_q8(sw.x, 64)
+        refs = []
+        for i, (_, rows, cols) in enumerate(shapes):
+            k0, k1 = int(sw.koff[i]), int(sw.koff[i + 1])
+            refs.append(oracle.matvec(Q2, canon[i], rows, cols, q_ref[k0:k1], d_ref[k0 // 64:k1 // 64], 64,
+                                      threads=THREADS)[0])
+        for how in ("two launches", "one launch"):
+            sw.y.fill_(float("nan"))
+            sw.run() if how == "two launches" else sw.sweep_fused()
+            t.cuda.synchronize()
+            y = sw.y.cpu().numpy()
+            for i, (nm, _, _) in enumerate(shapes):
+                assert_parity(y[int(sw.yoff[i]):int(sw.yoff[i + 1])], refs[i], f"code 3 sweep, {how}, {nm}")
+        ys = [t.empty(shapes[i][1], dtype=t.float32, device="cuda") for i in (1,)]
+        bq.bq_group_matvec([sw.weights[1]], sw.xd[int(sw.koff[1]):int(sw.koff[2])], 64, ys)
+        t.cuda.synchronize()
+        assert_parity(ys[0].cpu().numpy(), refs[1], "code 3 decode group")
+    finally:
+        sw.close()
+
+
 # ------------------------------------------------------------ token sweeps
 def _check_sweep(fmt, shapes, seed, qa=128, f16_scale=False):
     t = torch()
@@ -302,3 +347,41 @@ def test_gpu_errors_are_reported():
     with pytest.raises(bq.BQError) as e:
         bq.bq_quantize_act_q8(x, 48, t.zeros(256, dtype=t.int8, device="cuda"), t.zeros(8, device="cuda"))
     assert e.value.code == bq.BQ_EARG and "bq_quantize_act_q8" in str(e.value)
+
+
+def test_binding_refuses_short_or_wrong_tensors():
+    """The binding checks every tensor it turns into a pointer (device, dtype,
+    contiguity, enough elements) and raises BQError before any launch, so a
+    short output cannot become an out-of-bounds write on the GPU."""
+    import ternary_quantized_gemv_amd as bq
+    t = torch()
+    rows, cols = 256, 4096
+    w = bq.Weights.upload(Q1, synth.blocks(Q1, rows, cols, 3), rows, cols)
+    q = t.zeros(cols, dtype=t.int8, device="cuda")
+    d = t.ones(cols // 128, dtype=t.float32, device="cuda")
+    a = bq.Act(q, d, cols, 128, 1)
+    x = t.zeros(cols, dtype=t.float32, device="cuda")
+    sentinel = t.full((rows + 64,), 7.0, dtype=t.float32, device="cuda")
+    bad_calls = [
+        ("short y", lambda: bq.bq_q1_0_matvec(w, a, sentinel[:rows - 1])),
+        ("f64 y", lambda: bq.bq_q1_0_matvec(w, a, t.zeros(rows, dtype=t.float64, device="cuda"))),
+        ("host y", lambda: bq.bq_q1_0_matvec(w, a, t.zeros(rows))),
+        ("strided y", lambda: bq.bq_q1_0_matvec(w, a, sentinel[::2])),
+        ("short q", lambda: bq.Act(q[:cols - 16], d, cols, 128, 1)),
+        ("f32 q", lambda: bq.Act(x, d, cols, 128, 1)),
+        ("short d", lambda: bq.Act(q, d[:-1], cols, 128, 1)),
+        ("two columns of one", lambda: bq.Act(q, d, cols, 128, 2)),
+        ("quantizer short q", lambda: bq.bq_quantize_act_q8(x, 128, q[:100], d)),
+        ("quantizer short d", lambda: bq.bq_quantize_act_q8(x, 128, q, d[:3])),
+        ("quantizer int x", lambda: bq.bq_quantize_act_q8(q, 128, q, d)),
+        ("short weights", lambda: bq.Weights(Q1, rows, cols, w.bits[:-16], w.scales)),
+        ("group short y", lambda: bq.bq_group_matvec([w], x, 128, [sentinel[:10]])),
+        ("sweep short y", lambda: bq.bq_sweep_create([(w, a, sentinel[:rows - 1])])),
+        ("sweep_x short x", lambda: bq.bq_sweep_create_x([(w, x[:cols - 4], sentinel[:rows])], 128)),
+    ]
+    for what, call in bad_calls:
+        with pytest.raises(bq.BQError):
+            call()
+        log(f"refused: {what}")
+    t.cuda.synchronize()
+    assert bool((sentinel == 7.0).all()), "a refused call wrote to the output"

@@ -3,7 +3,8 @@
 oracle's quantize-then-product on small mixes (ragged rows, partial and
 several table chunks, an all-zero activation block and exact ties, every qa,
 both formats), and on the full decode token the two-launch path
-(quantizer + bq_token_sweep) bit for bit."""
+(quantizer + bq_token_sweep) bit for bit -- and, on the full decode token
+of both formats, the oracle on every output and the two-launch path."""
 import numpy as np
 import pytest
 
@@ -67,25 +68,37 @@ def test_fused_sweep_against_oracle(fmt, qa, special):
 
 @pytest.mark.parametrize("fmt", [Q1, Q2])
 def test_fused_sweep_decode_token(fmt):
-    """All 253 products of the decode token: one fused launch == quantizer + sweep."""
+    """All 253 products of the decode token in one fused launch: every output
+    equals the oracle's quantize-then-product, and the two-launch path
+    (quantizer + bq_token_sweep) gives the same bits."""
     from ternary_quantized_gemv_amd.staging import StagedSweep
     t = torch()
     shapes = synth.decode_sweep_shapes()
     log(f"fused sweep decode token fmt={fmt}: staging")
     canon = [synth.blocks(fmt, r, c, 80 + fmt, i) for i, (_, r, c) in enumerate(shapes)]
     x = [synth.activation(c, 80 + fmt, 1000 + i) for i, (_, _, c) in enumerate(shapes)]
-    sw = StagedSweep(fmt, canon, shapes, x, 128, keep_host=False)
-    del canon
+    sw = StagedSweep(fmt, canon, shapes, x, 128)
     try:
-        sw.run()
-        t.cuda.synchronize()
-        y_two = sw.y.cpu().numpy()
-        sw.y.fill_(float("nan"))
         sw.sweep_fused()
         t.cuda.synchronize()
         y_one = sw.y.cpu().numpy()
-        log(f"fused sweep decode token fmt={fmt}: {sw.rows_total} outputs compared")
-        assert same_bits(y_one, y_two)
+        log(f"fused sweep decode token fmt={fmt}: oracle over {sw.rows_total} outputs")
+        q_ref, d_ref, _ = oracle.quantize_q8(sw.x, 128)
+        bad = 0
+        for i, (name, rows, cols) in enumerate(sw.shapes):
+            k0, k1 = int(sw.koff[i]), int(sw.koff[i + 1])
+            ref = oracle.matvec(fmt, canon[i], rows, cols, q_ref[k0:k1], d_ref[k0 // 128:k1 // 128], 128,
+                                threads=THREADS)[0]
+            got = y_one[int(sw.yoff[i]):int(sw.yoff[i + 1])]
+            nbad = int(np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32)))
+            if nbad:
+                log(f"  {name}: {nbad} of {rows} outputs differ from the oracle")
+            bad += nbad
+        assert bad == 0, f"{bad} outputs of the one-launch token differ from the oracle"
+        sw.y.fill_(float("nan"))
+        sw.run()
+        t.cuda.synchronize()
+        assert same_bits(sw.y.cpu().numpy(), y_one)
     finally:
         sw.close()
 

@@ -29,6 +29,8 @@ MUTANTS = [
     ("last_block_dropped", "for (int64_t b = 0; b < nb; ++b) {", "for (int64_t b = 0; b + 1 < nb; ++b) {"),
     ("q2_code_map_reversed", "s += (code - 1) * (int32_t)q[e0 + 4 * L + i];", "s += (1 - code) * (int32_t)q[e0 + 4 * L + i];"),
     ("q2_code_offset_wrong", "s += (code - 1) * (int32_t)q[e0 + 4 * L + i];", "s += code * (int32_t)q[e0 + 4 * L + i];"),
+    ("q2_code3_decoded_as_zero", "s += (code - 1) * (int32_t)q[e0 + 4 * L + i];",
+     "s += (code == 3 ? 0 : code - 1) * (int32_t)q[e0 + 4 * L + i];"),
     ("q2_code_shift_wrong", "int code = (qs[k >> 2] >> (2 * (k & 3))) & 3;", "int code = (qs[k >> 2] >> (k & 3)) & 3;"),
     ("quant_round_half_even", "float r = roundf(xb[i] / db);", "float r = rintf(xb[i] / db);"),
     ("quant_divisor_128", "float db = amax / 127.0f;", "float db = amax / 128.0f;"),
