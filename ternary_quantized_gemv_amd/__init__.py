@@ -136,6 +136,21 @@ def _dev(t, what: str) -> int:
     return t.data_ptr()
 
 
+def _need(t, what: str, dtype, numel: int, fn: str) -> None:
+    """Refuses (BQError, before anything is launched) a tensor that is not on
+    a ROCm device, not of dtype, not contiguous, or holds fewer than numel
+    elements: the library takes bare pointers and would read or write past
+    its end."""
+    if t is None or not getattr(t, "is_cuda", False):
+        raise BQError(BQ_EARG, f"{fn}: {what} must be a tensor on a ROCm device")
+    if t.dtype != dtype:
+        raise BQError(BQ_EARG, f"{fn}: {what} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise BQError(BQ_EARG, f"{fn}: {what} must be contiguous")
+    if t.numel() < numel:
+        raise BQError(BQ_EARG, f"{fn}: {what} holds {t.numel()} elements, needs {numel}")
+
+
 def _stream(stream) -> int:
     if stream is None:
         import torch
@@ -182,15 +197,24 @@ def bq_unpack(fmt: int, bits: np.ndarray, scales: np.ndarray, rows: int, cols: i
 
 
 # ------------------------------------------------------------------ GPU calls
+def _quantize_args(fn: str, x, qa: int, q, d) -> int:
+    import torch
+    _need(x, "x", torch.float32, 0, fn)
+    n = x.numel()
+    _need(q, "q", torch.int8, n, fn)
+    _need(d, "d", torch.float32, n // qa if qa > 0 else 0, fn)
+    return n
+
+
 def bq_quantize_act_q8(x, qa: int, q, d, stream=None) -> None:
     """x: float32 device tensor (n); q: int8 device tensor (n); d: float32 device tensor (n/qa)."""
-    n = x.numel()
+    n = _quantize_args("bq_quantize_act_q8", x, qa, q, d)
     _check(lib.bq_quantize_act_q8(_dev(x, "x"), n, qa, _dev(q, "q"), _dev(d, "d"), _stream(stream)))
 
 
 def bq_quantize_act_q8_f16(x, qa: int, q, d, stream=None) -> None:
     """As bq_quantize_act_q8, with the scales narrowed to f16 values."""
-    n = x.numel()
+    n = _quantize_args("bq_quantize_act_q8_f16", x, qa, q, d)
     _check(lib.bq_quantize_act_q8_f16(_dev(x, "x"), n, qa, _dev(q, "q"), _dev(d, "d"), _stream(stream)))
 
 
@@ -208,6 +232,10 @@ class Weights:
     """A packed matrix resident on the GPU (the two planes of bq_pack)."""
 
     def __init__(self, fmt: int, rows: int, cols: int, bits, scales):
+        import torch
+        nb, ns = bq_packed_bytes(fmt, rows, cols)
+        _need(bits, "weights.bits", torch.uint8, nb, "Weights")
+        _need(scales, "weights.scales", torch.int16, ns // 2, "Weights")
         self.fmt, self.rows, self.cols = fmt, rows, cols
         self.bits, self.scales = bits, scales
 
@@ -227,15 +255,33 @@ class Act:
     """ncols quantized activation columns on the GPU: q int8 [ncols, ld_q], d f32 [ncols, ld_d]."""
 
     def __init__(self, q, d, n: int, qa: int, ncols: int = 1):
+        import torch
+        for t, what, dt in ((q, "act.q", torch.int8), (d, "act.d", torch.float32)):
+            if not getattr(t, "is_cuda", False) or t.dtype != dt:
+                raise BQError(BQ_EARG, f"Act: {what} must be a {dt} tensor on a ROCm device")
+            if t.dim() not in (1, 2) or t.stride(-1) != 1 or (t.dim() == 2 and t.shape[0] < ncols):
+                raise BQError(BQ_EARG, f"Act: {what} must be 1-D, or 2-D [>= ncols, ...] with unit stride")
         self.q, self.d, self.n, self.qa, self.ncols = q, d, n, qa, ncols
+        # the library reads column c at q + c ld_q (n values) and d + c ld_d (n / qa values)
+        ld_q, ld_d = self._ld()
+        for t, ld, need, what in ((q, ld_q, n, "act.q"), (d, ld_d, n // qa if qa > 0 else 0, "act.d")):
+            short = t.shape[1] < need if t.dim() == 2 else t.numel() < (ncols - 1) * ld + need
+            if short:
+                raise BQError(BQ_EARG, f"Act: {what} holds fewer values than {ncols} column(s) of {need} need")
+
+    def _ld(self):
+        ld_q = self.q.stride(0) if self.q.dim() == 2 else self.n
+        ld_d = self.d.stride(0) if self.d.dim() == 2 else (self.n // self.qa if self.qa > 0 else 0)
+        return ld_q, ld_d
 
     def c(self) -> bq_act:
-        ld_q = self.q.stride(0) if self.q.dim() == 2 else self.n
-        ld_d = self.d.stride(0) if self.d.dim() == 2 else self.n // self.qa
+        ld_q, ld_d = self._ld()
         return bq_act(_dev(self.q, "act.q"), _dev(self.d, "act.d"), self.n, self.qa, self.ncols, ld_q, ld_d)
 
 
 def _matvec(fn, w: Weights, a: Act, y, stream):
+    import torch
+    _need(y, "y", torch.float32, a.ncols * w.rows, fn.__name__)
     wc, ac = w.c(), a.c()
     _check(fn(ctypes.byref(wc), ctypes.byref(ac), _dev(y, "y"), _stream(stream)))
 
@@ -259,8 +305,10 @@ class GroupCall:
             raise BQError(BQ_EARG, "bq_group_matvec: one output per product")
         if n and x.numel() != weights[0].cols:
             raise BQError(BQ_EARG, "bq_group_matvec: x length differs from the weights' cols")
-        if any(y.numel() < w.rows for w, y in zip(weights, ys)):
-            raise BQError(BQ_EARG, "bq_group_matvec: an output is shorter than its product's rows")
+        import torch
+        _need(x, "x", torch.float32, 0, "bq_group_matvec")
+        for w, y in zip(weights, ys):
+            _need(y, "y", torch.float32, w.rows, "bq_group_matvec")
         self.w = (bq_weights * n)(*[w.c() for w in weights])
         self.y = (ctypes.c_void_p * n)(*[_dev(y, "y") for y in ys])
         self.n, self.x, self.qa = n, _dev(x, "x"), qa
@@ -297,8 +345,10 @@ class Sweep:
 
 def bq_sweep_create(entries) -> Sweep:
     """entries: [(Weights, Act, y tensor)]."""
+    import torch
     arr = (bq_gemv * len(entries))()
     for i, (w, a, y) in enumerate(entries):
+        _need(y, f"entry {i} y", torch.float32, w.rows, "bq_sweep_create")
         arr[i].w = w.c()
         arr[i].a = a.c()
         arr[i].y = _dev(y, "y")
@@ -310,10 +360,11 @@ def bq_sweep_create(entries) -> Sweep:
 def bq_sweep_create_x(entries, qa: int) -> Sweep:
     """entries: [(Weights, x f32 tensor of length cols, y tensor)]; the launch
     quantizes each x in blocks of qa."""
+    import torch
     arr = (bq_gemv_x * len(entries))()
     for i, (w, x, y) in enumerate(entries):
-        if x.numel() != w.cols:
-            raise ValueError(f"bq_sweep_create_x: entry {i}: x has {x.numel()} values, cols is {w.cols}")
+        _need(x, f"entry {i} x", torch.float32, w.cols, "bq_sweep_create_x")
+        _need(y, f"entry {i} y", torch.float32, w.rows, "bq_sweep_create_x")
         arr[i].w = w.c()
         arr[i].x = _dev(x, "x")
         arr[i].y = _dev(y, "y")

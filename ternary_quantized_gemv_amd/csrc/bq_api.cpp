@@ -52,11 +52,14 @@ static int check_weights(const char *fn, const bq_weights *w, int fmt)
         return set_error(BQ_EARG, "%s: weights format %d, expected %d", fn, (int)w->fmt, fmt);
     if (w->reserved != 0)
         return set_error(BQ_EARG, "%s: weights.reserved must be 0", fn);
-    if (w->rows < 1 || w->rows >= (int64_t(1) << 31) || w->cols < 1 || w->cols >= (int64_t(1) << 31))
+    if (w->rows < 1 || w->rows >= kMaxDim || w->cols < 1 || w->cols >= kMaxDim)
         return set_error(BQ_EARG, "%s: rows %lld / cols %lld out of range", fn, (long long)w->rows,
                          (long long)w->cols);
     if (w->cols % block_len(fmt))
         return set_error(BQ_EARG, "%s: cols %lld not a multiple of %d", fn, (long long)w->cols, block_len(fmt));
+    if (!tile_fits(w->cols / block_len(fmt)))
+        return set_error(BQ_EARG, "%s: cols %lld: a 64-row tile's payload would exceed %lld bytes", fn,
+                         (long long)w->cols, (long long)kMaxTileBytes);
     if (!w->bits || !w->scales)
         return set_error(BQ_EARG, "%s: null weight plane", fn);
     if (!aligned(w->bits, 16) || !aligned(w->scales, 16))

@@ -15,11 +15,12 @@ typedef const float __attribute__((address_space(4))) *cfptr;
 // Weight planes are read through buffer resources: the wave-uniform base of
 // a tile sits in scalar registers, each lane adds its 16-byte offset, and the
 // block offset is a scalar constant, so a load costs no vector address math.
+// A resource spans kMaxTileBytes (the entry points refuse larger tiles).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ __forceinline__ rsrc_t rsrc_of(const u32x4 *base)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(base), (short)0, 0x7FFFFFF0, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(base), (short)0, (int)kMaxTileBytes, 0x00020000);
 }
 
 // 16 bytes at base + voff + soff, streamed (non-temporal).

@@ -30,6 +30,13 @@ constexpr int kTileRows = 64;
 constexpr int kBlockBytes = 18;
 constexpr int kPayloadBytes = 16;
 constexpr int kScalesPerGroup = 8;
+// The kernels address a 64-row tile's payload (nb * 1 KiB) and its scales
+// through one buffer resource with 32-bit offsets, so a tile's payload may
+// not exceed this many bytes (cols up to 268,435,328 for Q1_0, 134,217,664
+// for Q2_0); rows and cols stay below 2^31.
+constexpr int64_t kMaxTileBytes = 0x7FFFFFF0;
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // rows and cols must be below this
+inline bool tile_fits(int64_t nb) { return nb * kTileRows * kPayloadBytes <= kMaxTileBytes; }
 
 inline int block_len(int fmt) { return fmt == 1 ? 128 : fmt == 2 ? 64 : 0; }
 inline int64_t tiles_of(int64_t rows) { return (rows + kTileRows - 1) / kTileRows; }

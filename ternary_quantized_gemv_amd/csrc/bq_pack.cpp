@@ -36,8 +36,11 @@ static int check_shape(const char *fn, int32_t fmt, int64_t rows, int64_t cols)
     if (cols % qk)
         return set_error(BQ_EARG, "%s: cols (%lld) is not a multiple of the block length %d", fn,
                          (long long)cols, qk);
-    if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31))
+    if (rows >= kMaxDim || cols >= kMaxDim)
         return set_error(BQ_EARG, "%s: rows and cols must be below 2^31", fn);
+    if (!tile_fits(cols / qk))
+        return set_error(BQ_EARG, "%s: cols %lld: a 64-row tile's payload would exceed %lld bytes", fn,
+                         (long long)cols, (long long)kMaxTileBytes);
     return BQ_OK;
 }
 

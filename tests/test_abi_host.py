@@ -205,3 +205,40 @@ def test_host_tensors_are_refused():
     x = torch.zeros(256)
     with pytest.raises(bq.BQError):
         bq.bq_quantize_act_q8(x, 128, torch.zeros(256, dtype=torch.int8), torch.zeros(2))
+
+
+def test_size_limits():
+    """Shapes the kernels cannot address are refused before anything runs:
+    rows and cols below 2^31, and a 64-row tile's payload (nb x 1 KiB) within
+    the 2^31 - 16 bytes one buffer resource spans."""
+    lim = {bq.BQ_Q1_0: 2097151, bq.BQ_Q2_0: 2097151}  # blocks per row
+    for fmt, qk in ((bq.BQ_Q1_0, 128), (bq.BQ_Q2_0, 64)):
+        b, s = bq.bq_packed_bytes(fmt, 64, lim[fmt] * qk)
+        assert b == lim[fmt] * 1024 <= 0x7FFFFFF0
+        with pytest.raises(bq.BQError) as e:
+            bq.bq_packed_bytes(fmt, 64, (lim[fmt] + 1) * qk)
+        assert e.value.code == bq.BQ_EARG and "payload" in str(e.value)
+    bq.bq_packed_bytes(bq.BQ_Q1_0, (1 << 31) - 1, 128)
+    for rows, cols in (((1 << 31), 128), (64, 1 << 31)):
+        with pytest.raises(bq.BQError) as e:
+            bq.bq_packed_bytes(bq.BQ_Q1_0, rows, cols)
+        assert e.value.code == bq.BQ_EARG and "2^31" in str(e.value)
+
+    lib = bq.lib
+    big = (lim[bq.BQ_Q1_0] + 1) * 128
+    w = bq.bq_weights(1, 0, 64, big, 0x1000, 0x2000)
+    a = bq.bq_act(0x3000, 0x4000, big, 128, 1, big, big // 128)
+    assert lib.bq_q1_0_matvec(ctypes.byref(w), ctypes.byref(a), 0x5000, None) == bq.BQ_EARG
+    assert "payload" in bq.bq_last_error()
+    w.rows = 1 << 31
+    w.cols = 256
+    assert lib.bq_q1_0_matvec(ctypes.byref(w), ctypes.byref(a), 0x5000, None) == bq.BQ_EARG
+    w.rows, w.cols = 64, big
+    y = (ctypes.c_void_p * 1)(0x5000)
+    assert lib.bq_group_matvec(ctypes.byref(w), 1, ctypes.c_void_p(0x6000), 128, y, None) == bq.BQ_EARG
+    assert "payload" in bq.bq_last_error()
+    arr = (bq.bq_gemv * 1)()
+    arr[0].w, arr[0].a, arr[0].y = w, a, 0x5000
+    plan = ctypes.c_void_p()
+    assert lib.bq_sweep_create(arr, 1, ctypes.byref(plan)) == bq.BQ_EARG and not plan.value
+    assert "payload" in bq.bq_last_error()
