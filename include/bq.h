@@ -115,15 +115,30 @@ typedef struct bq_gemv_x {
 
 typedef struct bq_sweep bq_sweep; /* opaque plan */
 
-/* BQ_ABI_VERSION of the loaded library. */
+/* BQ_ABI_VERSION of the loaded library, so that a binding can refuse a
+ * library built for another version of this interface instead of passing it
+ * structs of another layout (bankML "gpu/ -- the video-card component",
+ * section "Advantages and efficiency": checks fail closed).  Host only. */
 int bq_abi_version(void);
 
-/* Text of the calling thread's last error ("" if none).  Valid until the
- * thread's next failing call. */
+/* Text of the calling thread's last error ("" if none): the failing call,
+ * the argument and why (bankML "gpu/ -- the video-card component", section
+ * "Advantages and efficiency": errors name the failing call; OneModel GPU
+ * docs, section "Errors": a failure names what was being done).  Owned by
+ * the library, thread-local, valid until the thread's next failing call.
+ * Host only. */
 const char *bq_last_error(void);
 
-/* Sizes in bytes of the two device planes that hold a packed rows x cols
- * matrix of format fmt.  Host only; touches no GPU. */
+/* Sizes in bytes of the two device planes that bq_pack writes for a packed
+ * rows x cols matrix of format fmt (bankML "gpu/ -- the video-card
+ * component", section "kernels.rs -- the Q1_0 kernels": weights are
+ * repacked once into the card's layout, bits as 32-bit words).  Writes
+ * *bits_bytes and *scale_bytes (host pointers) and returns BQ_OK, or BQ_EARG
+ * (unknown fmt; rows or cols not in [1, 2^31); cols not a multiple of the
+ * block length; a 64-row tile's payload above 2^31 - 16 bytes; a null output
+ * pointer) with nothing written.  The sizes come back through pointers so
+ * that the result is a return code like every other call.  Host only;
+ * touches no GPU. */
 int bq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols, size_t *bits_bytes, size_t *scale_bytes);
 
 /* Repack canonical blocks into the device layout (bankML "gpu/", section
@@ -135,16 +150,29 @@ int bq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols, size_t *bits_bytes,
 int bq_pack(int32_t fmt, const uint8_t *canon, int64_t rows, int64_t cols, void *bits_out,
             uint16_t *scales_out);
 
-/* Inverse of bq_pack (host only): recovers the canonical blocks. */
+/* Inverse of bq_pack: bits and scales (host, the planes bq_pack wrote for
+ * the same fmt, rows, cols) give back the canonical blocks in canon_out
+ * (host, rows x (cols / block length) x 18 bytes), byte for byte -- the
+ * repacking changes no number, it only re-orders them (bankML "gpu/ -- the
+ * video-card component", section "kernels.rs -- the Q1_0 kernels").
+ * Returns BQ_OK, or BQ_EARG (shape as bq_packed_bytes, null pointer).
+ * Host only. */
 int bq_unpack(int32_t fmt, const void *bits, const uint16_t *scales, int64_t rows, int64_t cols,
               uint8_t *canon_out);
 
-/* Quantize n floats x (device, 16-byte aligned) in blocks of qa values:
- * d = amax / 127 (f32, correctly rounded), q = x / d (correctly rounded)
- * rounded half away from zero into [-127, 127]; an all-zero block gives
- * d = 0 and q = 0.  q (device, 4-byte aligned) receives n int8 values and d
- * (device, 4-byte aligned) n / qa floats.  qa is 32, 64 or 128; n % qa == 0.
- * Non-finite inputs are outside the contract.  Asynchronous on s. */
+/* The activation quantizer: the int8 activation with one scale per block
+ * that the products read (bankML "gpu/ -- the video-card component",
+ * section "kernels.rs -- the Q1_0 kernels": the activation binding holds
+ * f32 scales, one per 32 values, and int8 quants, and the activation is
+ * repacked per call; here the block length qa is a parameter, 128 in the
+ * configured workloads).  Quantize n floats x (device, 16-byte aligned) in
+ * blocks of qa values: d = amax / 127 (f32, correctly rounded), q = x / d
+ * (correctly rounded) rounded half away from zero into [-127, 127]; an
+ * all-zero block gives d = 0 and q = 0.  q (device, 4-byte aligned)
+ * receives n int8 values and d (device, 4-byte aligned) n / qa floats.  qa
+ * is 32, 64 or 128; n % qa == 0 (n = 0 does nothing).  Non-finite inputs are
+ * outside the contract.  Returns BQ_EARG / BQ_EALIGN before any launch, or
+ * BQ_EHIP if the launch fails.  Allocates nothing.  Asynchronous on s. */
 int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s);
 
 /* The same quantizer with f16-valued scales, the flavour of the pages' q8_0
@@ -161,10 +189,15 @@ int bq_quantize_act_q8(const float *x, int64_t n, int32_t qa, int8_t *q, float *
  * and errors as bq_quantize_act_q8.  Asynchronous on s. */
 int bq_quantize_act_q8_f16(const float *x, int64_t n, int32_t qa, int8_t *q, float *d, bq_stream s);
 
-/* y (device, 4-byte aligned, a.ncols * w->rows floats; column c at
- * y + c * rows) = W times each activation column, in the order given at the
- * top of this file.  w->fmt must be BQ_Q1_0 (resp. BQ_Q2_0 for the second
- * call); a->n must equal w->cols.  Allocates nothing.  Asynchronous on s. */
+/* The product itself (bankML "gpu/ -- the video-card component", section
+ * "kernels.rs -- the Q1_0 kernels": one f32 dot product per row, in the
+ * order given at the top of this file; Q2_0 by the same order, readings of
+ * the format noted above).  y (device, 4-byte aligned, a.ncols * w->rows
+ * floats; column c at y + c * rows) = W times each activation column.
+ * w (host struct, device planes) must have fmt BQ_Q1_0 (resp. BQ_Q2_0 for
+ * the second call); a (host struct, device arrays) must have a->n ==
+ * w->cols.  Returns BQ_EARG / BQ_EALIGN before any launch, or BQ_EHIP if the
+ * launch fails.  Allocates nothing.  Asynchronous on s. */
 int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
 int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
 
@@ -206,11 +239,20 @@ int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **plan);
  * bq_token_sweep and bq_sweep_destroy. */
 int bq_sweep_create_x(const bq_gemv_x *list, int32_t count, int32_t qa, bq_sweep **plan);
 
-/* Enqueue the whole plan on s as one kernel launch.  Each entry's y equals
- * what bq_q1_0_matvec / bq_q2_0_matvec would write for it. */
+/* Enqueue the whole plan on s as ONE kernel launch (bankML "gpu/ -- the
+ * video-card component", section "Limitations": each of the token's 253
+ * matrix calls paid one submit and wait there; here the token is one
+ * submission).  Each entry's y equals what bq_q1_0_matvec / bq_q2_0_matvec
+ * would write for it; the plan's pointers must still be valid.  Returns
+ * BQ_EARG (null plan) or BQ_EHIP if the launch fails.  Allocates nothing.
+ * Asynchronous on s. */
 int bq_token_sweep(const bq_sweep *plan, bq_stream s);
 
-/* Release a plan (NULL is allowed).  Synchronises the device first. */
+/* Release a plan and its device table (NULL is allowed): resources are
+ * released only by an explicit call, never behind the caller's back (bankML
+ * "gpu/ -- the video-card component", section "compute.rs -- Vulkan
+ * compute": a buffer is released only by the free call).  Synchronises the
+ * device first, so launches of the plan still in flight finish. */
 void bq_sweep_destroy(bq_sweep *plan);
 
 /* The streaming-read floor, a measurement aid and not a step of the
