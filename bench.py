@@ -75,18 +75,38 @@ def measured_traffic(fmt_name: str):
     return prof.get("traffic_bytes_per_launch")
 
 
-def cpu_threads() -> int:
+def host_cpus() -> dict:
+    """What the host offers: logical CPUs, the ones this process may run on,
+    and the CPU model."""
     try:
-        n = len(os.sched_getaffinity(0))
+        aff = len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        aff = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"logical_cpus": os.cpu_count(), "affinity_cpus": aff, "model": model}
 
 
-def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
+# A GPU box gives one GPU's job a share of 16 host threads, whatever the host
+# has in all; the oracle's thread pool is sized to that share.
+BOX_THREADS = 16
+
+
+def cpu_threads() -> int:
+    return max(1, min(host_cpus()["affinity_cpus"], BOX_THREADS))
+
+
+def oracle_leg(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
     """The CPU oracle on a bounded sample of the same token: whole products,
-    taken in sweep order until about budget_s seconds of work.  Also checks
-    the GPU's outputs for those products bit for bit."""
+    taken in sweep order until about budget_s seconds of work, at `threads`
+    threads.  Also checks the GPU's outputs for those products bit for bit."""
     import oracle
 
     q_ref, d_ref, _ = oracle.quantize_q8(sw.x, sw.qa, sw.f16_scale)
@@ -110,17 +130,51 @@ def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float, threads: int):
         n += 1
         if secs >= budget_s:
             break
+    return {"threads": threads, "value": round(done_bytes / secs / 1e9, 4), "unit": "GB/s",
+            "s_per_token_equiv": round(sw.sweep_bytes() / (done_bytes / secs), 3),
+            "sample": f"first {n} of {len(sw.shapes)} products of the token ({done_bytes / 1e9:.3f} GB, "
+                      f"{secs:.1f} s); quantizer excluded",
+            "gpu_outputs_checked": int(sum(r for _, r, _ in sw.shapes[:n])),
+            "gpu_outputs_mismatched": mismatched, "gpu_max_rel_err": max_rel}
+
+
+def host_floor_leg(threads: int) -> dict:
+    """The host's streaming-read floor over 768 MiB (the pages' buffer) and
+    4 GiB, at 1, 2, 4, ... threads up to `threads` (median of 3 passes)."""
+    import oracle
+
+    counts = sorted({1, threads} | {t for t in (2, 4, 8, 16) if t < threads})
+    out = {"threads": counts}
+    for name, nbytes in (("768MiB", 768 << 20), ("4GiB", 4 << 30)):
+        out[name + "_GB_s"] = [round(v, 2) for v in oracle.host_read_floor(nbytes, counts, 3)]
+    return out
+
+
+def cpu_baseline(sw, y_gpu: np.ndarray, budget_s: float):
+    """The oracle timed on the host: at all the threads this job may use (the
+    headline cpu_baseline figure) and at one thread, plus the host's memory
+    floor; GPU outputs are checked bit for bit by both legs."""
+    host = host_cpus()
+    threads = cpu_threads()
+    full = oracle_leg(sw, y_gpu, budget_s, threads)
+    one = oracle_leg(sw, y_gpu, budget_s / 2, 1)
+    try:
+        floor = host_floor_leg(threads)
+    except Exception as e:  # context only
+        floor = {"error": f"{type(e).__name__}: {e}"}
     return {
-        "value": round(done_bytes / secs / 1e9, 4),
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"first {n} of {len(sw.shapes)} products of the token ({done_bytes / 1e9:.3f} GB, "
-                  f"{secs:.1f} s); quantizer excluded",
-        "ms_per_token_equiv": round(sw.sweep_bytes() / (done_bytes / secs) * 1e3, 1),
-        "gpu_outputs_checked": int(sum(r for _, r, _ in sw.shapes[:n])),
-        "gpu_outputs_mismatched": mismatched,
-        "gpu_max_rel_err": max_rel,
+        "value": full["value"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": full["sample"],
+        "ms_per_token_equiv": round(full["s_per_token_equiv"] * 1e3, 1),
+        # both legs take products in sweep order, so the larger sample holds the smaller
+        "gpu_outputs_checked": max(full["gpu_outputs_checked"], one["gpu_outputs_checked"]),
+        "gpu_outputs_mismatched": max(full["gpu_outputs_mismatched"], one["gpu_outputs_mismatched"]),
+        "gpu_max_rel_err": max(full["gpu_max_rel_err"], one["gpu_max_rel_err"]),
+        "one_thread": {k: one[k] for k in ("value", "unit", "s_per_token_equiv", "sample")},
+        "host": dict(host, threads_used=threads,
+                     why=f"a GPU job's share of the host is {BOX_THREADS} threads; the oracle's pool is "
+                         "sized to min(affinity, that share)"),
+        "host_memory_floor": floor,
     }
 
 
@@ -350,6 +404,8 @@ def main():
     ap.add_argument("--act", choices=["q8_128", "q8_0"], default="q8_128",
                     help="sweep activations: qa 128 with f32 scales, or qa 32 with f16-valued scales")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of back-to-back steps before the W warm-up steps (untimed)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache sweep timing")
     ap.add_argument("--no-chain", action="store_true", help="skip the decode-chain context field")
@@ -386,18 +442,93 @@ def main():
     q8_0 = args.act == "q8_0"
     sw = StagedSweep(fmt, canon, shapes, x, qa=32 if q8_0 else 128, f16_scale=q8_0)
     log(f"staged {len(shapes)} products, {sw.weight_bytes / 1e9:.3f} GB of weights in {time.time() - t0:.1f} s")
-
     stream = torch.cuda.current_stream()
+    K = args.steps
+
+    def event_pairs(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    # ---- context legs, run BEFORE the timed loop so that the headline is
+    # taken on a GPU that has been busy for a while (clocks settled)
+    floor = read_floor()
+    log(f"streaming-read floor {floor['value']:.0f} GB/s")
+    sw.run()
+    torch.cuda.synchronize()
+    y_ref = sw.y.cpu().numpy()
+
+    # the sweep with the 256 MB last-level cache flushed before each launch (a
+    # streaming read of 512 MB between launches, outside the events; a read
+    # leaves no dirty lines to write back during the sweep)
+    cold = None
+    if not args.no_cold:
+        try:
+            scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+            sink = torch.empty(bq.BQ_FLOOR_SINK_WORDS, dtype=torch.int32, device="cuda")
+            torch.cuda.synchronize()
+            cev = event_pairs(20)
+            for b, c in cev:
+                bq.bq_read_floor(scratch, sink)
+                b.record(stream)
+                sw.sweep()
+                c.record(stream)
+            torch.cuda.synchronize()
+            cms = np.array([b.elapsed_time(c) for b, c in cev])
+            cold = {"mean": round(float(cms.mean()), 5), "median": round(float(np.median(cms)), 5)}
+            del scratch, sink
+            log(f"sweep after a 512 MB cache flush: {cold['median'] * 1e3:.1f} us (median of 20)")
+        except Exception as e:  # context only; the headline line must print regardless
+            log(f"cold-cache timing skipped: {type(e).__name__}: {e}")
+
+    # the same token in ONE launch that quantizes the f32 activations itself
+    # (bq_sweep_create_x), checked against the two-launch outputs bit for bit
+    fused = None
+    if not q8_0:
+        try:
+            sw.y.fill_(float("nan"))
+            sw.sweep_fused()
+            torch.cuda.synchronize()
+            same = bool(np.array_equal(sw.y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)))
+            nf = max(K, 20)
+            fev = event_pairs(nf)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for b, c in fev:
+                b.record(stream)
+                sw.sweep_fused()
+                c.record(stream)
+            torch.cuda.synchronize()
+            f_ms = (time.perf_counter() - t0) * 1e3 / nf
+            fk = np.array([b.elapsed_time(c) for b, c in fev])
+            fused = {"ms_per_step": round(f_ms, 5), "value": round(sw.fused_bytes() / (f_ms * 1e-3) / 1e9, 2),
+                     "kernel_ms": round(float(fk.mean()), 5), "kernel_ms_median": round(float(np.median(fk)), 5),
+                     "bytes_per_launch": sw.fused_bytes(),
+                     "kernel_GB_s": round(sw.fused_bytes() / (float(fk.mean()) * 1e-3) / 1e9, 2),
+                     "same_bits_as_two_launch": same,
+                     "how": "one bq_token_sweep launch of a bq_sweep_create_x plan (f32 activations quantized "
+                            "in the launch)"}
+            log(f"one-launch token: {f_ms * 1e3:.1f} us per step, kernel {np.median(fk) * 1e3:.1f} us (median), "
+                f"same bits: {same}")
+        except Exception as e:  # the headline line must print regardless
+            fused = {"error": f"{type(e).__name__}: {e}"}
+
+    # settle: the step, back to back, for a fixed time (the GPU's clocks ramp
+    # over the first ~100 launches), then the W warm-up steps the command asks for
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(50):
+            sw.run()
+        settle_steps += 50
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         sw.run()
     torch.cuda.synchronize()
 
-    K = args.steps
-    # events bracket each sweep launch only: a third marker before the
-    # quantizer measured ~4 us more per step; the quantizer's share is the
-    # time from one sweep's end to the next one's start (its kernel and the
-    # two launch gaps)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # ---- the timed region: exactly K steps.  Events bracket each sweep
+    # launch only (a marker before the quantizer measured ~4 us more per
+    # step); the quantizer's share is the time from one sweep's end to the
+    # next one's start (its kernel and the two launch gaps).
+    ev = event_pairs(K)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(K):
@@ -412,63 +543,14 @@ def main():
     sweep_ms_all = np.array([b.elapsed_time(c) for b, c in ev])
     sweep_ms = float(np.mean(sweep_ms_all))
     ms_per_step = wall * 1e3 / K
+    y_gpu = sw.y.cpu().numpy()
+    same_as_first = bool(np.array_equal(y_gpu.view(np.uint32), y_ref.view(np.uint32)))
 
     step_bytes = sw.sweep_bytes() + sw.quantize_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = sw.sweep_bytes() / (sweep_ms * 1e-3) / 1e9
-    y_gpu = sw.y.cpu().numpy()
-    # the same sweep with the 256 MB last-level cache flushed before each launch
-    # (a streaming read of 512 MB between launches, outside the events; a read
-    # leaves no dirty lines to write back during the sweep): cold-cache time
-    cold_ms = None
-    if not args.no_cold:
-        try:
-            scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
-            sink = torch.empty(bq.BQ_FLOOR_SINK_WORDS, dtype=torch.int32, device="cuda")
-            torch.cuda.synchronize()
-            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-            for b, c in cev:
-                bq.bq_read_floor(scratch, sink)
-                b.record(stream)
-                sw.sweep()
-                c.record(stream)
-            torch.cuda.synchronize()
-            cold_ms = float(np.mean([b.elapsed_time(c) for b, c in cev]))
-            del scratch, sink
-            log(f"sweep after a 512 MB cache flush: {cold_ms * 1e3:.1f} us (back to back {sweep_ms * 1e3:.1f} us)")
-        except Exception as e:  # context only; the headline line must print regardless
-            log(f"cold-cache timing skipped: {type(e).__name__}: {e}")
-
-    # context, not the headline: the same token in ONE launch that quantizes
-    # the f32 activations itself (bq_sweep_create_x), checked against the
-    # two-launch outputs bit for bit
-    fused = None
-    if not q8_0:
-        try:
-            sw.y.fill_(float("nan"))
-            for _ in range(args.warmup):
-                sw.sweep_fused()
-            torch.cuda.synchronize()
-            same = bool(np.array_equal(sw.y.cpu().numpy().view(np.uint32), y_gpu.view(np.uint32)))
-            fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for b, c in fev:
-                b.record(stream)
-                sw.sweep_fused()
-                c.record(stream)
-            torch.cuda.synchronize()
-            f_ms = (time.perf_counter() - t0) * 1e3 / K
-            f_kernel = float(np.mean([b.elapsed_time(c) for b, c in fev]))
-            fused = {"ms_per_step": round(f_ms, 5), "value": round(sw.fused_bytes() / (f_ms * 1e-3) / 1e9, 2),
-                     "kernel_ms": round(f_kernel, 5), "bytes_per_launch": sw.fused_bytes(),
-                     "kernel_GB_s": round(sw.fused_bytes() / (f_kernel * 1e-3) / 1e9, 2),
-                     "same_bits_as_two_launch": same,
-                     "how": "one bq_token_sweep launch of a bq_sweep_create_x plan (f32 activations quantized in the launch)"}
-            log(f"one-launch token: {f_ms * 1e3:.1f} us per step, kernel {f_kernel * 1e3:.1f} us, same bits: {same}")
-        except Exception as e:  # the headline line must print regardless
-            fused = {"error": f"{type(e).__name__}: {e}"}
-
+    log(f"timed: {K} steps, {ms_per_step * 1e3:.1f} us per step; sweep events mean {sweep_ms * 1e3:.1f} us, "
+        f"median {np.median(sweep_ms_all) * 1e3:.1f} us")
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -478,12 +560,10 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device-to-device copies done")
 
-    floor = read_floor()
-    log(f"streaming-read floor {floor['value']:.0f} GB/s")
-
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(sw, y_gpu, args.cpu_budget, cpu_threads())
+        cpu = cpu_baseline(sw, y_gpu, args.cpu_budget)
+        log(f"cpu oracle: {cpu['value']} GB/s at {cpu['cores']} threads, {cpu['one_thread']['value']} GB/s at 1")
 
     # context, not the headline: the same products as a dependency-ordered
     # decode (145 groups, each the quantized output of the one before)
@@ -525,10 +605,15 @@ def main():
         },
         "kernels": {
             "sweep_ms": round(sweep_ms, 5),
+            "sweep_ms_median": round(float(np.median(sweep_ms_all)), 5),
             "sweep_ms_min": round(float(sweep_ms_all.min()), 5),
             "quantize_with_gaps_ms": round(quant_ms, 5),
-            "sweep_ms_cold_cache": None if cold_ms is None else round(cold_ms, 5),
+            "sweep_ms_cold_cache": cold,
         },
+        "before_timing": {"settle_s": args.settle, "settle_steps": settle_steps,
+                          "how": "the context legs (floor, cold-cache and one-launch sweeps), then the step back "
+                                 "to back for settle_s, then the W warm-up steps; outputs of the timed steps "
+                                 "equal the first step's bit for bit: " + str(same_as_first)},
         "roofline": {
             "bound": "hbm",
             "kernel": "bq::sweep_kernel",

@@ -19,6 +19,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+FLOOR_SRC = os.path.join(HERE, "host_floor.c")
+FLOOR_LIB = os.path.join(HERE, "libhostfloor.so")
 
 Q1_0 = 1
 Q2_0 = 2
@@ -30,8 +32,12 @@ GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", 
 
 
 def build(src: str = SRC, out: str = LIB) -> str:
-    """Compile ``oracle.c`` (or a variant of it) with plain gcc, no fast-math."""
+    """Compile ``oracle.c`` (or a variant of it) with plain gcc, no fast-math;
+    the default build also compiles the host memory-floor probe."""
     subprocess.run(["gcc", *GCC_FLAGS, "-o", out, src, "-lm", "-lpthread"], check=True)
+    if src == SRC:
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-o", FLOOR_LIB, FLOOR_SRC,
+                        "-lpthread"], check=True)
     return out
 
 
@@ -165,3 +171,20 @@ def matvec(fmt, canon, rows, cols, q, d, qa, ncols=1, threads=1):
 
 def cover_rows(rows, threads):
     return default().cover_rows(rows, threads)
+
+
+def host_read_floor(nbytes: int, thread_counts, reps: int = 3) -> list:
+    """The host's streaming-read bandwidth (GB/s, median of reps passes) over
+    a buffer of nbytes, for each thread count (host_floor.c).  A measurement
+    aid of the benchmark's CPU leg, not part of the oracle's arithmetic."""
+    if not os.path.exists(FLOOR_LIB) or os.path.getmtime(FLOOR_LIB) < os.path.getmtime(FLOOR_SRC):
+        build()
+    lib = ctypes.CDLL(FLOOR_LIB)
+    lib.host_read_floor.restype = ctypes.c_int
+    lib.host_read_floor.argtypes = [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    tc = np.ascontiguousarray(thread_counts, dtype=np.int32)
+    out = np.zeros(tc.size, dtype=np.float64)
+    rc = lib.host_read_floor(int(nbytes), _ptr(tc), int(tc.size), int(reps), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"host_read_floor failed ({rc})")
+    return [float(v) for v in out]
