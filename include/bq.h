@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 5
+#define BQ_ABI_VERSION 6
 
 /* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
  * then 16 payload bytes).
@@ -247,6 +247,26 @@ int bq_sweep_create_x(const bq_gemv_x *list, int32_t count, int32_t qa, bq_sweep
  * BQ_EARG (null plan) or BQ_EHIP if the launch fails.  Allocates nothing.
  * Asynchronous on s. */
 int bq_token_sweep(const bq_sweep *plan, bq_stream s);
+
+/* The sweep of bq_sweep_create + bq_token_sweep in ONE call that allocates
+ * nothing, for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  The
+ * list (host array of count bq_gemv, rules as bq_sweep_create) is validated
+ * and planned on fixed host storage, and the plan (descriptors and work
+ * items) is copied on s into a fixed device array of the library: 320 KiB
+ * per GPU, held until the process ends, room for up to 1024 products and
+ * 16384 work items (the 253 products of a decode token need about 1,900).
+ * Larger lists are refused with BQ_EARG, as is every invalid entry, before
+ * anything is copied or launched.  The copy is from pageable memory, so the
+ * call returns once the table is staged; it may wait for earlier work on s.
+ * Each entry's y equals what bq_token_sweep of a bq_sweep_create plan of the
+ * same list writes.  All calls on one GPU share that GPU's array: calls on
+ * one stream are ordered, but calls that overlap on one GPU (several streams
+ * or threads with launches in flight together) race on it.  Calls from
+ * several host threads are serialised while they plan.  Returns BQ_OK,
+ * BQ_EARG / BQ_EALIGN, or BQ_EHIP if the copy or the launch fails.
+ * Asynchronous on s. */
+int bq_token_sweep_noalloc(const bq_gemv *list, int32_t count, bq_stream s);
 
 /* Release a plan and its device table (NULL is allowed): resources are
  * released only by an explicit call, never behind the caller's back (bankML

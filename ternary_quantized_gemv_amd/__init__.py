@@ -22,7 +22,7 @@ BQ_Q1_0 = 1
 BQ_Q2_0 = 2
 BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
 BQ_FLOOR_SINK_WORDS = 8192
-BQ_ABI_VERSION = 5  # include/bq.h
+BQ_ABI_VERSION = 6  # include/bq.h
 BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
 BLOCK_BYTES = 18
 
@@ -30,6 +30,7 @@ EXPORTS = (
     "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
     "bq_quantize_act_q8", "bq_quantize_act_q8_f16", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
     "bq_sweep_create", "bq_sweep_create_x", "bq_token_sweep", "bq_sweep_destroy", "bq_read_floor",
+    "bq_token_sweep_noalloc",
 )
 
 
@@ -114,6 +115,8 @@ def _load() -> ctypes.CDLL:
     lib.bq_token_sweep.argtypes = [vp, vp]
     lib.bq_sweep_destroy.restype = None
     lib.bq_sweep_destroy.argtypes = [vp]
+    lib.bq_token_sweep_noalloc.restype = ctypes.c_int
+    lib.bq_token_sweep_noalloc.argtypes = [ctypes.POINTER(bq_gemv), i32, vp]
     lib.bq_read_floor.restype = ctypes.c_int
     lib.bq_read_floor.argtypes = [vp, i64, vp, vp]
     return lib
@@ -343,15 +346,20 @@ class Sweep:
             pass
 
 
-def bq_sweep_create(entries) -> Sweep:
-    """entries: [(Weights, Act, y tensor)]."""
+def _gemv_list(entries, fn: str):
     import torch
     arr = (bq_gemv * len(entries))()
     for i, (w, a, y) in enumerate(entries):
-        _need(y, f"entry {i} y", torch.float32, w.rows, "bq_sweep_create")
+        _need(y, f"entry {i} y", torch.float32, w.rows, fn)
         arr[i].w = w.c()
         arr[i].a = a.c()
         arr[i].y = _dev(y, "y")
+    return arr
+
+
+def bq_sweep_create(entries) -> Sweep:
+    """entries: [(Weights, Act, y tensor)]."""
+    arr = _gemv_list(entries, "bq_sweep_create")
     h = ctypes.c_void_p()
     _check(lib.bq_sweep_create(arr, len(entries), ctypes.byref(h)))
     return Sweep(h.value, list(entries))
@@ -379,3 +387,11 @@ def bq_token_sweep(plan: Sweep, stream=None) -> None:
 
 def bq_sweep_destroy(plan: Sweep) -> None:
     plan.destroy()
+
+
+def bq_token_sweep_noalloc(entries, stream=None) -> None:
+    """entries: [(Weights, Act, y tensor)], as bq_sweep_create; planned and
+    launched in one call that allocates no memory (the library's fixed
+    scratch holds the plan)."""
+    arr = _gemv_list(entries, "bq_token_sweep_noalloc")
+    _check(lib.bq_token_sweep_noalloc(arr, len(entries), _stream(stream)))

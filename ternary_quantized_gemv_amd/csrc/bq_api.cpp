@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -259,56 +260,81 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
     return hip_check(fn, launch_group(fmt, qa, shape, args, static_cast<hipStream_t>(s)));
 }
 
-// The work items of a plan over the products descs (validated), balanced
-// over the GPU, and the plan that owns their device copy.
-static int make_plan(const char *fn, const std::vector<GemvDesc> &descs, int fmt, int qa, bool quantize, bq_sweep **plan)
+// The work items of a sweep over the products descs[0..n) (validated),
+// balanced over the GPU, written to out (room for cap items; tmp has room
+// for cap more).  Returns the number of items, or -1 if cap is too small.
+// Allocates nothing, so the no-allocation entry point can use it on fixed
+// storage.  Order: most work first -- the hardware dispatches workgroups in
+// order, so the short items fill the tail; the last kTailItems are cut to
+// one tile per wavefront.  Ties keep the order items were made in (the
+// sequence number rides in WorkItem::pad while sorting).
+static int plan_items(const GemvDesc *descs, int n, WorkItem *out, WorkItem *tmp, int cap)
 {
-    std::vector<WorkItem> items;
-    for (size_t i = 0; i < descs.size(); ++i) {
+    int m = 0;
+    for (int i = 0; i < n; ++i) {
         const int tiles = (int)tiles_of(descs[i].rows);
         const int per_item = descs[i].nb <= kChunkBlocks ? kWaves * kMaxRounds : kWaves;
         for (int t = 0; t < tiles; t += per_item) {
-            WorkItem it;
-            it.gemv = (int32_t)i;
-            it.tile0 = t;
-            it.ntiles = std::min(per_item, tiles - t);
-            it.pad = 0;
-            items.push_back(it);
+            if (m >= cap)
+                return -1;
+            out[m] = WorkItem{(int32_t)i, t, std::min(per_item, tiles - t), m};
+            ++m;
         }
     }
-    // Most work first: the hardware dispatches workgroups in order, so the
-    // short items fill the tail.  The last kTailItems are cut to one tile per
-    // wavefront.
-    auto cost = [&](const WorkItem &w) { return (int64_t)w.ntiles * descs[(size_t)w.gemv].nb; };
-    auto by_cost = [&](const WorkItem &a, const WorkItem &b) { return cost(a) > cost(b); };
-    std::stable_sort(items.begin(), items.end(), by_cost);
-    std::vector<WorkItem> tail;
-    size_t head = items.size();
-    while (head > 0 && tail.size() < (size_t)kTailItems) {
-        const WorkItem w = items[--head];
-        if (descs[(size_t)w.gemv].nb > kChunkBlocks || w.ntiles <= kWaves) {
-            tail.push_back(w);
+    auto cost = [&](const WorkItem &w) { return (int64_t)w.ntiles * descs[w.gemv].nb; };
+    auto before = [&](const WorkItem &a, const WorkItem &b) {
+        const int64_t ca = cost(a), cb = cost(b);
+        return ca != cb ? ca > cb : a.pad < b.pad;
+    };
+    std::sort(out, out + m, before);
+    int head = m, nt = 0;
+    while (head > 0 && nt < kTailItems) {
+        const WorkItem w = out[--head];
+        if (descs[w.gemv].nb > kChunkBlocks || w.ntiles <= kWaves) {
+            if (nt >= cap)
+                return -1;
+            tmp[nt] = w;
+            tmp[nt].pad = nt;
+            ++nt;
             continue;
         }
         for (int t = 0; t < w.ntiles; t += kWaves) {
-            WorkItem piece = w;
-            piece.tile0 = w.tile0 + t;
-            piece.ntiles = std::min(kWaves, w.ntiles - t);
-            tail.push_back(piece);
+            if (nt >= cap)
+                return -1;
+            tmp[nt] = WorkItem{w.gemv, w.tile0 + t, std::min(kWaves, w.ntiles - t), nt};
+            ++nt;
         }
     }
-    std::stable_sort(tail.begin(), tail.end(), by_cost);
-    std::vector<WorkItem> sorted(items.begin(), items.begin() + (ptrdiff_t)head);
-    sorted.insert(sorted.end(), tail.begin(), tail.end());
+    std::sort(tmp, tmp + nt, before);
+    if (head + nt > cap)
+        return -1;
+    for (int k = 0; k < nt; ++k)
+        out[head + k] = tmp[k];
+    for (int k = 0; k < head + nt; ++k)
+        out[k].pad = 0;
+    return head + nt;
+}
 
+// A plan over the products descs (validated) that owns the device copy of
+// its descriptors and work items.
+static int make_plan(const char *fn, const std::vector<GemvDesc> &descs, int fmt, int qa, bool quantize, bq_sweep **plan)
+{
+    // every first-pass item becomes at most kMaxRounds pieces
+    size_t cap = 0;
+    for (const GemvDesc &g : descs)
+        cap += (size_t)((tiles_of(g.rows) + kWaves - 1) / kWaves);
+    std::vector<WorkItem> items(cap + 1), tmp(cap + 1);
+    const int nitems = plan_items(descs.data(), (int)descs.size(), items.data(), tmp.data(), (int)cap + 1);
+    if (nitems < 0)
+        return set_error(BQ_EARG, "%s: too many work items", fn);
     const size_t dbytes = descs.size() * sizeof(GemvDesc);
-    const size_t ibytes = sorted.size() * sizeof(WorkItem);
+    const size_t ibytes = (size_t)nitems * sizeof(WorkItem);
     void *dev = nullptr;
     if (hipMalloc(&dev, dbytes + ibytes) != hipSuccess)
         return set_error(BQ_ENOMEM, "%s: hipMalloc of %zu bytes failed", fn, dbytes + ibytes);
     hipError_t e = hipMemcpy(dev, descs.data(), dbytes, hipMemcpyHostToDevice);
     if (e == hipSuccess)
-        e = hipMemcpy(static_cast<char *>(dev) + dbytes, sorted.data(), ibytes, hipMemcpyHostToDevice);
+        e = hipMemcpy(static_cast<char *>(dev) + dbytes, items.data(), ibytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         (void)hipFree(dev);
         return set_error(BQ_EHIP, "%s: %s", fn, hipGetErrorString(e));
@@ -322,11 +348,32 @@ static int make_plan(const char *fn, const std::vector<GemvDesc> &descs, int fmt
     p->qa = qa;
     p->quantize = quantize;
     p->count = (int)descs.size();
-    p->nitems = (int)sorted.size();
+    p->nitems = nitems;
     p->dev = dev;
     p->descs = static_cast<const GemvDesc *>(dev);
     p->items = reinterpret_cast<const WorkItem *>(static_cast<char *>(dev) + dbytes);
     *plan = p;
+    return BQ_OK;
+}
+
+// One entry of a bq_gemv list, checked against the list's format and qa,
+// as its descriptor.
+static int gemv_entry(const char *fn, int i, const bq_gemv &e, int fmt, int qa, GemvDesc *out)
+{
+    char where[96];
+    snprintf(where, sizeof where, "%s: entry %d", fn, i);
+    if (e.w.fmt != fmt || e.a.qa != qa)
+        return set_error(BQ_EARG, "%s: every entry must share the format and qa of entry 0", where);
+    int rc = check_weights(where, &e.w, fmt);
+    if (!rc)
+        rc = check_act(where, &e.a, e.w.cols, 1);
+    if (rc)
+        return rc;
+    if (!e.y)
+        return set_error(BQ_EARG, "%s: null y", where);
+    if (!aligned(e.y, 4))
+        return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
+    *out = make_desc(&e.w, &e.a, e.y);
     return BQ_OK;
 }
 
@@ -341,21 +388,9 @@ BQ_EXPORT int bq_sweep_create(const bq_gemv *list, int32_t count, bq_sweep **pla
     const int fmt = list[0].w.fmt, qa = list[0].a.qa;
     std::vector<GemvDesc> descs((size_t)count);
     for (int i = 0; i < count; ++i) {
-        const bq_gemv &e = list[i];
-        char where[96];
-        snprintf(where, sizeof where, "%s: entry %d", fn, i);
-        if (e.w.fmt != fmt || e.a.qa != qa)
-            return set_error(BQ_EARG, "%s: every entry must share the format and qa of entry 0", where);
-        int rc = check_weights(where, &e.w, fmt);
-        if (!rc)
-            rc = check_act(where, &e.a, e.w.cols, 1);
+        const int rc = gemv_entry(fn, i, list[i], fmt, qa, &descs[(size_t)i]);
         if (rc)
             return rc;
-        if (!e.y)
-            return set_error(BQ_EARG, "%s: null y", where);
-        if (!aligned(e.y, 4))
-            return set_error(BQ_EALIGN, "%s: y must be 4-byte aligned", where);
-        descs[(size_t)i] = make_desc(&e.w, &e.a, e.y);
     }
     return make_plan(fn, descs, fmt, qa, false, plan);
 }
@@ -402,6 +437,48 @@ BQ_EXPORT int bq_token_sweep(const bq_sweep *plan, bq_stream s)
         return set_error(BQ_EARG, "%s: null plan", fn);
     return hip_check(fn, launch_sweep(plan->fmt, plan->qa, plan->quantize, (unsigned)plan->nitems, plan->descs, plan->items,
                                       static_cast<hipStream_t>(s)));
+}
+
+// bq_token_sweep_noalloc: the plan is built on fixed host storage (one call
+// at a time, under g_stage_mu) and copied into the library's fixed device
+// scratch (bq_sweep.hip), so nothing is allocated on the host or the device.
+static std::mutex g_stage_mu;
+alignas(256) static unsigned char g_stage[kScratchBytes];
+static WorkItem g_tmp[kScratchItems];
+
+BQ_EXPORT int bq_token_sweep_noalloc(const bq_gemv *list, int32_t count, bq_stream s)
+{
+    const char *fn = "bq_token_sweep_noalloc";
+    if (!list || count < 1)
+        return set_error(BQ_EARG, "%s: empty list", fn);
+    if (count > kScratchProducts)
+        return set_error(BQ_EARG, "%s: %d products exceed the fixed scratch's %d", fn, (int)count, kScratchProducts);
+    std::lock_guard<std::mutex> lock(g_stage_mu);
+    GemvDesc *descs = reinterpret_cast<GemvDesc *>(g_stage);
+    WorkItem *items = reinterpret_cast<WorkItem *>(g_stage + kScratchItemsOffset);
+    const int fmt = list[0].w.fmt, qa = list[0].a.qa;
+    for (int i = 0; i < count; ++i) {
+        const int rc = gemv_entry(fn, i, list[i], fmt, qa, &descs[i]);
+        if (rc)
+            return rc;
+    }
+    const int nitems = plan_items(descs, count, items, g_tmp, kScratchItems);
+    if (nitems < 0)
+        return set_error(BQ_EARG, "%s: the products need more than the fixed scratch's %d work items", fn,
+                         kScratchItems);
+    unsigned char *ptr = nullptr;
+    int rc = hip_check(fn, scratch_address(reinterpret_cast<void **>(&ptr)));
+    if (rc)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(s);
+    // one copy of the used part: descriptors from offset 0, work items from
+    // kScratchItemsOffset (pageable source: the call returns once it is staged)
+    const size_t used = (size_t)kScratchItemsOffset + (size_t)nitems * sizeof(WorkItem);
+    rc = hip_check(fn, hipMemcpyAsync(ptr, g_stage, used, hipMemcpyHostToDevice, st));
+    if (rc)
+        return rc;
+    return hip_check(fn, launch_sweep(fmt, qa, false, (unsigned)nitems, reinterpret_cast<const GemvDesc *>(ptr),
+                                      reinterpret_cast<const WorkItem *>(ptr + kScratchItemsOffset), st));
 }
 
 BQ_EXPORT void bq_sweep_destroy(bq_sweep *plan)

@@ -90,6 +90,18 @@ hipError_t launch_wide_q8(int fmt, int qa, GroupShape shape, const GroupArgs &a,
 constexpr int kFloorGrid = 1024;
 constexpr int kFloorSinkWords = 8192;
 hipError_t launch_floor(const void *p, int64_t bytes, uint32_t *sink, hipStream_t st);
+// The fixed device scratch of bq_token_sweep_noalloc (bq_sweep.hip): the
+// descriptors of up to kScratchProducts products from offset 0, the work
+// items (up to kScratchItems) from kScratchItemsOffset.  One copy per GPU,
+// held until the process ends.
+constexpr int kScratchProducts = 1024;
+constexpr int kScratchItems = 16384;
+constexpr int kScratchItemsOffset = kScratchProducts * (int)sizeof(GemvDesc);
+constexpr int kScratchBytes = kScratchItemsOffset + kScratchItems * (int)sizeof(WorkItem);
+static_assert(kScratchItemsOffset % 256 == 0, "work items start aligned");
+// The scratch's address on the current device (looked up once per device
+// with hipGetSymbolAddress, then cached).
+hipError_t scratch_address(void **out);
 // launch_quantize: n values in blocks of qa, f32 or f16-valued scales (bq_quantize.hip).
 hipError_t launch_quantize(const float *x, int64_t n, int qa, bool f16_scale, int8_t *q, float *d, hipStream_t st);
 

@@ -29,6 +29,8 @@
 //   workgroup per work item (up to 8 tiles of one matrix), ordered from the
 //   most to the least work so the hardware's in-order dispatch balances the
 //   GPU.
+#include <mutex>
+
 #include "bq_device.h"
 #include "bq_launch.h"
 #include "bq_split.h"
@@ -450,6 +452,36 @@ hipError_t launch_sweep(int fmt, int qa, bool quantize, unsigned nitems, const G
                               : sweep_fmt<BQ_Q2_0, true>(qa, nitems, descs, items, st);
     return fmt == BQ_Q1_0 ? sweep_fmt<BQ_Q1_0, false>(qa, nitems, descs, items, st)
                           : sweep_fmt<BQ_Q2_0, false>(qa, nitems, descs, items, st);
+}
+
+// ------------------------------------------------------------ fixed scratch
+// The descriptor table of bq_token_sweep_noalloc lives in this array rather
+// than in an allocation.  In host code `scratch` only names the symbol; the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current and kept per device (each GPU has its own copy).
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void **out)
+{
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
 }
 
 template <int FMT>

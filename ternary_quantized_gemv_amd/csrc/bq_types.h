@@ -53,6 +53,8 @@ struct GemvDesc {
     const float *x;  // f32 activation, for sweeps that quantize it in the launch (q and d unused)
 };
 
+static_assert(sizeof(GemvDesc) == 64, "descriptor layout");
+
 // A work item of a sweep: tiles tile0 .. tile0 + ntiles - 1 of product gemv;
 // wavefront w takes tiles tile0 + w, tile0 + w + kWaves, ...
 struct WorkItem {

@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 5
+    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 6
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
@@ -242,3 +242,29 @@ def test_size_limits():
     plan = ctypes.c_void_p()
     assert lib.bq_sweep_create(arr, 1, ctypes.byref(plan)) == bq.BQ_EARG and not plan.value
     assert "payload" in bq.bq_last_error()
+
+
+def test_noalloc_sweep_validates_before_launch():
+    """The no-allocation sweep refuses bad lists on the host, before it looks
+    up its scratch or touches the GPU."""
+    lib = bq.lib
+    w = bq.bq_weights(1, 0, 64, 256, 0x1000, 0x2000)
+    a = bq.bq_act(0x3000, 0x4000, 256, 128, 1, 256, 2)
+    assert lib.bq_token_sweep_noalloc(None, 1, None) == bq.BQ_EARG
+    arr = (bq.bq_gemv * 2)()
+    assert lib.bq_token_sweep_noalloc(arr, 0, None) == bq.BQ_EARG
+    assert lib.bq_token_sweep_noalloc(arr, 1025, None) == bq.BQ_EARG and "1024" in bq.bq_last_error()
+    arr[0].w, arr[0].a, arr[0].y = w, a, 0x5000
+    arr[1].w, arr[1].a, arr[1].y = w, a, 0x6000
+    arr[1].a.qa = 32
+    assert lib.bq_token_sweep_noalloc(arr, 2, None) == bq.BQ_EARG and "entry 1" in bq.bq_last_error()
+    arr[1].a.qa = 128
+    arr[1].y = 0x6002
+    assert lib.bq_token_sweep_noalloc(arr, 2, None) == bq.BQ_EALIGN
+    # more work items than the scratch holds: 400 products of 151,936 rows (2,374 tiles each)
+    big = (bq.bq_gemv * 400)()
+    for i in range(400):
+        big[i].w = bq.bq_weights(1, 0, 151936, 4096, 0x1000, 0x2000)
+        big[i].a = bq.bq_act(0x3000, 0x4000, 4096, 128, 1, 4096, 32)
+        big[i].y = 0x5000
+    assert lib.bq_token_sweep_noalloc(big, 400, None) == bq.BQ_EARG and "16384" in bq.bq_last_error()
