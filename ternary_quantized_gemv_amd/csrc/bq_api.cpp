@@ -26,14 +26,33 @@ namespace bq {
 // a tile's blocks spread over the whole CU; one grid row per column) up to
 // 512 tiles, beyond that one row per lane with up to eight tiles per
 // workgroup (rows_kernel for groups; matvec_kernel, the sweep's walk, for
-// single products).  Several columns past 512 tiles in all: four wavefronts
-// per tile, one grid row per column (launch_split), up to kSplitMaxTiles
-// tiles per column, above that four columns per workgroup from interleaved
-// tables (launch_cols) for at least kColsMinCols columns, else one row per
-// lane per column: there the per-column kernels re-stream the weights once
-// per column, while on smaller matrices their extra parallelism wins.
+// single products).  Several columns past 512 tiles in all: on matrices of
+// up to kSplitMaxTiles tiles, the split-columns kernel (several wavefronts
+// per tile, four columns per workgroup from interleaved tables; shape by
+// splitcols_shape), one stream of the weights per group of four columns; on
+// taller matrices four columns per workgroup one row per lane
+// (launch_cols) for at least kColsMinCols columns, else one row per lane
+// per column.
 constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
+
+// Shape of the split-columns kernel for ncols >= 2 columns on `tiles` row
+// tiles (at most kSplitMaxTiles): the one with the most wavefronts per tile
+// whose workgroups (row blocks times groups of four columns) fit one round
+// of the 256 compute units, else the one with the fewest workgroups.
+// Measured on MI355X against one grid row per column, us: Q1_0 12288x4096
+// N = 4 / 8 / 16 17.1 / 24.7 / 44.7 -> 15.4 / 18.2 / 24.9; Q2_0 the same
+// 27.8 / 42.3 / 78.1 -> 27.1 / 28.8 / 44.4; Q1_0 44800x1024 N = 2 / 4 / 16
+// 13.4 / 23.0 / 79.1 -> 8.2 / 8.5 / 22.0; Q1_0 4096x12288 N = 16 43.3 ->
+// 37.4.  Every choice the rule makes was within noise of the fastest shape.
+static int splitcols_shape(int tiles, int ncols)
+{
+    const int cgroups = (ncols + 3) / 4;
+    for (int s = 0; s < kSplitColsShapes; ++s)
+        if ((int64_t)((tiles + kSplitColsTpw[s] - 1) / kSplitColsTpw[s]) * cgroups <= 256)
+            return s;
+    return kSplitColsShapes - 1;
+}
 
 // ------------------------------------------------------------ validation
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -135,6 +154,8 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
         e = launch_wide_q8(FMT, a->qa, shape, args, a->ncols, st);
     } else if (a->ncols >= kColsMinCols && tiles > kSplitMaxTiles)
         e = launch_cols(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
+    else if (a->ncols >= 2 && tiles <= kSplitMaxTiles)
+        e = launch_splitcols(FMT, splitcols_shape(tiles, a->ncols), a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
     else if (tiles <= kSplitMaxTiles)
         e = launch_split(FMT, a->qa, g, a->ld_q, a->ld_d, tiles, a->ncols, st);
     else

@@ -53,13 +53,14 @@ __device__ __forceinline__ f32x4 tab4(const f32x4 *T, int slot, uint32_t idx16)
 // lane group t%8); entry n: sum_i (bit i of n ? q_i : wrap8(-q_i)), times d1
 // on sub-block 0.  Q2_0 slot t covers values 2t, 2t+1; entry n = 4h + e:
 // (e-1)*q_2t + (h-1)*q_2t+1.
-template <int FMT, int QA>
+template <int FMT, int QA, int CHUNK = kColsChunk, int THREADS = kColsWaves * 64>
 __device__ void build_cols(f32x4 *T, float *D1, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int c0, int ncols,
                            int k0, int nbc)
 {
     constexpr int S = FMT == BQ_Q1_0 ? 4 : 2;
-    constexpr int kThreadsHere = kColsWaves * 64;
-    constexpr int kIters = kColsChunk * kSlotsPerBlock * 4 * kColsNC / kThreadsHere;
+    constexpr int kThreadsHere = THREADS;
+    constexpr int kIters = CHUNK * kSlotsPerBlock * 4 * kColsNC / kThreadsHere;
+    static_assert(kIters * kThreadsHere == CHUNK * kSlotsPerBlock * 4 * kColsNC, "whole table quarters per thread");
     // unit u = (slot t, quarter h, column c): entries 4h..4h+3 of column c.
     // All of a thread's loads are issued before any is used.
     const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
@@ -275,6 +276,294 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 {
     return fmt == BQ_Q1_0 ? cols_fmt<BQ_Q1_0>(qa, g, ld_q, ld_d, tiles, ncols, st)
                           : cols_fmt<BQ_Q2_0>(qa, g, ld_q, ld_d, tiles, ncols, st);
+}
+
+// ------------------------------------------------------------ split columns
+// Several activation columns against a matrix of few row tiles (too few for
+// cols_kernel's one row per lane to fill the GPU): W wavefronts share a
+// 64-row tile, wavefront k carrying the chains of lane groups
+// L = k, k + W, ... (LG = 8 / W of them) of every row, for four columns at
+// once from the interleaved tables above (one ds_read_b128 serves the four).
+// The lane groups of a wavefront are ones the final tree joins first --
+// W = 4: a_k + a_(k+4); W = 2: (a_k + a_(k+4)) + (a_(k+2) + a_(k+6)) -- so a
+// wavefront adds them in the tree's order and the remaining additions of
+// the tree go through LDS.  Tables cover 8-block chunks (64 KiB); the
+// wavefronts of a tile read the same payload (one HBM stream, the rest from
+// the caches), each rotating a word once so that its lane groups' nibbles
+// sit at bits 4..7 of bytes (nibble * 16: an entry of four floats).
+constexpr int kScChunk = 8;  // blocks per table chunk (one scale group)
+constexpr int kScRing = 4;   // payload blocks loaded ahead
+
+// The partial of a wavefront's lane groups, in the tree's order.
+template <int LG>
+__device__ __forceinline__ float sc_part(const float (&acc)[LG][kColsNC], int c)
+{
+    if constexpr (LG == 1)
+        return acc[0][c];
+    else if constexpr (LG == 2)
+        return acc[0][c] + acc[1][c];
+    else
+        return (acc[0][c] + acc[2][c]) + (acc[1][c] + acc[3][c]);
+}
+
+// The inputs of one chunk's interleaved tables, read a chunk ahead into
+// registers so that the build after the next barrier does not wait for
+// memory: unit u = (slot t, quarter h, column c) of the table.  Unlike
+// build_cols, every entry holds the integer sum s (sub-block 0 too); the
+// walk forms d1 * s itself, the same single rounding.
+template <int FMT, int QA, int CHUNK, int THREADS>
+struct ColsInputs {
+    static constexpr int kIters = CHUNK * kSlotsPerBlock * 4 * kColsNC / THREADS;
+    static constexpr int S = FMT == BQ_Q1_0 ? 4 : 2;
+    static constexpr int kD1 = (CHUNK * S * kColsNC + THREADS - 1) / THREADS;
+    uint32_t wq[kIters];
+    float dd[kD1];
+
+    __device__ __forceinline__ void load(const GemvDesc &g, int64_t ld_q, int64_t ld_d, int c0, int ncols, int k0,
+                                         int nbc)
+    {
+        const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int u = threadIdx.x + it * THREADS;
+            const int c = u % kColsNC, t = u / (4 * kColsNC);
+            const bool ok = u < nunits && c0 + c < ncols;
+            const int cc = ok ? c0 + c : c0;
+            const int8_t *q = g.q + (int64_t)cc * ld_q + k0;
+            if (FMT == BQ_Q1_0)
+                wq[it] = ok ? *reinterpret_cast<const uint32_t *>(q + 4 * t) : 0u;
+            else
+                wq[it] = ok ? *reinterpret_cast<const uint16_t *>(q + 2 * t) : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < kD1; ++r) {
+            const int i = threadIdx.x + r * THREADS;
+            const int sb = i / kColsNC, c = i % kColsNC;
+            const bool ok = i < nbc * S * kColsNC && c0 + c < ncols;
+            dd[r] = ok ? g.d[(int64_t)(c0 + c) * ld_d + (k0 + 32 * sb) / QA] : 0.0f;
+        }
+    }
+
+    // the tables of the loaded chunk (entries as in build_cols)
+    __device__ __forceinline__ void store(f32x4 *T, float *D1, int nbc) const
+    {
+        const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
+        float *Tf = reinterpret_cast<float *>(T);
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int u = threadIdx.x + it * THREADS;
+            if (u >= nunits)
+                break;
+            const int c = u % kColsNC, h = (u / kColsNC) & 3, t = u / (4 * kColsNC);
+            float v[4];
+            if (FMT == BQ_Q1_0) {
+                int p1[4], p0[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = (int8_t)(wq[it] >> (8 * i));
+                    p1[i] = x;
+                    p0[i] = x == -128 ? -128 : -x;
+                }
+                const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (float)(((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]) + hi);
+            } else {
+                const int qa0 = (int8_t)(wq[it] & 0xFF), qa1 = (int8_t)(wq[it] >> 8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Tf[(t * 16 + 4 * h + e) * kColsNC + c] = v[e];
+        }
+#pragma unroll
+        for (int r = 0; r < kD1; ++r) {
+            const int i = threadIdx.x + r * THREADS;
+            if (i < nbc * S * kColsNC)
+                D1[i] = dd[r];
+        }
+    }
+};
+
+// One block (index b within the chunk) of the calling lane's row: the chains
+// of lane groups k + W*i, four columns each.
+template <int FMT, int W>
+__device__ __forceinline__ void sc_block(const f32x4 *__restrict__ T, const float *__restrict__ D1, int b, u32x4 w,
+                                         float d0, int k, float (&acc)[8 / W][kColsNC])
+{
+    constexpr int LG = 8 / W;
+    float ab[LG][kColsNC];
+    if (FMT == BQ_Q1_0) {
+        // nibble L sits at bits 4L+2 .. 4L+5; a right rotation by 4k - 2 brings
+        // nibble k + W*i to bits 4..7 of byte i*W/2
+        const uint32_t rot = (uint32_t)(4 * k + 30) & 31u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t x = __builtin_amdgcn_alignbit(w[j], w[j], rot);
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1 + (b * 4 + j) * kColsNC);
+#pragma unroll
+            for (int i = 0; i < LG; ++i) {
+                const int L = k + W * i;
+                const f32x4 v = tab4(T, b * kSlotsPerBlock + j * 8 + L, nib16(x, i * W / 2));
+#pragma unroll
+                for (int c = 0; c < kColsNC; ++c)
+                    ab[i][c] = j == 0 ? d1[c] * v[c] : __builtin_fmaf(d1[c], v[c], ab[i][c]);
+            }
+        }
+    } else {
+        // lane group L of sub-block j is byte L & 3 of word 2j + (L >> 2); its low
+        // nibble after a right rotation by 8(k & 3) - 2, its high nibble after
+        // one by 8(k & 3) + 2, at bits 4..7 of byte (L & 3) - (k & 3)
+        const uint32_t rlo = (uint32_t)(8 * (k & 3) + 30) & 31u, rhi = (uint32_t)(8 * (k & 3) + 2) & 31u;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1 + (b * 2 + j) * kColsNC);
+#pragma unroll
+            for (int i = 0; i < LG; ++i) {
+                const int L = k + W * i;
+                const int m = 2 * j + (L >> 2), beta = L & 3, byte = beta - (k & 3);
+                const uint32_t xl = __builtin_amdgcn_alignbit(w[m], w[m], rlo);
+                const uint32_t xh = __builtin_amdgcn_alignbit(w[m], w[m], rhi);
+                const int slot = b * kSlotsPerBlock + m * 8 + 2 * beta;
+                const f32x4 lo = tab4(T, slot, nib16(xl, byte));
+                const f32x4 hi = tab4(T, slot + 1, nib16(xh, byte));
+#pragma unroll
+                for (int c = 0; c < kColsNC; ++c) {
+                    const float sv = lo[c] + hi[c];
+                    ab[i][c] = j == 0 ? d1[c] * sv : __builtin_fmaf(d1[c], sv, ab[i][c]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < LG; ++i)
+#pragma unroll
+        for (int c = 0; c < kColsNC; ++c)
+            acc[i][c] = __builtin_fmaf(d0, ab[i][c], acc[i][c]);
+}
+
+// Workgroup id -> (row block of TPW tiles, column group); ids 8 apart share
+// an XCD, so the column groups of one row block read its weights from one L2.
+template <int FMT, int QA, int W, int TPW>
+__global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int ncols,
+                                                                 int tiles, int cgroups)
+{
+    constexpr int kThreadsHere = W * TPW * 64;
+    constexpr int LG = 8 / W;
+    __shared__ f32x4 T[kScChunk * kSlotsPerBlock * 16];
+    __shared__ float D1[kScChunk * 4 * kColsNC];
+    __shared__ float P[TPW][W][kColsNC][64];
+    const int id = blockIdx.x, slot = id & 7, rest = id >> 3;
+    const int cg = rest % cgroups, rb = (rest / cgroups) * 8 + slot;
+    if (rb * TPW >= tiles)
+        return;  // padding workgroup (the grid is a multiple of 8 row blocks)
+    const int c0 = cg * kColsNC;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int tl = wave / W, k = wave % W;
+    const int tile = rb * TPW + tl;
+    const bool live = tile < tiles;
+    // a wavefront past the last tile reads the workgroup's first tile and stores nothing
+    const int rt = live ? tile : rb * TPW;
+    const rsrc_t wp = rsrc_of(g.bits + (int64_t)rt * g.nb * kTileRows);
+    const rsrc_t sp = rsrc_of(g.scales + (int64_t)rt * g.ng * kTileRows);
+    const uint32_t lo = (uint32_t)lane * 16;
+    const int bl = FMT == BQ_Q1_0 ? 128 : 64;
+
+    float acc[LG][kColsNC];
+#pragma unroll
+    for (int i = 0; i < LG; ++i)
+#pragma unroll
+        for (int c = 0; c < kColsNC; ++c)
+            acc[i][c] = 0.0f;
+    // payload ring kScRing blocks ahead (continuing across chunks); one scale group per chunk
+    u32x4 ring[kScRing];
+#pragma unroll
+    for (int i = 0; i < kScRing; ++i)
+        ring[i] = bload(wp, lo, (uint32_t)min(i, g.nb - 1) * kStep);
+    u32x4 sc = bload(sp, lo, 0);
+
+    ColsInputs<FMT, QA, kScChunk, kThreadsHere> in;
+    in.load(g, ld_q, ld_d, c0, ncols, 0, min(kScChunk, g.nb));
+    for (int cb = 0; cb < g.nb; cb += kScChunk) {
+        const int nbc = min(kScChunk, g.nb - cb);
+        if (cb > 0)
+            __syncthreads();  // every wavefront is done with the previous tables
+        in.store(T, D1, nbc);
+        __syncthreads();
+        if (cb + kScChunk < g.nb)  // the next chunk's table inputs, read during this walk
+            in.load(g, ld_q, ld_d, c0, ncols, (cb + kScChunk) * bl, min(kScChunk, g.nb - cb - kScChunk));
+        const u32x4 sc_next = bload(sp, lo, (uint32_t)min(cb / kScChunk + 1, g.ng - 1) * kStep);
+#pragma unroll
+        for (int i0 = 0; i0 < kScChunk; i0 += kScRing) {
+#pragma unroll
+            for (int i = 0; i < kScRing; ++i) {
+                const u32x4 w = ring[i];
+                ring[i] = bload(wp, lo, (uint32_t)min(cb + i0 + i + kScRing, g.nb - 1) * kStep);
+                if (i0 + i < nbc) {
+                    float d0 = scale_of(sc, i0 + i);
+                    asm volatile("" : "+v"(d0));
+                    sc_block<FMT, W>(T, D1, i0 + i, w, d0, k, acc);
+                }
+            }
+        }
+        sc = sc_next;
+    }
+#pragma unroll
+    for (int c = 0; c < kColsNC; ++c)
+        P[tl][k][c][lane] = sc_part<LG>(acc, c);
+    __syncthreads();
+    const int row = tile * kTileRows + lane;
+    if (k == 0 && live && row < g.rows) {
+#pragma unroll
+        for (int c = 0; c < kColsNC; ++c) {
+            if (c0 + c < ncols) {
+                float y;
+                if constexpr (W == 8)
+                    y = ((P[tl][0][c][lane] + P[tl][4][c][lane]) + (P[tl][2][c][lane] + P[tl][6][c][lane])) +
+                        ((P[tl][1][c][lane] + P[tl][5][c][lane]) + (P[tl][3][c][lane] + P[tl][7][c][lane]));
+                else if constexpr (W == 4)
+                    y = (P[tl][0][c][lane] + P[tl][2][c][lane]) + (P[tl][1][c][lane] + P[tl][3][c][lane]);
+                else
+                    y = P[tl][0][c][lane] + P[tl][1][c][lane];
+                g.y[(int64_t)(c0 + c) * g.rows + row] = y;
+            }
+        }
+    }
+}
+
+template <int FMT, int W, int TPW>
+static hipError_t splitcols_shape(int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                                  hipStream_t st)
+{
+    const int cgroups = (ncols + kColsNC - 1) / kColsNC;
+    const int rblocks = (tiles + TPW - 1) / TPW;
+    const dim3 grid((unsigned)(((rblocks + 7) / 8) * 8 * cgroups)), block(W * TPW * 64);
+    switch (qa) {
+    case 32: hipLaunchKernelGGL((splitcols_kernel<FMT, 32, W, TPW>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, cgroups); break;
+    case 64: hipLaunchKernelGGL((splitcols_kernel<FMT, 64, W, TPW>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, cgroups); break;
+    default: hipLaunchKernelGGL((splitcols_kernel<FMT, 128, W, TPW>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, cgroups); break;
+    }
+    return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t splitcols_fmt(int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
+                                hipStream_t st)
+{
+    switch (shape) {
+    case 0: return splitcols_shape<FMT, 8, 1>(qa, g, ld_q, ld_d, tiles, ncols, st);
+    case 1: return splitcols_shape<FMT, 4, 2>(qa, g, ld_q, ld_d, tiles, ncols, st);
+    default: return splitcols_shape<FMT, 2, 4>(qa, g, ld_q, ld_d, tiles, ncols, st);
+    }
+}
+
+hipError_t launch_splitcols(int fmt, int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles,
+                            int ncols, hipStream_t st)
+{
+    return fmt == BQ_Q1_0 ? splitcols_fmt<BQ_Q1_0>(shape, qa, g, ld_q, ld_d, tiles, ncols, st)
+                          : splitcols_fmt<BQ_Q2_0>(shape, qa, g, ld_q, ld_d, tiles, ncols, st);
 }
 
 }  // namespace bq
