@@ -37,21 +37,27 @@ constexpr int kSplitMaxTiles = 1024;
 constexpr int kColsMinCols = 4;
 
 // Shape of the split-columns kernel for ncols >= 2 columns on `tiles` row
-// tiles (at most kSplitMaxTiles): the one with the most wavefronts per tile
-// whose workgroups (row blocks times groups of four columns) fit one round
-// of the 256 compute units, else the one with the fewest workgroups.
-// Measured on MI355X against one grid row per column, us: Q1_0 12288x4096
-// N = 4 / 8 / 16 17.1 / 24.7 / 44.7 -> 15.4 / 18.2 / 24.9; Q2_0 the same
-// 27.8 / 42.3 / 78.1 -> 27.1 / 28.8 / 44.4; Q1_0 44800x1024 N = 2 / 4 / 16
-// 13.4 / 23.0 / 79.1 -> 8.2 / 8.5 / 22.0; Q1_0 4096x12288 N = 16 43.3 ->
-// 37.4.  Every choice the rule makes was within noise of the fastest shape.
+// tiles (at most kSplitMaxTiles): the first of eight wavefronts per tile
+// with one tile per workgroup, then four per tile with two, three or four
+// tiles, whose workgroups (row blocks times groups of four columns) fit one
+// round of the 256 compute units; failing that three tiles per workgroup up
+// to two rounds, else four.  Measured on MI355X (us, event-timed replays of
+// ~1 GB of weight copies) against one grid row per column:
+//   Q1_0 12288x4096  N = 4 / 8 / 16   17.1 / 24.7 / 44.7 -> 15.0 / 18.0 / 20.7
+//   Q2_0 12288x4096  N = 8 / 16       42.3 / 78.1 -> 28.8 / 33.8
+//   Q1_0 44800x1024  N = 2 / 4 / 16   13.4 / 23.3 / 79.1 -> 7.7 / 7.8 / 21.4
+//   Q1_0 20000x4096  N = 2 / 4 / 16   17.8 / 25.4 / 77.1 -> 17.8 / 18.0 / 39.0
+//   Q1_0 65536x1024  N = 4 / 8        31.7 / 57.2 -> 8.7 / 15.5
+// and every choice this rule makes was the fastest shape measured or within
+// 0.4 us of it.
 static int splitcols_shape(int tiles, int ncols)
 {
-    const int cgroups = (ncols + 3) / 4;
+    const int64_t cgroups = (ncols + 3) / 4;
+    auto wgs = [&](int s) { return (int64_t)((tiles + kSplitColsTpw[s] - 1) / kSplitColsTpw[s]) * cgroups; };
     for (int s = 0; s < kSplitColsShapes; ++s)
-        if ((int64_t)((tiles + kSplitColsTpw[s] - 1) / kSplitColsTpw[s]) * cgroups <= 256)
+        if (wgs(s) <= 256)
             return s;
-    return kSplitColsShapes - 1;
+    return wgs(2) <= 512 ? 2 : 3;
 }
 
 // ------------------------------------------------------------ validation

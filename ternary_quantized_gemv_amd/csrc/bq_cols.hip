@@ -313,7 +313,7 @@ __device__ __forceinline__ float sc_part(const float (&acc)[LG][kColsNC], int c)
 // walk forms d1 * s itself, the same single rounding.
 template <int FMT, int QA, int CHUNK, int THREADS>
 struct ColsInputs {
-    static constexpr int kIters = CHUNK * kSlotsPerBlock * 4 * kColsNC / THREADS;
+    static constexpr int kIters = (CHUNK * kSlotsPerBlock * 4 * kColsNC + THREADS - 1) / THREADS;
     static constexpr int S = FMT == BQ_Q1_0 ? 4 : 2;
     static constexpr int kD1 = (CHUNK * S * kColsNC + THREADS - 1) / THREADS;
     uint32_t wq[kIters];
@@ -552,10 +552,12 @@ template <int FMT>
 static hipError_t splitcols_fmt(int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles, int ncols,
                                 hipStream_t st)
 {
+    static_assert(kSplitColsShapes == 4, "one case per shape");
     switch (shape) {
     case 0: return splitcols_shape<FMT, 8, 1>(qa, g, ld_q, ld_d, tiles, ncols, st);
     case 1: return splitcols_shape<FMT, 4, 2>(qa, g, ld_q, ld_d, tiles, ncols, st);
-    default: return splitcols_shape<FMT, 2, 4>(qa, g, ld_q, ld_d, tiles, ncols, st);
+    case 2: return splitcols_shape<FMT, 4, 3>(qa, g, ld_q, ld_d, tiles, ncols, st);
+    default: return splitcols_shape<FMT, 4, 4>(qa, g, ld_q, ld_d, tiles, ncols, st);
     }
 }
 

@@ -56,10 +56,10 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
                        hipStream_t st);
 // launch_splitcols: ncols columns, four per workgroup from interleaved
 // tables, several wavefronts per tile (bq_cols.hip); shape 0: eight
-// wavefronts per tile, one tile per workgroup; 1: four per tile, two tiles;
-// 2: two per tile, four tiles.
-constexpr int kSplitColsShapes = 3;
-constexpr int kSplitColsTpw[kSplitColsShapes] = {1, 2, 4};
+// wavefronts per tile, one tile per workgroup; 1, 2, 3: four wavefronts per
+// tile, two, three or four tiles per workgroup.
+constexpr int kSplitColsShapes = 4;
+constexpr int kSplitColsTpw[kSplitColsShapes] = {1, 2, 3, 4};
 hipError_t launch_splitcols(int fmt, int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles,
                             int ncols, hipStream_t st);
 // launch_group: a group of products sharing one f32 activation, quantized

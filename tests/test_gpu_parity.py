@@ -196,19 +196,21 @@ def test_small_batch_tall(fmt, rows, cols, ncols, qa, regime):
 
 # Several columns on matrices of up to 1024 row tiles past the wide shapes:
 # the split-columns kernel, four columns per workgroup from interleaved
-# tables and eight, four or two wavefronts per tile (shape chosen so the
-# workgroups fit one round of the GPU).  Cases: each shape and format, rows
-# ragged, rows of 9 / 33 / 96 blocks (partial and several 8-block chunks), a
-# last group of one to three columns, every qa, the -128 regimes, 1024 tiles.
+# tables, eight wavefronts per tile (one tile per workgroup) or four (two,
+# three or four tiles), the shape chosen so the workgroups fit one round of
+# the GPU.  Cases: each shape and format, rows ragged, rows of 5 / 8 / 9 / 32
+# / 34 / 96 blocks (partial and several 8-block chunks), a last group of one
+# to three columns, every qa, the -128 regimes, 1024 tiles.
 SPLITCOLS = [
     (Q1, 12800, 1152, 3, 128, "quant"),   # 200 tiles: eight per tile; 9 blocks (8 + 1)
     (Q2, 12801, 576, 3, 64, "raw"),       # 201 ragged tiles, eight per tile
     (Q1, 19200, 4096, 2, 32, "raw"),      # 300 tiles: four per tile, two tiles per workgroup
-    (Q2, 19250, 2176, 5, 128, "quant"),   # 301 tiles, five columns: two per tile, four tiles; 34 blocks
-    (Q1, 44800, 1024, 2, 64, "mixed"),    # 700 tiles: two per tile
+    (Q2, 19250, 2176, 5, 128, "quant"),   # 301 tiles, five columns: four per tile, three tiles; 34 blocks
+    (Q1, 44800, 1024, 2, 64, "mixed"),    # 700 tiles: four per tile, three tiles
     (Q1, 4096, 12288, 16, 128, "raw"),    # 64 tiles, sixteen columns: eight per tile; 96 blocks
     (Q2, 8192, 4096, 8, 64, "quant"),     # 128 tiles, eight columns: eight per tile
-    (Q1, 65536, 640, 6, 32, "quant"),     # 1024 tiles, six columns: two per tile (two rounds); 5 blocks
+    (Q1, 65536, 640, 6, 32, "quant"),     # 1024 tiles, six columns: four per tile, four tiles (two rounds)
+    (Q2, 65536, 512, 3, 64, "raw"),       # 1024 tiles: four per tile, four tiles
     (Q2, 6400, 2048, 7, 32, "mixed"),     # 100 tiles, seven columns (a group of three)
 ]
 
