@@ -24,7 +24,7 @@ Other workloads (each prints its own JSON line; not the headline):
                     12288x4096, 4096x12288, 151936x4096; Q2_0 4096x4096,
                     1024x4096, 12288x4096, 4096x12288): us per product, GB/s,
                     fraction of HBM peak, ms per token-equivalent
-  --workload batch  Q1_0 12288x4096 and 151936x4096 with N = 1, 4, 8, 16
+  --workload batch  12288x4096 and 151936x4096 with N = 1, 4, 8, 16 (--fmt)
                     activation columns: us per call against the HBM and the
                     fp32 vector-ALU rooflines
   --workload chain  the token as 145 dependent groups (each group's
@@ -295,34 +295,56 @@ def bench_gemv(args):
 
 
 def bench_batch(args):
+    """Small batch: us per call of bq_q1_0_matvec / bq_q2_0_matvec with N
+    activation columns, weights cycled from ~1.1 GB of copies; for N >= 8 the
+    table and matrix-core paths are each timed beside the automatic choice."""
     import torch
     import ternary_quantized_gemv_amd as bq
 
+    fmt = bq.BQ_Q1_0 if args.fmt == "q1_0" else bq.BQ_Q2_0
+    name = "Q1_0" if fmt == bq.BQ_Q1_0 else "Q2_0"
+    f = bq.bq_q1_0_matvec if fmt == bq.BQ_Q1_0 else bq.bq_q2_0_matvec
     rows_out = []
     for rows in (12288, 151936):
         cols = 4096
-        ws, wbytes = weight_copies(bq, bq.BQ_Q1_0, rows, cols, args.seed)
+        ws, wbytes = weight_copies(bq, fmt, rows, cols, args.seed)
         for ncols in (1, 4, 8, 16):
             a = quantized_columns(bq, cols, ncols, args.seed)
             y = torch.empty(ncols * rows, device="cuda")
-            us = timed_calls(lambda i: bq.bq_q1_0_matvec(ws[i % len(ws)], a, y), max(args.steps // 4, 2 * len(ws)))
+            reps = max(args.steps // 4, 2 * len(ws))
+            paths = {"auto": bq.BQ_BATCH_AUTO}
+            if ncols >= 8:
+                paths.update({"tables": bq.BQ_BATCH_TABLES, "mfma": bq.BQ_BATCH_MFMA})
+            times = {}
+            for pname, path in paths.items():
+                prev = bq.bq_set_batch_path(path)
+                try:
+                    times[pname] = timed_calls(lambda i: f(ws[i % len(ws)], a, y), reps)
+                finally:
+                    bq.bq_set_batch_path(prev)
+            us = times["auto"]
             nbytes = wbytes + ncols * (cols + 4 * (cols // 128) + 4 * rows)
             flops = rows * cols * ncols * 0.625  # 0.3125 f32 multiply-adds per weight per column
             hbm_us = nbytes / (HBM_PEAK_GBS * 1e3)
             valu_us = flops / (VALU_PEAK_TFLOPS * 1e6)
             bound = "hbm" if hbm_us >= valu_us else "alu"
-            rows_out.append({"shape": f"{rows}x{cols}", "ncols": ncols, "us_per_call": round(us, 2),
-                             "GB_s": round(nbytes / us / 1e3, 1), "TFLOP_s": round(flops / us / 1e6, 2),
-                             "bound": bound, "roofline_us": round(max(hbm_us, valu_us), 2),
-                             "frac": round(max(hbm_us, valu_us) / us, 4)})
-            log(f"batch {rows}x{cols} N={ncols}: {us:.2f} us")
+            row = {"shape": f"{rows}x{cols}", "ncols": ncols, "us_per_call": round(us, 2),
+                   "GB_s": round(nbytes / us / 1e3, 1), "TFLOP_s": round(flops / us / 1e6, 2),
+                   "bound": bound, "roofline_us": round(max(hbm_us, valu_us), 2),
+                   "frac": round(max(hbm_us, valu_us) / us, 4)}
+            if ncols >= 8:
+                row["us_tables"] = round(times["tables"], 2)
+                row["us_mfma"] = round(times["mfma"], 2)
+            rows_out.append(row)
+            log(f"batch {name} {rows}x{cols} N={ncols}: " + ", ".join(f"{k} {v:.2f} us" for k, v in times.items()))
         del ws
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "small-batch Q1_0 us per call against the HBM and fp32 vector rooflines",
+    print(json.dumps({"metric": f"small-batch {name} us per call against the HBM and fp32 vector rooflines",
                       "unit": "us", "higher_is_better": False, "n_gpus": 1,
-                      "dtype": "int8xQ1_0->f32", "data": "synthetic (seeded)",
-                      "config": {"workload": "Q1_0 12288x4096 and 151936x4096, N = 1, 4, 8, 16 activation "
-                                             "columns, qa 128; peaks 8 TB/s and 157.3 TFLOP/s"},
+                      "dtype": f"int8x{name}->f32", "data": "synthetic (seeded)",
+                      "config": {"workload": f"{name} 12288x4096 and 151936x4096, N = 1, 4, 8, 16 activation "
+                                             "columns, qa 128; peaks 8 TB/s and 157.3 TFLOP/s; us_tables / "
+                                             "us_mfma: the lane-group sums from LDS tables or the matrix cores"},
                       "results": rows_out}), flush=True)
 
 

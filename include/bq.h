@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 6
+#define BQ_ABI_VERSION 7
 
 /* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
  * then 16 payload bytes).
@@ -200,6 +200,22 @@ int bq_quantize_act_q8_f16(const float *x, int64_t n, int32_t qa, int8_t *q, flo
  * launch fails.  Allocates nothing.  Asynchronous on s. */
 int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
 int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
+
+/* Which kernels compute the lane-group sums of bq_q1_0_matvec /
+ * bq_q2_0_matvec for 8 to 16 activation columns: BQ_BATCH_AUTO (the path
+ * measured faster for the shape), BQ_BATCH_TABLES (LDS lookup tables of the
+ * activation, the VALU path) or BQ_BATCH_MFMA (exact integer sums on the
+ * matrix cores, as products with a block-diagonal activation matrix; the f32
+ * chain of the order above stays on the VALU).  Both paths give the same
+ * bits; the choice affects only speed.  The sums are the integer part of
+ * bankML "gpu/ -- the video-card component", section "kernels.rs -- the
+ * Q1_0 kernels" (exact lane-group sums before the chain).  Process-wide,
+ * atomic; calls already launched keep their path.  Returns the previous
+ * setting, or -1 (with BQ_EARG's message) for an unknown path.  Host only. */
+#define BQ_BATCH_AUTO 0
+#define BQ_BATCH_TABLES 1
+#define BQ_BATCH_MFMA 2
+int bq_set_batch_path(int path);
 
 /* One group of a dependency-ordered decode step in ONE launch: the count
  * products (1..4) that read the same activation -- bankML "gpu/ -- the

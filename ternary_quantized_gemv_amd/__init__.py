@@ -22,7 +22,8 @@ BQ_Q1_0 = 1
 BQ_Q2_0 = 2
 BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
 BQ_FLOOR_SINK_WORDS = 8192
-BQ_ABI_VERSION = 6  # include/bq.h
+BQ_ABI_VERSION = 7  # include/bq.h
+BQ_BATCH_AUTO, BQ_BATCH_TABLES, BQ_BATCH_MFMA = 0, 1, 2
 BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
 BLOCK_BYTES = 18
 
@@ -30,7 +31,7 @@ EXPORTS = (
     "bq_abi_version", "bq_last_error", "bq_packed_bytes", "bq_pack", "bq_unpack",
     "bq_quantize_act_q8", "bq_quantize_act_q8_f16", "bq_q1_0_matvec", "bq_q2_0_matvec", "bq_group_matvec",
     "bq_sweep_create", "bq_sweep_create_x", "bq_token_sweep", "bq_sweep_destroy", "bq_read_floor",
-    "bq_token_sweep_noalloc",
+    "bq_token_sweep_noalloc", "bq_set_batch_path",
 )
 
 
@@ -119,6 +120,8 @@ def _load() -> ctypes.CDLL:
     lib.bq_token_sweep_noalloc.argtypes = [ctypes.POINTER(bq_gemv), i32, vp]
     lib.bq_read_floor.restype = ctypes.c_int
     lib.bq_read_floor.argtypes = [vp, i64, vp, vp]
+    lib.bq_set_batch_path.restype = ctypes.c_int
+    lib.bq_set_batch_path.argtypes = [ctypes.c_int]
     return lib
 
 
@@ -295,6 +298,15 @@ def bq_q1_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
 
 def bq_q2_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
     _matvec(lib.bq_q2_0_matvec, w, a, y, stream)
+
+
+def bq_set_batch_path(path: int) -> int:
+    """Kernels for 8..16 activation columns: BQ_BATCH_AUTO, BQ_BATCH_TABLES or
+    BQ_BATCH_MFMA (process-wide); returns the previous setting."""
+    prev = lib.bq_set_batch_path(int(path))
+    if prev < 0:
+        raise BQError(BQ_EARG, lib.bq_last_error().decode())
+    return prev
 
 
 class GroupCall:

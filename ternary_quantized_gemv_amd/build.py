@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbq.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("bq_sweep.hip", "bq_cols.hip", "bq_group.hip", "bq_quantize.hip",
+SOURCES = [os.path.join(CSRC, f) for f in ("bq_sweep.hip", "bq_cols.hip", "bq_mfma.hip", "bq_group.hip", "bq_quantize.hip",
                                             "bq_floor.hip", "bq_api.cpp", "bq_pack.cpp")]
 HEADERS = [os.path.join(CSRC, f) for f in ("bq_layout.h", "bq_types.h", "bq_device.h", "bq_split.h",
                                             "bq_launch.h")] + [os.path.join(ROOT, "include", "bq.h")]

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -58,6 +59,32 @@ static int splitcols_shape(int tiles, int ncols)
         if (wgs(s) <= 256)
             return s;
     return wgs(2) <= 512 ? 2 : 3;
+}
+
+// The small batch of at least kMfmaMinCols columns on the matrix cores
+// (launch_mfma) or on the table kernels above: BQ_BATCH_AUTO takes the one
+// measured faster for the shape, the others force a path.
+constexpr int kMfmaMinCols = 8;
+static std::atomic<int> g_batch_path{BQ_BATCH_AUTO};
+
+static bool use_mfma(int tiles, int ncols)
+{
+    if (ncols < kMfmaMinCols)
+        return false;
+    const int path = g_batch_path.load(std::memory_order_relaxed);
+    if (path != BQ_BATCH_AUTO)
+        return path == BQ_BATCH_MFMA;
+    (void)tiles;
+    return false;
+}
+
+// Shape of the matrix-core kernel: slice halves in separate wavefronts
+// (shape 1) while one wavefront per 32 rows and eight columns would leave
+// the GPU's 1024 SIMDs with fewer than two each.
+static int mfma_shape(int tiles, int ncols)
+{
+    const int64_t waves = (int64_t)tiles * 2 * ((ncols + 7) / 8);
+    return waves < 2048 ? 1 : 0;
 }
 
 // ------------------------------------------------------------ validation
@@ -147,7 +174,9 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
     const int tiles = (int)tiles_of(w->rows);
     hipStream_t st = static_cast<hipStream_t>(s);
     hipError_t e;
-    if (group_shape((int64_t)tiles * a->ncols) != kShapeRows) {
+    if (use_mfma(tiles, a->ncols)) {
+        e = launch_mfma(FMT, mfma_shape(tiles, a->ncols), a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
+    } else if (group_shape((int64_t)tiles * a->ncols) != kShapeRows) {
         // the shape is chosen for all columns together (grid row c = column c)
         GroupArgs args;
         memset(&args, 0, sizeof args);
@@ -226,6 +255,13 @@ BQ_EXPORT int bq_read_floor(const void *p, int64_t bytes, uint32_t *sink, bq_str
 BQ_EXPORT int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)
 {
     return launch_matvec<BQ_Q1_0>("bq_q1_0_matvec", w, a, y, s);
+}
+
+BQ_EXPORT int bq_set_batch_path(int path)
+{
+    if (path != BQ_BATCH_AUTO && path != BQ_BATCH_TABLES && path != BQ_BATCH_MFMA)
+        return set_error(BQ_EARG, "bq_set_batch_path: path %d unknown", path), -1;
+    return g_batch_path.exchange(path);
 }
 
 BQ_EXPORT int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s)

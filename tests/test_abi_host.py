@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 6
+    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 7
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
@@ -268,3 +268,15 @@ def test_noalloc_sweep_validates_before_launch():
         big[i].a = bq.bq_act(0x3000, 0x4000, 4096, 128, 1, 4096, 32)
         big[i].y = 0x5000
     assert lib.bq_token_sweep_noalloc(big, 400, None) == bq.BQ_EARG and "16384" in bq.bq_last_error()
+
+
+def test_batch_path_knob():
+    """bq_set_batch_path returns the previous setting and refuses unknown paths."""
+    prev = bq.bq_set_batch_path(bq.BQ_BATCH_TABLES)
+    try:
+        assert bq.bq_set_batch_path(bq.BQ_BATCH_MFMA) == bq.BQ_BATCH_TABLES
+        with pytest.raises(bq.BQError, match="path 5 unknown"):
+            bq.bq_set_batch_path(5)
+        assert bq.bq_set_batch_path(bq.BQ_BATCH_AUTO) == bq.BQ_BATCH_MFMA
+    finally:
+        bq.bq_set_batch_path(prev)

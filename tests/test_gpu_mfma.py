@@ -1,0 +1,113 @@
+"""The small batch with its lane-group sums on the matrix cores
+(bq_set_batch_path(BQ_BATCH_MFMA)): every output bit-identical to the oracle.
+
+Cases cover both formats, both workgroup shapes of the kernel (slice halves
+in one wavefront on tall matrices, in two on short ones), 8 and 16 columns
+per workgroup (ragged column counts pad a group), every qa, the -128 regimes
+(Q1_0's int8 wrap goes through the MFMA accumulator input), rows not a
+multiple of 32, and block counts that leave a partial 4-block chunk."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_parity, bqmod, log, matvec_gpu
+
+pytestmark = pytest.mark.gpu
+
+Q1, Q2 = 1, 2
+THREADS = 8
+
+
+@pytest.fixture
+def mfma_path():
+    bq = bqmod()
+    prev = bq.bq_set_batch_path(bq.BQ_BATCH_MFMA)
+    try:
+        yield
+    finally:
+        bq.bq_set_batch_path(prev)
+
+
+def _inputs(fmt, rows, cols, ncols, qa, regime, seed):
+    """Weights and ncols columns.  "quant": the quantizer's output; "raw": raw
+    int8 quants with -128 planted; "mixed": -128 only in the last column."""
+    w = synth.blocks(fmt, rows, cols, seed, rows, ncols)
+    if regime in ("raw", "mixed"):
+        qs, ds = zip(*[synth.raw_q8(cols, qa, 11 * c + seed, force_min=regime == "raw") for c in range(ncols)])
+        if regime == "mixed":
+            qs = [q.copy() for q in qs]
+            qs[-1][7] = -128
+            qs[-1][cols - 2] = -128
+    else:
+        qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, seed, c), qa)[:2] for c in range(ncols)])
+    return w, np.stack(qs), np.stack(ds)
+
+
+CASES = [
+    # short matrices: each slice half in its own wavefront
+    (Q1, 4096, 4096, 8, 128, "quant"),
+    (Q1, 4100, 1152, 16, 32, "raw"),       # ragged rows, 9 blocks (a chunk of 1)
+    (Q1, 12288, 640, 12, 64, "mixed"),     # 12 columns in a group of 16
+    (Q1, 1000, 128, 9, 128, "raw"),        # one block per row
+    (Q2, 4096, 4096, 16, 128, "quant"),
+    (Q2, 3001, 320, 8, 64, "raw"),         # 5 blocks
+    (Q2, 12288, 576, 11, 32, "quant"),
+    # tall matrices: both slice halves in one wavefront
+    (Q1, 65600, 640, 8, 128, "quant"),
+    (Q1, 40001, 1152, 16, 64, "raw"),
+    (Q1, 65601, 384, 13, 32, "mixed"),
+    (Q2, 65600, 448, 8, 32, "raw"),
+    (Q2, 40000, 4096, 16, 128, "quant"),
+    # two column groups (at most 16 columns per call: 16 = one group; 8 < 16)
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,ncols,qa,regime", CASES,
+                         ids=[f"q{f}-{r}x{c}-n{n}-qa{a}-{g}" for f, r, c, n, a, g in CASES])
+def test_mfma_parity(mfma_path, fmt, rows, cols, ncols, qa, regime):
+    name = f"mfma fmt={fmt} {rows}x{cols} N={ncols} qa={qa} {regime}"
+    log(name)
+    w, q, d = _inputs(fmt, rows, cols, ncols, qa, regime, 61)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
+
+
+@pytest.mark.parametrize("fmt,rows", [(Q1, 12288), (Q1, 151936), (Q2, 12288)])
+def test_mfma_full_size(mfma_path, fmt, rows):
+    """The small-batch workloads at their full sizes (qa 128, quantizer output)."""
+    cols, qa = 4096, 128
+    w = synth.blocks(fmt, rows, cols, 51, rows)
+    for ncols in (8, 16):
+        name = f"mfma full fmt={fmt} {rows}x{cols} N={ncols}"
+        log(name)
+        qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 51, c), qa)[:2] for c in range(ncols)])
+        q, d = np.stack(qs), np.stack(ds)
+        y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+        assert_parity(matvec_gpu(fmt, w, rows, cols, q, d, qa), y_ref, name)
+
+
+def test_mfma_q2_code3(mfma_path):
+    """Q2_0 code 3 (+2) through the matrix cores."""
+    rows, cols, ncols, qa = 5000, 640, 10, 64
+    w = synth.q2_0_blocks_all_codes(rows, cols, 93, rows, ncols)
+    qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 93, c), qa)[:2] for c in range(ncols)])
+    q, d = np.stack(qs), np.stack(ds)
+    y_ref = oracle.matvec(Q2, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(matvec_gpu(Q2, w, rows, cols, q, d, qa), y_ref, "mfma Q2_0 code 3")
+
+
+def test_batch_paths_agree():
+    """Both small-batch paths and the automatic choice give the same bits."""
+    bq = bqmod()
+    fmt, rows, cols, ncols, qa = Q1, 20000, 1024, 16, 128
+    w, q, d = _inputs(fmt, rows, cols, ncols, qa, "quant", 67)
+    ys = []
+    for path in (bq.BQ_BATCH_TABLES, bq.BQ_BATCH_MFMA, bq.BQ_BATCH_AUTO):
+        prev = bq.bq_set_batch_path(path)
+        try:
+            ys.append(matvec_gpu(fmt, w, rows, cols, q, d, qa))
+        finally:
+            bq.bq_set_batch_path(prev)
+    assert_parity(ys[1], ys[0], "mfma vs tables")
+    assert_parity(ys[2], ys[0], "auto vs tables")
