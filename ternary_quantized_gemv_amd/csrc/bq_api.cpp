@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -62,30 +63,33 @@ static int splitcols_shape(int tiles, int ncols)
 }
 
 // The small batch of at least kMfmaMinCols columns on the matrix cores
-// (launch_mfma) or on the table kernels above: BQ_BATCH_AUTO takes the one
-// measured faster for the shape, the others force a path.
+// (launch_mfma, eight columns per workgroup) or on the table kernels above.
+// BQ_BATCH_AUTO takes the matrix cores where they measured faster (MI355X,
+// us, event-timed replays of ~1 GB of weight copies, tables -> matrix cores):
+//   Q2_0 151936x4096  N = 8 / 16   178.0 / 328.7 -> 99.6 / 170.9
+//   Q2_0 12288x4096   N = 8 / 16   28.9 / 34.1 -> 27.3 / 32.2
+//   Q1_0 151936x4096  N = 8 / 16   107.1 / 193.1 -> 98.8 / 180.7
+//   Q1_0 12288x4096   N = 8 / 16   17.9 / 20.7 -> 21.5 / 29.2 (tables kept)
+// so Q2_0 from 8 columns on, Q1_0 for whole groups of eight columns on
+// matrices of more than kSplitMaxTiles tiles.  The other settings force a path.
 constexpr int kMfmaMinCols = 8;
 static std::atomic<int> g_batch_path{BQ_BATCH_AUTO};
 
-static bool use_mfma(int tiles, int ncols)
+static bool use_mfma(int fmt, int tiles, int ncols)
 {
     if (ncols < kMfmaMinCols)
         return false;
     const int path = g_batch_path.load(std::memory_order_relaxed);
     if (path != BQ_BATCH_AUTO)
         return path == BQ_BATCH_MFMA;
-    (void)tiles;
-    return false;
+    return fmt == BQ_Q2_0 || (tiles > kSplitMaxTiles && ncols % 8 == 0);
 }
 
-// Shape of the matrix-core kernel: slice halves in separate wavefronts
-// (shape 1) while one wavefront per 32 rows and eight columns would leave
-// the GPU's 1024 SIMDs with fewer than two each.
-static int mfma_shape(int tiles, int ncols)
-{
-    const int64_t waves = (int64_t)tiles * 2 * ((ncols + 7) / 8);
-    return waves < 2048 ? 1 : 0;
-}
+// Shape of the matrix-core kernel: both slice halves of 32 rows in one
+// wavefront on tall matrices (shape 0, measured faster there), the two halves
+// in two wavefronts on matrices of up to kSplitMaxTiles tiles (shape 1: twice
+// the wavefronts where a wavefront per 32 rows cannot fill the GPU).
+static int mfma_shape(int tiles) { return tiles > kSplitMaxTiles ? 0 : 1; }
 
 // ------------------------------------------------------------ validation
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -174,8 +178,8 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
     const int tiles = (int)tiles_of(w->rows);
     hipStream_t st = static_cast<hipStream_t>(s);
     hipError_t e;
-    if (use_mfma(tiles, a->ncols)) {
-        e = launch_mfma(FMT, mfma_shape(tiles, a->ncols), a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
+    if (use_mfma(FMT, tiles, a->ncols)) {
+        e = launch_mfma(FMT, mfma_shape(tiles), a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
     } else if (group_shape((int64_t)tiles * a->ncols) != kShapeRows) {
         // the shape is chosen for all columns together (grid row c = column c)
         GroupArgs args;

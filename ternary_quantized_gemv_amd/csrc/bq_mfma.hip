@@ -42,10 +42,11 @@
 // and s+2, s+6 (lane half 1): the pairs a_k + a_(k+4) of the tree sit in one
 // lane, and p_k + p_(k+2) across the two halves.
 //
-// A wavefront owns 32 rows (lanes l and l + 32 read the same row's payload,
-// each taking its half's nibbles); a workgroup of four wavefronts stages the
-// activation fragments of a 4-block chunk in LDS (1 KiB per slice and eight
-// columns; zeros included) once for all its rows.
+// A wavefront owns 32 rows and eight columns (lanes l and l + 32 read the
+// same row's payload, each taking its half's nibbles); a workgroup of four
+// wavefronts stages the activation fragments of a 4-block chunk in LDS (1 KiB
+// per slice; zeros included) once for all its rows, the next chunk's quants
+// already loaded into registers while the current chunk runs.
 #include "bq_device.h"
 #include "bq_launch.h"
 
@@ -57,6 +58,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMfChunk = 4;  // blocks per staged chunk
 constexpr int kMfWaves = 4;  // wavefronts per workgroup
+constexpr int kMfCols = 8;   // activation columns per workgroup
 
 // bf16 bits of a small integer (exact: at most 8 significant bits).
 __device__ __forceinline__ uint32_t bf16_of_int(int v)
@@ -64,79 +66,78 @@ __device__ __forceinline__ uint32_t bf16_of_int(int v)
     return __builtin_bit_cast(uint32_t, (float)v) >> 16;
 }
 
-// Lane group (0..7 of the sub-block) of slice s, local lane group g' (0..3).
-__device__ __forceinline__ int mf_group(int s, int gl)
-{
-    return s + (gl == 0 ? 0 : gl == 1 ? 4 : gl == 2 ? 2 : 6);
-}
+// One chunk's activation for the workgroup's columns, loaded into registers
+// ahead of its staging: thread t holds 16 consecutive quants (four lane
+// groups) of one column, and one d1.
+template <int FMT, int QA>
+struct MfChunk {
+    static constexpr int JS = FMT == BQ_Q1_0 ? 4 : 2;     // sub-blocks per block
+    static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;  // weights per block
+    static constexpr int kPieces = kMfChunk * BL / 16;    // 16-quant pieces of one column's chunk
+    static constexpr int kDBlocks = (kMfChunk * BL + QA - 1) / QA;
+    static_assert(kMfCols * kPieces <= kMfWaves * 64, "one piece per thread");
+    static_assert(kDBlocks * kMfCols <= kMfWaves * 64, "one d1 per thread");
+    u32x4 qv;
+    float dv;
+    int nbc;
 
-// Stage one chunk: the nonzero halves of the A fragments of every (block,
-// sub-block, slice, eight columns), the -128 corrections (Q1_0), and d1 per
-// (block, sub-block, column).  The other halves, and the fragments of lanes
-// whose lane group lies in the other half of the slice, stay zero from the
-// kernel's start.  A thread takes 16 consecutive quants of one
-// column (four lane groups) at a time.  Sets *wrap if any quant of the chunk
-// is -128 (Q1_0).
-template <int FMT, int QA, int NC>
-__device__ __forceinline__ void mf_stage(u32x4 *Afr, float *Bias, float *D1s, int *wrap, const GemvDesc &g,
-                                         int64_t ld_q, int64_t ld_d, int c0, int ncols, int k0, int nbc)
-{
-    constexpr int JS = FMT == BQ_Q1_0 ? 4 : 2;     // sub-blocks per block
-    constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;  // weights per block
-    constexpr int MT = NC / 8;
-    constexpr int kPieces = kMfChunk * BL / 16;  // 16-quant pieces of one column's chunk
-    constexpr int kLoads = (NC * kPieces + kMfWaves * 64 - 1) / (kMfWaves * 64);
-    const int npieces = nbc * BL / 16;
-    u32x4 qv[kLoads];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int idx = threadIdx.x + i * kMfWaves * 64, c = idx / kPieces, p = idx % kPieces;
-        const bool ok = c < NC && p < npieces && c0 + c < ncols;
-        qv[i] = ok ? *reinterpret_cast<const u32x4 *>(g.q + (int64_t)(c0 + c) * ld_q + k0 + 16 * p)
-                   : u32x4{0u, 0u, 0u, 0u};
+    __device__ __forceinline__ void load(const GemvDesc &g, int64_t ld_q, int64_t ld_d, int c0, int ncols, int k0,
+                                         int nblocks)
+    {
+        nbc = nblocks;
+        const int c = threadIdx.x / kPieces, p = threadIdx.x % kPieces;
+        const bool ok = c < kMfCols && p < nbc * BL / 16 && c0 + c < ncols;
+        qv = ok ? *reinterpret_cast<const u32x4 *>(g.q + (int64_t)(c0 + c) * ld_q + k0 + 16 * p)
+                : u32x4{0u, 0u, 0u, 0u};
+        // d1 per activation-scale block of the chunk (k0 is a multiple of QA) and column
+        const int dc = threadIdx.x % kMfCols, db = threadIdx.x / kMfCols;
+        const bool dok = db < (nbc * BL + QA - 1) / QA && c0 + dc < ncols;
+        dv = dok ? g.d[(int64_t)(c0 + dc) * ld_d + k0 / QA + db] : 0.0f;
     }
-    bool any = false;
+
+    // The nonzero halves of the A fragments of every (block, sub-block,
+    // slice), the -128 corrections (Q1_0), and d1 per (scale block, column).
+    // The other halves, and the fragments of lanes whose lane group lies in
+    // the other half of the slice, stay zero from the kernel's start.  Sets
+    // *wrap if a quant is -128 (Q1_0).
+    __device__ __forceinline__ void store(u32x4 *Afr, float *Bias, float *D1s, int *wrap) const
+    {
+        const int c = threadIdx.x / kPieces, p = threadIdx.x % kPieces;
+        if (c < kMfCols && p < nbc * BL / 16) {
+            const int b = 16 * p / BL, o = 16 * p % BL, j = o / 32, L0 = (o % 32) / 4;
+            bool any = false;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int idx = threadIdx.x + i * kMfWaves * 64, c = idx / kPieces, p = idx % kPieces;
-        if (!(c < NC && p < npieces && c0 + c < ncols))
-            continue;
-        const int b = 16 * p / BL, o = 16 * p % BL, j = o / 32, L0 = (o % 32) / 4;
-        const int mt = c / 8, c8 = c % 8;
+            for (int e = 0; e < 4; ++e) {
+                // lane group L of slice s = L % 2 sits at local position gl: lane half
+                // kh = gl / 2, fragment half gl % 2 (slice s: groups s, s+4 | s+2, s+6)
+                const int L = L0 + e, sl = L & 1, gl = (L & 2) | ((L >> 2) & 1);
+                const int kh = gl >> 1, m = 8 * (c >> 1) + 4 * kh + 2 * (c & 1) + (gl & 1);
+                const int fi = (b * JS + j) * 2 + sl;
+                int cnt = 0;
+                uint32_t h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // lane group L of slice s = L % 2 sits at local position gl: lane half
-            // kh = gl / 2, fragment half gl % 2 (slice s: groups s, s+4 | s+2, s+6)
-            const int L = L0 + e, sl = L & 1, gl = (L & 2) | ((L >> 2) & 1);
-            const int kh = gl >> 1, m = 8 * (c8 >> 1) + 4 * kh + 2 * (c8 & 1) + (gl & 1);
-            const int fi = ((b * JS + j) * 2 + sl) * MT + mt;
-            const uint32_t qw = qv[i][e];
-            int cnt = 0;
-            uint32_t h[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                int v = (int8_t)(qw >> (8 * k));
-                if (FMT == BQ_Q1_0 && v == -128) {
-                    ++cnt;
-                    v = 0;
+                for (int k = 0; k < 4; ++k) {
+                    int v = (int8_t)(qv[e] >> (8 * k));
+                    if (FMT == BQ_Q1_0 && v == -128) {
+                        ++cnt;
+                        v = 0;
+                    }
+                    h[k] = bf16_of_int(v);
                 }
-                h[k] = bf16_of_int(v);
+                reinterpret_cast<u32x2 *>(&Afr[fi * 64 + 32 * kh + m])[gl & 1] =
+                    u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                if (FMT == BQ_Q1_0) {
+                    Bias[fi * 32 + m] = -128.0f * (float)cnt;
+                    any |= cnt > 0;
+                }
             }
-            reinterpret_cast<u32x2 *>(&Afr[fi * 64 + 32 * kh + m])[gl & 1] =
-                u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-            if (FMT == BQ_Q1_0) {
-                Bias[fi * 32 + m] = -128.0f * (float)cnt;
-                any |= cnt > 0;
-            }
+            if (FMT == BQ_Q1_0 && any)
+                *wrap = 1;
         }
+        if (threadIdx.x < kDBlocks * kMfCols)
+            D1s[threadIdx.x] = dv;
     }
-    for (int i = threadIdx.x; i < nbc * JS * NC; i += kMfWaves * 64) {
-        const int c = i % NC, bj = i / NC, b = bj / JS, j = bj % JS;
-        D1s[i] = c0 + c < ncols ? g.d[(int64_t)(c0 + c) * ld_d + (k0 + b * BL + 32 * j) / QA] : 0.0f;
-    }
-    if (FMT == BQ_Q1_0 && any)
-        *wrap = 1;
-}
+};
 
 // The B fragment (eight weights of this lane's row) of slice s of sub-block
 // j, from the 16-entry tables TB: Q1_0 entry n = four bf16 of nibble n's
@@ -162,19 +163,19 @@ __device__ __forceinline__ bf16x8 mf_bfrag(const char *TB, const uint32_t (&xr)[
     return __builtin_bit_cast(bf16x8, f);
 }
 
-// One block of this wavefront's 32 rows: slice halves S0 .. S0 + HALVES - 1,
-// m-tiles (eight columns each) mg*MTW .. mg*MTW + MTW - 1.  The wavefront's
-// MFMAs form a list of items (half, m-tile, sub-block j) in chain order; the
-// MFMA of item t + 1 is issued before the chain of item t consumes its
-// result, so the matrix core works while the VALU runs the chain.
-template <int FMT, int NC, int HALVES, int MTW, int S0, bool WRAP>
+// One block of this wavefront's 32 rows: slice halves S0 .. S0 + HALVES - 1.
+// The wavefront's MFMAs form a list of items (half, sub-block j) in chain
+// order; the MFMA of item t + 1 is issued before the chain of item t
+// consumes its result, so the matrix core works while the VALU runs the
+// chain.
+template <int FMT, int QA, int HALVES, int S0, bool WRAP>
 __device__ __forceinline__ void mf_block(const u32x4 *__restrict__ Afr, const float *__restrict__ Bias,
                                          const float *__restrict__ D1s, const char *TB, int b, u32x4 w, float d0,
-                                         int mg, uint32_t rot0, uint32_t rot1, f32x16 (&acc)[HALVES][MTW])
+                                         uint32_t rot0, uint32_t rot1, f32x16 (&acc)[HALVES])
 {
     constexpr int JS = FMT == BQ_Q1_0 ? 4 : 2;
-    constexpr int MT = NC / 8;
-    constexpr int T = HALVES * MTW * JS;
+    constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
+    constexpr int T = HALVES * JS;
     const int lane = threadIdx.x & 63;
     // Q1_0: xr[2j] = word j with the nibbles of even lane groups 2h, 2h + 4 at
     // bits 3..6 of bytes 0 and 2, xr[2j+1] the same for odd lane groups.
@@ -187,9 +188,8 @@ __device__ __forceinline__ void mf_block(const u32x4 *__restrict__ Afr, const fl
         xr[2 * i + 1] = __builtin_amdgcn_alignbit(w[i], w[i], rot1);
     }
     auto issue = [&](int t) -> f32x16 {
-        const int j = t % JS, mt = (t / JS) % MTW, s = S0 + t / (JS * MTW);
-        const int gm = mg * MTW + mt;
-        const int fi = ((b * JS + j) * 2 + s) * MT + gm;
+        const int j = t % JS, s = S0 + t / JS;
+        const int fi = (b * JS + j) * 2 + s;
         const bf16x8 bf = mf_bfrag<FMT>(TB, xr, j, s);
         const bf16x8 af = __builtin_bit_cast(bf16x8, Afr[fi * 64 + lane]);
         f32x16 c = {};
@@ -209,11 +209,11 @@ __device__ __forceinline__ void mf_block(const u32x4 *__restrict__ Afr, const fl
     f32x16 cur = issue(0);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const int j = t % JS, mt = (t / JS) % MTW, hs = t / (JS * MTW);
+        const int j = t % JS, hs = t / JS;
         f32x16 nxt = {};
         if (!WRAP && t + 1 < T)
             nxt = issue(t + 1);  // the -128 path (rare) keeps one MFMA in flight
-        const f32x4 *dp = reinterpret_cast<const f32x4 *>(D1s + (b * JS + j) * NC + (mg * MTW + mt) * 8);
+        const f32x4 *dp = reinterpret_cast<const f32x4 *>(D1s + (b * BL + 32 * j) / QA * kMfCols);
         const f32x4 dlo = dp[0], dhi = dp[1];
         const float d1[8] = {dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
 #pragma unroll
@@ -224,7 +224,7 @@ __device__ __forceinline__ void mf_block(const u32x4 *__restrict__ Afr, const fl
         if (j == JS - 1) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                acc[hs][mt][r] = __builtin_fmaf(d0, ab[r], acc[hs][mt][r]);
+                acc[hs][r] = __builtin_fmaf(d0, ab[r], acc[hs][r]);
         }
         if (WRAP) {
             if (t + 1 < T)
@@ -235,22 +235,23 @@ __device__ __forceinline__ void mf_block(const u32x4 *__restrict__ Afr, const fl
     }
 }
 
-// Workgroup id -> (row group of 32-row tiles, column group of NC columns);
-// ids 8 apart share an XCD, so the column groups of one row group read its
-// weights through one L2.
-template <int FMT, int QA, int NC, int HALVES, int MTW>
-__global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == BQ_Q1_0 && HALVES == 2 ? 2 : 3))) void mfma_kernel(
+// Workgroup id -> (row group of 32-row tiles, group of eight columns); ids 8
+// apart share an XCD, so the column groups of one row group read its weights
+// through one L2.  HALVES = 2: a wavefront takes both slice halves of its 32
+// rows, four tiles per workgroup; HALVES = 1: the two halves of a tile in
+// two wavefronts, two tiles per workgroup, joined through LDS at the end.
+template <int FMT, int QA, int HALVES>
+__global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void mfma_kernel(
     GemvDesc g, int64_t ld_q, int64_t ld_d, int ncols, int ntiles, int cgroups)
 {
-    constexpr int JS = FMT == BQ_Q1_0 ? 4 : 2;
-    constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
-    constexpr int MT = NC / 8;
-    constexpr int TASKS = (2 / HALVES) * (MT / MTW);  // wavefronts per 32-row tile
-    constexpr int NTW = kMfWaves / TASKS;             // 32-row tiles per workgroup
-    static_assert(NTW * TASKS == kMfWaves, "whole tiles per workgroup");
-    __shared__ u32x4 Afr[kMfChunk * JS * 2 * MT * 64];
-    __shared__ f32x4 Bias4[FMT == BQ_Q1_0 ? kMfChunk * JS * 2 * MT * 8 : 1];
-    __shared__ f32x4 D1s4[kMfChunk * JS * NC / 4];
+    using Chunk = MfChunk<FMT, QA>;
+    constexpr int JS = Chunk::JS;
+    constexpr int BL = Chunk::BL;
+    constexpr int TASKS = 2 / HALVES;       // wavefronts per 32-row tile
+    constexpr int NTW = kMfWaves / TASKS;   // 32-row tiles per workgroup
+    __shared__ u32x4 Afr[kMfChunk * JS * 2 * 64];
+    __shared__ f32x4 Bias4[FMT == BQ_Q1_0 ? kMfChunk * JS * 2 * 8 : 1];
+    __shared__ f32x4 D1s4[Chunk::kDBlocks * kMfCols / 4];
     float *Bias = reinterpret_cast<float *>(Bias4);
     float *D1s = reinterpret_cast<float *>(D1s4);
     __shared__ u32x2 TB[16];
@@ -260,10 +261,9 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(F
     const int cg = rest % cgroups, rg = (rest / cgroups) * 8 + slot;
     if (rg * NTW >= ntiles)
         return;  // padding workgroup (the grid is a multiple of 8 row groups)
-    const int c0 = cg * NC;
+    const int c0 = cg * kMfCols;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int task = wave % TASKS, nt = rg * NTW + wave / TASKS;
-    const int sh = HALVES == 2 ? 0 : task % 2, mg = task / (2 / HALVES);
+    const int nt = rg * NTW + wave / TASKS, sh = HALVES == 2 ? 0 : wave % 2;
     const bool live = nt < ntiles;
     const int ntc = live ? nt : rg * NTW;  // a wavefront past the last tile repeats the first and stores nothing
     const int kh = lane >> 5;
@@ -274,44 +274,44 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(F
     const uint32_t rot0 = FMT == BQ_Q1_0 ? (8u * kh + 31u) & 31u : 16u * kh;
     const uint32_t rot1 = FMT == BQ_Q1_0 ? 8u * kh + 3u : 16u * kh + 4u;
 
+    Chunk next;
+    next.load(g, ld_q, ld_d, c0, ncols, 0, min(kMfChunk, g.nb));
     if (threadIdx.x < 16) {
         const uint32_t n = threadIdx.x;
-        u32x2 e;
         if (FMT == BQ_Q1_0) {
             uint32_t h[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 h[i] = ((n >> i) & 1) ? 0x3F80u : 0xBF80u;  // bf16 +1 / -1
-            e = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            TB[n] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
         } else {
-            const uint32_t a = bf16_of_int((int)(n & 3) - 1), c = bf16_of_int((int)(n >> 2) - 1);
-            e = u32x2{a | (c << 16), 0u};
             // Q2_0 entries are 4 bytes: entry n at byte 4n
-            reinterpret_cast<uint32_t *>(TB)[n] = e[0];
+            reinterpret_cast<uint32_t *>(TB)[n] = bf16_of_int((int)(n & 3) - 1) | (bf16_of_int((int)(n >> 2) - 1) << 16);
         }
-        if (FMT == BQ_Q1_0)
-            TB[n] = e;
     }
     if (threadIdx.x == 0)
         Wrap[0] = 0;
-    for (int i = threadIdx.x; i < kMfChunk * JS * 2 * MT * 64; i += kMfWaves * 64)
+    for (int i = threadIdx.x; i < kMfChunk * JS * 2 * 64; i += kMfWaves * 64)
         Afr[i] = u32x4{0u, 0u, 0u, 0u};
     if (FMT == BQ_Q1_0)
-        for (int i = threadIdx.x; i < kMfChunk * JS * 2 * MT * 8; i += kMfWaves * 64)
+        for (int i = threadIdx.x; i < kMfChunk * JS * 2 * 8; i += kMfWaves * 64)
             Bias4[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     __syncthreads();
 
-    f32x16 acc[HALVES][MTW];
+    f32x16 acc[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-            acc[h][mt] = f32x16{};
+        acc[h] = f32x16{};
     u32x4 ring[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         ring[i] = bload(wp, lo, (uint32_t)min(i, g.nb - 1) * kStep);
-    u32x4 sc = bload(sp, lo, 0);
+    // the weight scales of a chunk's four blocks: 8 bytes of the lane's 16-byte scale group
+    auto scales4 = [&](int cb) {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             sp, lo + (uint32_t)(cb % 8) * 2, (uint32_t)(cb / 8) * kStep, 2));
+    };
+    u32x2 sc = scales4(0);
 
     for (int cb = 0; cb < g.nb; cb += kMfChunk) {
         const int nbc = min(kMfChunk, g.nb - cb), par = (cb / kMfChunk) & 1;
@@ -319,94 +319,83 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(F
             __syncthreads();  // every wavefront is done with the previous chunk
         if (threadIdx.x == 0)
             Wrap[par ^ 1] = 0;
-        mf_stage<FMT, QA, NC>(Afr, Bias, D1s, &Wrap[par], g, ld_q, ld_d, c0, ncols, cb * BL, nbc);
+        next.store(Afr, Bias, D1s, &Wrap[par]);
         __syncthreads();
+        if (cb + kMfChunk < g.nb)
+            next.load(g, ld_q, ld_d, c0, ncols, (cb + kMfChunk) * BL, min(kMfChunk, g.nb - cb - kMfChunk));
         const bool wrap = __builtin_amdgcn_readfirstlane(Wrap[par]) != 0;
-        const u32x4 sc_next = bload(sp, lo, (uint32_t)min((cb + kMfChunk) / 8, g.ng - 1) * kStep);
+        const u32x2 sc_next = scales4(min(cb + kMfChunk, (g.nb - 1) & ~(kMfChunk - 1)));
 #pragma unroll
         for (int i = 0; i < kMfChunk; ++i) {
             const u32x4 w = ring[i];
             ring[i] = bload(wp, lo, (uint32_t)min(cb + i + 4, g.nb - 1) * kStep);
             if (i < nbc) {
-                float d0 = scale_of(sc, cb + i);
+                float d0 = f16_bits_to_f32((i & 1) ? (sc[i >> 1] >> 16) : (sc[i >> 1] & 0xFFFFu));
                 asm volatile("" : "+v"(d0));
                 const char *tb = reinterpret_cast<const char *>(TB);
                 if (FMT == BQ_Q1_0 && wrap) {
                     if (sh == 0)
-                        mf_block<FMT, NC, HALVES, MTW, 0, true>(Afr, Bias, D1s, tb, i, w, d0, mg, rot0, rot1, acc);
+                        mf_block<FMT, QA, HALVES, 0, true>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc);
                     else
-                        mf_block<FMT, NC, HALVES, MTW, 1, true>(Afr, Bias, D1s, tb, i, w, d0, mg, rot0, rot1, acc);
+                        mf_block<FMT, QA, HALVES, 1, true>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc);
                 } else {
                     if (sh == 0)
-                        mf_block<FMT, NC, HALVES, MTW, 0, false>(Afr, Bias, D1s, tb, i, w, d0, mg, rot0, rot1, acc);
+                        mf_block<FMT, QA, HALVES, 0, false>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc);
                     else
-                        mf_block<FMT, NC, HALVES, MTW, 1, false>(Afr, Bias, D1s, tb, i, w, d0, mg, rot0, rot1, acc);
+                        mf_block<FMT, QA, HALVES, 1, false>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc);
                 }
             }
         }
-        if ((cb + kMfChunk) % 8 == 0)
-            sc = sc_next;
+        sc = sc_next;
     }
 
-    // The tree: in lane half h, registers 2k and 2k + 1 of a slice half s hold
-    // lane groups s + 2h and s + 2h + 4 of column k of the m-tile.
-    float P[HALVES][MTW][8];
+    // The tree: in lane half h, registers 2k and 2k + 1 of slice half s hold
+    // lane groups s + 2h and s + 2h + 4 of column k.
+    float P[HALVES][kMfCols];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h)
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float p = acc[h][mt][2 * k] + acc[h][mt][2 * k + 1];  // a_(s+2h) + a_(s+2h+4)
-                const float o = __shfl_xor(p, 32, 64);
-                P[h][mt][k] = kh == 0 ? p + o : o + p;  // p_s + p_(s+2)
-            }
+        for (int k = 0; k < kMfCols; ++k) {
+            const float p = acc[h][2 * k] + acc[h][2 * k + 1];  // a_(s+2h) + a_(s+2h+4)
+            const float o = __shfl_xor(p, 32, 64);
+            P[h][k] = kh == 0 ? p + o : o + p;  // p_s + p_(s+2)
+        }
     const int row = nt * 32 + (lane & 31);
     if (HALVES == 2) {
         if (live && kh == 0 && row < g.rows) {
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c = c0 + (mg * MTW + mt) * 8 + k;
-                    if (c < ncols)
-                        g.y[(int64_t)c * g.rows + row] = P[0][mt][k] + P[1][mt][k];
-                }
+            for (int k = 0; k < kMfCols; ++k)
+                if (c0 + k < ncols)
+                    g.y[(int64_t)(c0 + k) * g.rows + row] = P[0][k] + P[1][k];
         }
     } else {
         // the wavefront of slice half 1 hands its partial to that of half 0 through LDS
         float *X = reinterpret_cast<float *>(Afr);
         __syncthreads();
-        const int slot2 = (wave / TASKS) * (MT / MTW) + mg;  // (tile, m-group) of this wavefront
+        const int t2 = wave / TASKS;  // tile of this wavefront within the workgroup
         if (sh == 1 && kh == 0) {
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    X[((slot2 * MTW + mt) * 8 + k) * 32 + (lane & 31)] = P[0][mt][k];
+            for (int k = 0; k < kMfCols; ++k)
+                X[(t2 * kMfCols + k) * 32 + (lane & 31)] = P[0][k];
         }
         __syncthreads();
         if (sh == 0 && live && kh == 0 && row < g.rows) {
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c = c0 + (mg * MTW + mt) * 8 + k;
-                    if (c < ncols)
-                        g.y[(int64_t)c * g.rows + row] = P[0][mt][k] + X[((slot2 * MTW + mt) * 8 + k) * 32 + (lane & 31)];
-                }
+            for (int k = 0; k < kMfCols; ++k)
+                if (c0 + k < ncols)
+                    g.y[(int64_t)(c0 + k) * g.rows + row] = P[0][k] + X[(t2 * kMfCols + k) * 32 + (lane & 31)];
         }
     }
 }
 
-template <int FMT, int NC, int HALVES, int MTW>
+template <int FMT, int HALVES>
 static void mfma_shape(int qa, dim3 grid, hipStream_t st, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols,
                        int ntiles, int cgroups)
 {
     switch (qa) {
-    case 32: hipLaunchKernelGGL((mfma_kernel<FMT, 32, NC, HALVES, MTW>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
-    case 64: hipLaunchKernelGGL((mfma_kernel<FMT, 64, NC, HALVES, MTW>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
-    default: hipLaunchKernelGGL((mfma_kernel<FMT, 128, NC, HALVES, MTW>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
+    case 32: hipLaunchKernelGGL((mfma_kernel<FMT, 32, HALVES>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
+    case 64: hipLaunchKernelGGL((mfma_kernel<FMT, 64, HALVES>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
+    default: hipLaunchKernelGGL((mfma_kernel<FMT, 128, HALVES>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
     }
 }
 
@@ -414,25 +403,15 @@ template <int FMT>
 static hipError_t mfma_fmt(int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols,
                            hipStream_t st)
 {
-    const int nc = ncols > 8 ? 16 : 8;
-    const int cgroups = (ncols + nc - 1) / nc;
+    const int cgroups = (ncols + kMfCols - 1) / kMfCols;
     const int ntiles = (g.rows + 31) / 32;
-    // wavefronts per 32-row tile: one per eight columns (shape 0), or one per
-    // eight columns and slice half (shape 1)
-    const int ntw = kMfWaves / ((shape == 0 ? 1 : 2) * (nc / 8));
+    const int ntw = shape == 0 ? kMfWaves : kMfWaves / 2;  // 32-row tiles per workgroup
     const int rgroups = (ntiles + ntw - 1) / ntw;
     const dim3 grid((unsigned)(((rgroups + 7) / 8) * 8 * cgroups));
-    if (nc == 8) {
-        if (shape == 0)
-            mfma_shape<FMT, 8, 2, 1>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
-        else
-            mfma_shape<FMT, 8, 1, 1>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
-    } else {
-        if (shape == 0)
-            mfma_shape<FMT, 16, 2, 1>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
-        else
-            mfma_shape<FMT, 16, 1, 1>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
-    }
+    if (shape == 0)
+        mfma_shape<FMT, 2>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
+    else
+        mfma_shape<FMT, 1>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
     return hipGetLastError();
 }
 

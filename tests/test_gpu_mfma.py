@@ -2,10 +2,12 @@
 (bq_set_batch_path(BQ_BATCH_MFMA)): every output bit-identical to the oracle.
 
 Cases cover both formats, both workgroup shapes of the kernel (slice halves
-in one wavefront on tall matrices, in two on short ones), 8 and 16 columns
-per workgroup (ragged column counts pad a group), every qa, the -128 regimes
-(Q1_0's int8 wrap goes through the MFMA accumulator input), rows not a
-multiple of 32, and block counts that leave a partial 4-block chunk."""
+in one wavefront on matrices of more than 1024 row tiles, in two below),
+one and two groups of eight columns (a ragged count pads the last group),
+every qa, the -128 regimes (Q1_0's int8 wrap goes through the MFMA
+accumulator input), rows not a multiple of 32, and block counts that leave a
+partial 4-block chunk.  The table kernels are covered by test_gpu_parity.py,
+which forces them."""
 import numpy as np
 import pytest
 
@@ -45,21 +47,21 @@ def _inputs(fmt, rows, cols, ncols, qa, regime, seed):
 
 
 CASES = [
-    # short matrices: each slice half in its own wavefront
+    # up to 1024 row tiles: each slice half in its own wavefront
     (Q1, 4096, 4096, 8, 128, "quant"),
     (Q1, 4100, 1152, 16, 32, "raw"),       # ragged rows, 9 blocks (a chunk of 1)
-    (Q1, 12288, 640, 12, 64, "mixed"),     # 12 columns in a group of 16
-    (Q1, 1000, 128, 9, 128, "raw"),        # one block per row
+    (Q1, 12288, 640, 12, 64, "mixed"),     # two column groups, the second of four
+    (Q1, 1000, 128, 9, 128, "raw"),        # one block per row; a group of one column
     (Q2, 4096, 4096, 16, 128, "quant"),
     (Q2, 3001, 320, 8, 64, "raw"),         # 5 blocks
-    (Q2, 12288, 576, 11, 32, "quant"),
-    # tall matrices: both slice halves in one wavefront
+    (Q2, 40001, 576, 11, 32, "quant"),     # 626 ragged tiles
+    # more than 1024 row tiles: both slice halves in one wavefront
     (Q1, 65600, 640, 8, 128, "quant"),
-    (Q1, 40001, 1152, 16, 64, "raw"),
+    (Q1, 66000, 1152, 16, 64, "raw"),
     (Q1, 65601, 384, 13, 32, "mixed"),
     (Q2, 65600, 448, 8, 32, "raw"),
-    (Q2, 40000, 4096, 16, 128, "quant"),
-    # two column groups (at most 16 columns per call: 16 = one group; 8 < 16)
+    (Q2, 65700, 4096, 16, 128, "quant"),
+    (Q2, 70000, 320, 10, 64, "raw"),
 ]
 
 
@@ -97,10 +99,12 @@ def test_mfma_q2_code3(mfma_path):
     assert_parity(matvec_gpu(Q2, w, rows, cols, q, d, qa), y_ref, "mfma Q2_0 code 3")
 
 
-def test_batch_paths_agree():
-    """Both small-batch paths and the automatic choice give the same bits."""
+@pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 20000, 16), (Q1, 70000, 8), (Q2, 20000, 12), (Q2, 70000, 16)])
+def test_batch_paths_agree(fmt, rows, ncols):
+    """Both small-batch paths and the automatic choice give the same bits,
+    and the same as the oracle."""
     bq = bqmod()
-    fmt, rows, cols, ncols, qa = Q1, 20000, 1024, 16, 128
+    cols, qa = 1024, 128
     w, q, d = _inputs(fmt, rows, cols, ncols, qa, "quant", 67)
     ys = []
     for path in (bq.BQ_BATCH_TABLES, bq.BQ_BATCH_MFMA, bq.BQ_BATCH_AUTO):
@@ -109,5 +113,7 @@ def test_batch_paths_agree():
             ys.append(matvec_gpu(fmt, w, rows, cols, q, d, qa))
         finally:
             bq.bq_set_batch_path(prev)
-    assert_parity(ys[1], ys[0], "mfma vs tables")
-    assert_parity(ys[2], ys[0], "auto vs tables")
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    assert_parity(ys[0], y_ref, "tables")
+    assert_parity(ys[1], y_ref, "mfma")
+    assert_parity(ys[2], y_ref, "auto")

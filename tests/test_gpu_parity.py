@@ -3,7 +3,9 @@
 The bar is bit-exact equality for every output element: the order of every
 rounding is fixed (bankML "gpu/ -- the video-card component", section
 "kernels.rs -- the Q1_0 kernels"), so exactly one result is correct.  The
-scaled error max|gpu - oracle| / max|oracle| is reported beside it.
+scaled error max|gpu - oracle| / max|oracle| is reported beside it.  Several
+columns run on the table kernels here (bq_set_batch_path(BQ_BATCH_TABLES));
+the matrix-core path has its own cases in test_gpu_mfma.py.
 """
 import numpy as np
 import pytest
@@ -25,8 +27,12 @@ def _gpu():
     t = torch()
     if not t.cuda.is_available():
         pytest.fail("no GPU visible: the gpu tests need an MI355X")
-    import ternary_quantized_gemv_amd  # noqa: F401  (fails loudly if libbq.so is missing)
-    yield
+    import ternary_quantized_gemv_amd as bq  # fails loudly if libbq.so is missing
+    prev = bq.bq_set_batch_path(bq.BQ_BATCH_TABLES)
+    try:
+        yield
+    finally:
+        bq.bq_set_batch_path(prev)
 
 
 # --------------------------------------------------------------- witnesses
