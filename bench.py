@@ -325,7 +325,9 @@ def bench_batch(args):
                     bq.bq_set_batch_path(prev)
             us = times["auto"]
             nbytes = wbytes + ncols * (cols + 4 * (cols // 128) + 4 * rows)
-            flops = rows * cols * ncols * 0.625  # 0.3125 f32 multiply-adds per weight per column
+            # f32 chain operations per weight per column: Q1_0 0.3125 (5 per lane group of a
+            # 128-weight block: d1*s, three fmas, the block's fma), Q2_0 0.375 (3 per 64 weights)
+            flops = rows * cols * ncols * (0.625 if fmt == bq.BQ_Q1_0 else 0.75)
             hbm_us = nbytes / (HBM_PEAK_GBS * 1e3)
             valu_us = flops / (VALU_PEAK_TFLOPS * 1e6)
             bound = "hbm" if hbm_us >= valu_us else "alu"

@@ -85,8 +85,11 @@ struct MfChunk {
                                          int nblocks)
     {
         nbc = nblocks;
-        const int c = threadIdx.x / kPieces, p = threadIdx.x % kPieces;
-        const bool ok = c < kMfCols && p < nbc * BL / 16 && c0 + c < ncols;
+        // the column varies fastest across threads: the fragment stores of a
+        // wavefront then spread over the LDS banks (eight consecutive pieces
+        // of a column are still one 128-byte run of its quants)
+        const int c = threadIdx.x % kMfCols, p = threadIdx.x / kMfCols;
+        const bool ok = p < kPieces && p < nbc * BL / 16 && c0 + c < ncols;
         qv = ok ? *reinterpret_cast<const u32x4 *>(g.q + (int64_t)(c0 + c) * ld_q + k0 + 16 * p)
                 : u32x4{0u, 0u, 0u, 0u};
         // d1 per activation-scale block of the chunk (k0 is a multiple of QA) and column
@@ -102,8 +105,8 @@ struct MfChunk {
     // *wrap if a quant is -128 (Q1_0).
     __device__ __forceinline__ void store(u32x4 *Afr, float *Bias, float *D1s, int *wrap) const
     {
-        const int c = threadIdx.x / kPieces, p = threadIdx.x % kPieces;
-        if (c < kMfCols && p < nbc * BL / 16) {
+        const int c = threadIdx.x % kMfCols, p = threadIdx.x / kMfCols;
+        if (p < kPieces && p < nbc * BL / 16) {
             const int b = 16 * p / BL, o = 16 * p % BL, j = o / 32, L0 = (o % 32) / 4;
             bool any = false;
 #pragma unroll
