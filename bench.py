@@ -473,6 +473,17 @@ def main():
     def event_pairs(n):
         return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
+    # the step, back to back, for a fixed time: the GPU's clocks ramp over
+    # the first ~100 launches, so every timed leg below starts settled
+    def settle(seconds):
+        t_settle, n = time.perf_counter(), 0
+        while time.perf_counter() - t_settle < seconds:
+            for _ in range(50):
+                sw.run()
+            n += 50
+            torch.cuda.synchronize()
+        return n
+
     # ---- context legs, run BEFORE the timed loop so that the headline is
     # taken on a GPU that has been busy for a while (clocks settled)
     floor = read_floor()
@@ -480,6 +491,7 @@ def main():
     sw.run()
     torch.cuda.synchronize()
     y_ref = sw.y.cpu().numpy()
+    settle_legs = settle(args.settle)
 
     # the sweep with the 256 MB last-level cache flushed before each launch (a
     # streaming read of 512 MB between launches, outside the events; a read
@@ -536,15 +548,8 @@ def main():
         except Exception as e:  # the headline line must print regardless
             fused = {"error": f"{type(e).__name__}: {e}"}
 
-    # settle: the step, back to back, for a fixed time (the GPU's clocks ramp
-    # over the first ~100 launches), then the W warm-up steps the command asks for
-    t_settle = time.perf_counter()
-    settle_steps = 0
-    while time.perf_counter() - t_settle < args.settle:
-        for _ in range(50):
-            sw.run()
-        settle_steps += 50
-        torch.cuda.synchronize()
+    # settle again, then the W warm-up steps the command asks for
+    settle_steps = settle(args.settle)
     for _ in range(args.warmup):
         sw.run()
     torch.cuda.synchronize()
@@ -635,10 +640,11 @@ def main():
             "quantize_with_gaps_ms": round(quant_ms, 5),
             "sweep_ms_cold_cache": cold,
         },
-        "before_timing": {"settle_s": args.settle, "settle_steps": settle_steps,
-                          "how": "the context legs (floor, cold-cache and one-launch sweeps), then the step back "
-                                 "to back for settle_s, then the W warm-up steps; outputs of the timed steps "
-                                 "equal the first step's bit for bit: " + str(same_as_first)},
+        "before_timing": {"settle_s": args.settle, "settle_steps": [settle_legs, settle_steps],
+                          "how": "the floor read, the step back to back for settle_s, the context legs "
+                                 "(cold-cache and one-launch sweeps), the step back to back for settle_s again, "
+                                 "then the W warm-up steps; outputs of the timed steps equal the first step's "
+                                 "bit for bit: " + str(same_as_first)},
         "roofline": {
             "bound": "hbm",
             "kernel": "bq::sweep_kernel",
