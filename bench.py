@@ -296,7 +296,7 @@ def bench_gemv(args):
 
 def bench_batch(args):
     """Small batch: us per call of bq_q1_0_matvec / bq_q2_0_matvec with N
-    activation columns, weights cycled from ~1.1 GB of copies; for N >= 8 the
+    activation columns, weights cycled from ~1.1 GB of copies; for N >= 2 the
     table and matrix-core paths are each timed beside the automatic choice."""
     import torch
     import ternary_quantized_gemv_amd as bq
@@ -313,7 +313,7 @@ def bench_batch(args):
             y = torch.empty(ncols * rows, device="cuda")
             reps = max(args.steps // 4, 2 * len(ws))
             paths = {}
-            if ncols >= 8:
+            if ncols >= 2:
                 paths.update({"tables": bq.BQ_BATCH_TABLES, "mfma": bq.BQ_BATCH_MFMA})
             paths["auto"] = bq.BQ_BATCH_AUTO  # timed last, after both forced paths
             times = {}
@@ -335,7 +335,7 @@ def bench_batch(args):
                    "GB_s": round(nbytes / us / 1e3, 1), "TFLOP_s": round(flops / us / 1e6, 2),
                    "bound": bound, "roofline_us": round(max(hbm_us, valu_us), 2),
                    "frac": round(max(hbm_us, valu_us) / us, 4)}
-            if ncols >= 8:
+            if ncols >= 2:
                 row["us_tables"] = round(times["tables"], 2)
                 row["us_mfma"] = round(times["mfma"], 2)
             rows_out.append(row)

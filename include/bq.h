@@ -202,11 +202,11 @@ int bq_q1_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
 int bq_q2_0_matvec(const bq_weights *w, const bq_act *a, float *y, bq_stream s);
 
 /* Which kernels compute the lane-group sums of bq_q1_0_matvec /
- * bq_q2_0_matvec for 8 to 16 activation columns: BQ_BATCH_AUTO (the path
- * measured faster for the shape), BQ_BATCH_TABLES (LDS lookup tables of the
- * activation, the VALU path) or BQ_BATCH_MFMA (exact integer sums on the
- * matrix cores, as products with a block-diagonal activation matrix; the f32
- * chain of the order above stays on the VALU).  Both paths give the same
+ * bq_q2_0_matvec for 2 to 16 activation columns: BQ_BATCH_AUTO (the path
+ * measured faster for the shape and column count), BQ_BATCH_TABLES (LDS
+ * lookup tables of the activation, the VALU path) or BQ_BATCH_MFMA (exact
+ * integer sums on the matrix cores, as products with a block-diagonal
+ * activation matrix; the f32 chain of the order above stays on the VALU).  Both paths give the same
  * bits; the choice affects only speed.  The sums are the integer part of
  * bankML "gpu/ -- the video-card component", section "kernels.rs -- the
  * Q1_0 kernels" (exact lane-group sums before the chain).  Process-wide,

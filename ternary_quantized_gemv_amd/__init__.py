@@ -301,7 +301,7 @@ def bq_q2_0_matvec(w: Weights, a: Act, y, stream=None) -> None:
 
 
 def bq_set_batch_path(path: int) -> int:
-    """Kernels for 8..16 activation columns: BQ_BATCH_AUTO, BQ_BATCH_TABLES or
+    """Kernels for 2..16 activation columns: BQ_BATCH_AUTO, BQ_BATCH_TABLES or
     BQ_BATCH_MFMA (process-wide); returns the previous setting."""
     prev = lib.bq_set_batch_path(int(path))
     if prev < 0:

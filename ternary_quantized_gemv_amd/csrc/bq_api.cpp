@@ -62,34 +62,42 @@ static int splitcols_shape(int tiles, int ncols)
     return wgs(2) <= 512 ? 2 : 3;
 }
 
-// The small batch of at least kMfmaMinCols columns on the matrix cores
-// (launch_mfma, eight columns per workgroup) or on the table kernels above.
-// BQ_BATCH_AUTO takes the matrix cores where they measured faster (MI355X,
-// us, event-timed replays of ~1 GB of weight copies, tables -> matrix cores):
-//   Q2_0 151936x4096  N = 8 / 16   178.0 / 328.7 -> 99.6 / 170.9
-//   Q2_0 12288x4096   N = 8 / 16   28.9 / 34.1 -> 27.3 / 32.2
-//   Q1_0 151936x4096  N = 8 / 16   107.1 / 193.1 -> 98.8 / 180.7
-//   Q1_0 12288x4096   N = 8 / 16   17.9 / 20.7 -> 21.5 / 29.2 (tables kept)
-// so Q2_0 from 8 columns on, Q1_0 for whole groups of eight columns on
-// matrices of more than kSplitMaxTiles tiles.  The other settings force a path.
-constexpr int kMfmaMinCols = 8;
+// The small batch on the matrix cores (launch_mfma) or on the table kernels
+// above.  Shapes of the matrix-core kernel: 0, eight columns per workgroup,
+// both slice halves of 32 rows in one wavefront (measured faster on tall
+// matrices); 1, eight columns, the two halves in two wavefronts (twice the
+// wavefronts, for matrices of up to kSplitMaxTiles tiles); 2, four columns,
+// whole sub-blocks (two accumulating MFMAs each; no padded outputs below
+// five columns).  BQ_BATCH_AUTO takes the matrix cores where they measured
+// faster (MI355X, us, event-timed replays of ~1 GB of weight copies; tables
+// / four-column form / eight-column form):
+//   Q2_0 151936x4096  N = 2 / 4 / 6      88.0 / 110.8 / 177.3, 83.9 / 76.7 / 127.3, 98.3 / 88.7 / 91.0
+//                     N = 8 / 12 / 16    177.5 / 263.3 / 328.7, -, 93.1 / 161.4 / 165.8
+//   Q1_0 151936x4096  N = 2 / 4 / 6      46.2 / 68.8 / 107.9, 72.6 / 67.2 / 111.3, 98.1 / 93.6 / 92.4
+//                     N = 8 / 12 / 16    106.4 / 153.1 / 192.3, -, 92.5 / 165.9 / 168.4
+//   Q2_0 12288x4096   N = 8 / 16         28.9 / 34.1, -, 27.3 / 32.2 (shape 1)
+//   Q1_0 12288x4096   N = 8 / 16         17.9 / 20.7, -, 21.5 / 29.2 (shape 1; tables kept)
+// so: Q2_0 on more than kSplitMaxTiles tiles from 2 columns on (four-column
+// form up to 4), on fewer tiles from 8; Q1_0 on more than kSplitMaxTiles
+// tiles for 5-8 and 13-16 columns (the tables' cost grows by groups of
+// four columns, the matrix cores' by groups of eight).  Returns the shape,
+// or -1 for the tables.  BQ_BATCH_MFMA takes the matrix cores from 2
+// columns on, BQ_BATCH_TABLES never.
 static std::atomic<int> g_batch_path{BQ_BATCH_AUTO};
 
-static bool use_mfma(int fmt, int tiles, int ncols)
+static int mfma_choice(int fmt, int tiles, int ncols)
 {
-    if (ncols < kMfmaMinCols)
-        return false;
+    const bool tall = tiles > kSplitMaxTiles;
+    const int shape = ncols <= 4 ? 2 : tall ? 0 : 1;
+    if (ncols < 2)
+        return -1;
     const int path = g_batch_path.load(std::memory_order_relaxed);
     if (path != BQ_BATCH_AUTO)
-        return path == BQ_BATCH_MFMA;
-    return fmt == BQ_Q2_0 || (tiles > kSplitMaxTiles && ncols % 8 == 0);
+        return path == BQ_BATCH_MFMA ? shape : -1;
+    if (fmt == BQ_Q2_0)
+        return tall || ncols >= 8 ? shape : -1;
+    return tall && ((ncols >= 5 && ncols <= 8) || ncols >= 13) ? shape : -1;
 }
-
-// Shape of the matrix-core kernel: both slice halves of 32 rows in one
-// wavefront on tall matrices (shape 0, measured faster there), the two halves
-// in two wavefronts on matrices of up to kSplitMaxTiles tiles (shape 1: twice
-// the wavefronts where a wavefront per 32 rows cannot fill the GPU).
-static int mfma_shape(int tiles) { return tiles > kSplitMaxTiles ? 0 : 1; }
 
 // ------------------------------------------------------------ validation
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -178,8 +186,9 @@ static int launch_matvec(const char *fn, const bq_weights *w, const bq_act *a, f
     const int tiles = (int)tiles_of(w->rows);
     hipStream_t st = static_cast<hipStream_t>(s);
     hipError_t e;
-    if (use_mfma(FMT, tiles, a->ncols)) {
-        e = launch_mfma(FMT, mfma_shape(tiles), a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
+    const int mshape = mfma_choice(FMT, tiles, a->ncols);
+    if (mshape >= 0) {
+        e = launch_mfma(FMT, mshape, a->qa, g, a->ld_q, a->ld_d, a->ncols, st);
     } else if (group_shape((int64_t)tiles * a->ncols) != kShapeRows) {
         // the shape is chosen for all columns together (grid row c = column c)
         GroupArgs args;

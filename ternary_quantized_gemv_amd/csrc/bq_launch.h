@@ -62,10 +62,11 @@ constexpr int kSplitColsShapes = 4;
 constexpr int kSplitColsTpw[kSplitColsShapes] = {1, 2, 3, 4};
 hipError_t launch_splitcols(int fmt, int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int tiles,
                             int ncols, hipStream_t st);
-// launch_mfma: 8 to 16 columns, eight per workgroup, the lane-group sums on
-// the matrix cores (bq_mfma.hip); a wavefront takes 32 rows, all slices of
+// launch_mfma: 2 to 16 columns, the lane-group sums on the matrix cores
+// (bq_mfma.hip); a wavefront takes 32 rows and eight columns, all slices of
 // each sub-block (shape 0) or one of the two slice halves (shape 1, twice
-// the wavefronts for matrices of few rows).
+// the wavefronts for matrices of few rows), or 32 rows and four columns,
+// whole sub-blocks (shape 2).
 hipError_t launch_mfma(int fmt, int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols,
                        hipStream_t st);
 // launch_group: a group of products sharing one f32 activation, quantized

@@ -66,17 +66,17 @@ __device__ __forceinline__ uint32_t bf16_of_int(int v)
     return __builtin_bit_cast(uint32_t, (float)v) >> 16;
 }
 
-// One chunk's activation for the workgroup's columns, loaded into registers
-// ahead of its staging: thread t holds 16 consecutive quants (four lane
-// groups) of one column, and one d1.
-template <int FMT, int QA>
+// One chunk's activation for the workgroup's NC columns (8, or 4 in the
+// whole-sub-block form), loaded into registers ahead of its staging: thread t
+// holds 16 consecutive quants (four lane groups) of one column, and one d1.
+template <int FMT, int QA, int NC>
 struct MfChunk {
     static constexpr int JS = FMT == BQ_Q1_0 ? 4 : 2;     // sub-blocks per block
     static constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;  // weights per block
     static constexpr int kPieces = kMfChunk * BL / 16;    // 16-quant pieces of one column's chunk
     static constexpr int kDBlocks = (kMfChunk * BL + QA - 1) / QA;
-    static_assert(kMfCols * kPieces <= kMfWaves * 64, "one piece per thread");
-    static_assert(kDBlocks * kMfCols <= kMfWaves * 64, "one d1 per thread");
+    static_assert(NC * kPieces <= kMfWaves * 64, "one piece per thread");
+    static_assert(kDBlocks * NC <= kMfWaves * 64, "one d1 per thread");
     u32x4 qv;
     float dv;
     int nbc;
@@ -88,12 +88,12 @@ struct MfChunk {
         // the column varies fastest across threads: the fragment stores of a
         // wavefront then spread over the LDS banks (eight consecutive pieces
         // of a column are still one 128-byte run of its quants)
-        const int c = threadIdx.x % kMfCols, p = threadIdx.x / kMfCols;
+        const int c = threadIdx.x % NC, p = threadIdx.x / NC;
         const bool ok = p < kPieces && p < nbc * BL / 16 && c0 + c < ncols;
         qv = ok ? *reinterpret_cast<const u32x4 *>(g.q + (int64_t)(c0 + c) * ld_q + k0 + 16 * p)
                 : u32x4{0u, 0u, 0u, 0u};
         // d1 per activation-scale block of the chunk (k0 is a multiple of QA) and column
-        const int dc = threadIdx.x % kMfCols, db = threadIdx.x / kMfCols;
+        const int dc = threadIdx.x % NC, db = threadIdx.x / NC;
         const bool dok = db < (nbc * BL + QA - 1) / QA && c0 + dc < ncols;
         dv = dok ? g.d[(int64_t)(c0 + dc) * ld_d + k0 / QA + db] : 0.0f;
     }
@@ -103,19 +103,41 @@ struct MfChunk {
     // The other halves, and the fragments of lanes whose lane group lies in
     // the other half of the slice, stay zero from the kernel's start.  Sets
     // *wrap if a quant is -128 (Q1_0).
+    //
+    // NC = 8: fragment (block, sub-block j, slice s) holds lane groups s, s+4
+    // (lane half 0) and s+2, s+6 (half 1) of eight columns; element m of a
+    // result column is (lane group position 2((m/4)%2) + m%2, column
+    // 2(m/8) + (m%4)/2).  NC = 4: fragments (block, j, t) for the two
+    // 16-weight halves t of sub-block j, accumulated into one result whose
+    // element m is (lane group m % 8, column m / 8); the correction of a
+    // (block, j) goes in with t = 0.
     __device__ __forceinline__ void store(u32x4 *Afr, float *Bias, float *D1s, int *wrap) const
     {
-        const int c = threadIdx.x % kMfCols, p = threadIdx.x / kMfCols;
+        const int c = threadIdx.x % NC, p = threadIdx.x / NC;
         if (p < kPieces && p < nbc * BL / 16) {
             const int b = 16 * p / BL, o = 16 * p % BL, j = o / 32, L0 = (o % 32) / 4;
             bool any = false;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // lane group L of slice s = L % 2 sits at local position gl: lane half
-                // kh = gl / 2, fragment half gl % 2 (slice s: groups s, s+4 | s+2, s+6)
-                const int L = L0 + e, sl = L & 1, gl = (L & 2) | ((L >> 2) & 1);
-                const int kh = gl >> 1, m = 8 * (c >> 1) + 4 * kh + 2 * (c & 1) + (gl & 1);
-                const int fi = (b * JS + j) * 2 + sl;
+                const int L = L0 + e;
+                int kh, m, fi, half, bi;
+                if (NC == 8) {
+                    // lane group L of slice s = L % 2 sits at local position gl: lane half
+                    // kh = gl / 2, fragment half gl % 2 (slice s: groups s, s+4 | s+2, s+6)
+                    const int sl = L & 1, gl = (L & 2) | ((L >> 2) & 1);
+                    kh = gl >> 1;
+                    m = 8 * (c >> 1) + 4 * kh + 2 * (c & 1) + (gl & 1);
+                    fi = (b * JS + j) * 2 + sl;
+                    half = gl & 1;
+                    bi = fi * 32 + m;
+                } else {
+                    // weight k of half t = L / 4 in slot k % 8 of lane half (k % 16) / 8
+                    kh = (L & 3) >> 1;
+                    m = 8 * c + L;
+                    fi = (b * JS + j) * 2 + (L >> 2);
+                    half = L & 1;
+                    bi = (b * JS + j) * 32 + m;
+                }
                 int cnt = 0;
                 uint32_t h[4];
 #pragma unroll
@@ -127,17 +149,17 @@ struct MfChunk {
                     }
                     h[k] = bf16_of_int(v);
                 }
-                reinterpret_cast<u32x2 *>(&Afr[fi * 64 + 32 * kh + m])[gl & 1] =
+                reinterpret_cast<u32x2 *>(&Afr[fi * 64 + 32 * kh + m])[half] =
                     u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
                 if (FMT == BQ_Q1_0) {
-                    Bias[fi * 32 + m] = -128.0f * (float)cnt;
+                    Bias[bi] = -128.0f * (float)cnt;
                     any |= cnt > 0;
                 }
             }
             if (FMT == BQ_Q1_0 && any)
                 *wrap = 1;
         }
-        if (threadIdx.x < kDBlocks * kMfCols)
+        if (threadIdx.x < kDBlocks * NC)
             D1s[threadIdx.x] = dv;
     }
 };
@@ -164,6 +186,87 @@ __device__ __forceinline__ bf16x8 mf_bfrag(const char *TB, const uint32_t (&xr)[
         f[3] = *reinterpret_cast<const uint32_t *>(TB + nib4(xr[4 * j + 3], s));
     }
     return __builtin_bit_cast(bf16x8, f);
+}
+
+// The B fragment of 16-weight half t of sub-block j in the whole-sub-block
+// form: lane groups 4t + 2h (slots 0-3) and 4t + 2h + 1 (slots 4-7).
+template <int FMT>
+__device__ __forceinline__ bf16x8 mf_bfrag4(const char *TB, const uint32_t (&xr)[8], int j, int t)
+{
+    u32x4 f;
+    if (FMT == BQ_Q1_0) {
+        // even nibble 4t + 2h of word j at bits 3..6 of byte 2t of xr[2j], the odd one of xr[2j + 1]
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(TB + ((xr[2 * j] >> (16 * t)) & 0x78u));
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(TB + ((xr[2 * j + 1] >> (16 * t)) & 0x78u));
+        f = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+        // bytes 2h and 2h + 1 of word 2j + t, moved to bytes 0 and 1 (low and high nibbles)
+        const int m = 2 * j + t;
+        f[0] = *reinterpret_cast<const uint32_t *>(TB + nib4(xr[2 * m], 0));
+        f[1] = *reinterpret_cast<const uint32_t *>(TB + nib4(xr[2 * m + 1], 0));
+        f[2] = *reinterpret_cast<const uint32_t *>(TB + nib4(xr[2 * m], 1));
+        f[3] = *reinterpret_cast<const uint32_t *>(TB + nib4(xr[2 * m + 1], 1));
+    }
+    return __builtin_bit_cast(bf16x8, f);
+}
+
+// One block of this wavefront's 32 rows in the whole-sub-block form (four
+// columns): per sub-block two MFMAs accumulate the sums of all eight lane
+// groups; the pair of sub-block j + 1 is issued before the chain of j.
+template <int FMT, int QA, bool WRAP>
+__device__ __forceinline__ void mf_block4(const u32x4 *__restrict__ Afr, const float *__restrict__ Bias,
+                                          const float *__restrict__ D1s, const char *TB, int b, u32x4 w, float d0,
+                                          uint32_t rot0, uint32_t rot1, f32x16 &acc)
+{
+    constexpr int JS = FMT == BQ_Q1_0 ? 4 : 2;
+    constexpr int BL = FMT == BQ_Q1_0 ? 128 : 64;
+    const int lane = threadIdx.x & 63;
+    uint32_t xr[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xr[2 * i] = __builtin_amdgcn_alignbit(w[i], w[i], rot0);
+        xr[2 * i + 1] = __builtin_amdgcn_alignbit(w[i], w[i], rot1);
+    }
+    auto issue = [&](int j) -> f32x16 {
+        const int fi = (b * JS + j) * 2;
+        f32x16 c = {};
+        if (WRAP) {
+            const f32x4 *bp = reinterpret_cast<const f32x4 *>(Bias + (b * JS + j) * 32 + 4 * (lane >> 5));
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 v = bp[2 * a];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    c[4 * a + e] = v[e];
+            }
+        }
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, Afr[fi * 64 + lane]),
+                                                    mf_bfrag4<FMT>(TB, xr, j, 0), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, Afr[(fi + 1) * 64 + lane]),
+                                                       mf_bfrag4<FMT>(TB, xr, j, 1), c, 0, 0, 0);
+    };
+    f32x16 ab;
+    f32x16 cur = issue(0);
+#pragma unroll
+    for (int j = 0; j < JS; ++j) {
+        f32x16 nxt = {};
+        if (!WRAP && j + 1 < JS)
+            nxt = issue(j + 1);
+        // register r holds column r / 4
+        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(D1s + (b * BL + 32 * j) / QA * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            ab[r] = j == 0 ? d1[r >> 2] * cur[r] : __builtin_fmaf(d1[r >> 2], cur[r], ab[r]);
+        if (WRAP) {
+            if (j + 1 < JS)
+                cur = issue(j + 1);
+        } else {
+            cur = nxt;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        acc[r] = __builtin_fmaf(d0, ab[r], acc[r]);
 }
 
 // One block of this wavefront's 32 rows: slice halves S0 .. S0 + HALVES - 1.
@@ -238,23 +341,25 @@ __device__ __forceinline__ void mf_block(const u32x4 *__restrict__ Afr, const fl
     }
 }
 
-// Workgroup id -> (row group of 32-row tiles, group of eight columns); ids 8
+// Workgroup id -> (row group of 32-row tiles, group of NC columns); ids 8
 // apart share an XCD, so the column groups of one row group read its weights
-// through one L2.  HALVES = 2: a wavefront takes both slice halves of its 32
-// rows, four tiles per workgroup; HALVES = 1: the two halves of a tile in
-// two wavefronts, two tiles per workgroup, joined through LDS at the end.
-template <int FMT, int QA, int HALVES>
+// through one L2.  NC = 8, HALVES = 2: a wavefront takes both slice halves of
+// its 32 rows, four tiles per workgroup; HALVES = 1: the two halves of a tile
+// in two wavefronts, two tiles per workgroup, joined through LDS at the end.
+// NC = 4 (HALVES = 2): the whole-sub-block form, a wavefront per 32 rows.
+template <int FMT, int QA, int HALVES, int NC>
 __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void mfma_kernel(
     GemvDesc g, int64_t ld_q, int64_t ld_d, int ncols, int ntiles, int cgroups)
 {
-    using Chunk = MfChunk<FMT, QA>;
+    static_assert(NC == 8 || (NC == 4 && HALVES == 2), "forms");
+    using Chunk = MfChunk<FMT, QA, NC>;
     constexpr int JS = Chunk::JS;
     constexpr int BL = Chunk::BL;
     constexpr int TASKS = 2 / HALVES;       // wavefronts per 32-row tile
     constexpr int NTW = kMfWaves / TASKS;   // 32-row tiles per workgroup
     __shared__ u32x4 Afr[kMfChunk * JS * 2 * 64];
     __shared__ f32x4 Bias4[FMT == BQ_Q1_0 ? kMfChunk * JS * 2 * 8 : 1];
-    __shared__ f32x4 D1s4[Chunk::kDBlocks * kMfCols / 4];
+    __shared__ f32x4 D1s4[Chunk::kDBlocks * NC / 4];
     float *Bias = reinterpret_cast<float *>(Bias4);
     float *D1s = reinterpret_cast<float *>(D1s4);
     __shared__ u32x2 TB[16];
@@ -264,7 +369,7 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3
     const int cg = rest % cgroups, rg = (rest / cgroups) * 8 + slot;
     if (rg * NTW >= ntiles)
         return;  // padding workgroup (the grid is a multiple of 8 row groups)
-    const int c0 = cg * kMfCols;
+    const int c0 = cg * NC;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nt = rg * NTW + wave / TASKS, sh = HALVES == 2 ? 0 : wave % 2;
     const bool live = nt < ntiles;
@@ -336,7 +441,12 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3
                 float d0 = f16_bits_to_f32((i & 1) ? (sc[i >> 1] >> 16) : (sc[i >> 1] & 0xFFFFu));
                 asm volatile("" : "+v"(d0));
                 const char *tb = reinterpret_cast<const char *>(TB);
-                if (FMT == BQ_Q1_0 && wrap) {
+                if constexpr (NC == 4) {
+                    if (FMT == BQ_Q1_0 && wrap)
+                        mf_block4<FMT, QA, true>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc[0]);
+                    else
+                        mf_block4<FMT, QA, false>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc[0]);
+                } else if (FMT == BQ_Q1_0 && wrap) {
                     if (sh == 0)
                         mf_block<FMT, QA, HALVES, 0, true>(Afr, Bias, D1s, tb, i, w, d0, rot0, rot1, acc);
                     else
@@ -352,6 +462,25 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3
         sc = sc_next;
     }
 
+    const int row = nt * 32 + (lane & 31);
+    if constexpr (NC == 4) {
+        // The tree: register 4c + k of lane half h holds lane group 4h + k of
+        // column c; p_k = a_k + a_(k+4) across the halves, then
+        // (p0 + p2) + (p1 + p3) within the lane.
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float o = __shfl_xor(acc[0][r], 32, 64);
+            p[r] = acc[0][r] + o;
+        }
+        if (live && kh == 0 && row < g.rows) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (c0 + c < ncols)
+                    g.y[(int64_t)(c0 + c) * g.rows + row] = (p[4 * c] + p[4 * c + 2]) + (p[4 * c + 1] + p[4 * c + 3]);
+        }
+        return;
+    }
     // The tree: in lane half h, registers 2k and 2k + 1 of slice half s hold
     // lane groups s + 2h and s + 2h + 4 of column k.
     float P[HALVES][kMfCols];
@@ -363,7 +492,6 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3
             const float o = __shfl_xor(p, 32, 64);
             P[h][k] = kh == 0 ? p + o : o + p;  // p_s + p_(s+2)
         }
-    const int row = nt * 32 + (lane & 31);
     if (HALVES == 2) {
         if (live && kh == 0 && row < g.rows) {
 #pragma unroll
@@ -391,14 +519,14 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3
     }
 }
 
-template <int FMT, int HALVES>
+template <int FMT, int HALVES, int NC>
 static void mfma_shape(int qa, dim3 grid, hipStream_t st, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols,
                        int ntiles, int cgroups)
 {
     switch (qa) {
-    case 32: hipLaunchKernelGGL((mfma_kernel<FMT, 32, HALVES>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
-    case 64: hipLaunchKernelGGL((mfma_kernel<FMT, 64, HALVES>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
-    default: hipLaunchKernelGGL((mfma_kernel<FMT, 128, HALVES>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
+    case 32: hipLaunchKernelGGL((mfma_kernel<FMT, 32, HALVES, NC>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
+    case 64: hipLaunchKernelGGL((mfma_kernel<FMT, 64, HALVES, NC>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
+    default: hipLaunchKernelGGL((mfma_kernel<FMT, 128, HALVES, NC>), grid, dim3(kMfWaves * 64), 0, st, g, ld_q, ld_d, ncols, ntiles, cgroups); break;
     }
 }
 
@@ -406,15 +534,18 @@ template <int FMT>
 static hipError_t mfma_fmt(int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols,
                            hipStream_t st)
 {
-    const int cgroups = (ncols + kMfCols - 1) / kMfCols;
+    const int nc = shape == 2 ? 4 : kMfCols;
+    const int cgroups = (ncols + nc - 1) / nc;
     const int ntiles = (g.rows + 31) / 32;
-    const int ntw = shape == 0 ? kMfWaves : kMfWaves / 2;  // 32-row tiles per workgroup
+    const int ntw = shape == 1 ? kMfWaves / 2 : kMfWaves;  // 32-row tiles per workgroup
     const int rgroups = (ntiles + ntw - 1) / ntw;
     const dim3 grid((unsigned)(((rgroups + 7) / 8) * 8 * cgroups));
     if (shape == 0)
-        mfma_shape<FMT, 2>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
+        mfma_shape<FMT, 2, 8>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
+    else if (shape == 1)
+        mfma_shape<FMT, 1, 8>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
     else
-        mfma_shape<FMT, 1>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
+        mfma_shape<FMT, 2, 4>(qa, grid, st, g, ld_q, ld_d, ncols, ntiles, cgroups);
     return hipGetLastError();
 }
 

@@ -1,9 +1,10 @@
 """The small batch with its lane-group sums on the matrix cores
 (bq_set_batch_path(BQ_BATCH_MFMA)): every output bit-identical to the oracle.
 
-Cases cover both formats, both workgroup shapes of the kernel (slice halves
-in one wavefront on matrices of more than 1024 row tiles, in two below),
-one and two groups of eight columns (a ragged count pads the last group),
+Cases cover both formats, the three workgroup shapes of the kernel (eight
+columns with both slice halves in one wavefront on matrices of more than
+1024 row tiles, in two below; four columns with whole sub-blocks for 2-4
+columns), one and two column groups (a ragged count pads the last group),
 every qa, the -128 regimes (Q1_0's int8 wrap goes through the MFMA
 accumulator input), rows not a multiple of 32, and block counts that leave a
 partial 4-block chunk.  The table kernels are covered by test_gpu_parity.py,
@@ -62,6 +63,13 @@ CASES = [
     (Q2, 65600, 448, 8, 32, "raw"),
     (Q2, 65700, 4096, 16, 128, "quant"),
     (Q2, 70000, 320, 10, 64, "raw"),
+    # 2-4 columns: four columns per workgroup, whole sub-blocks
+    (Q1, 65600, 640, 4, 128, "quant"),
+    (Q1, 65601, 384, 2, 64, "mixed"),
+    (Q1, 4100, 1152, 3, 32, "raw"),        # few tiles, ragged rows, 9 blocks
+    (Q2, 65600, 448, 4, 32, "raw"),
+    (Q2, 70000, 320, 3, 64, "quant"),
+    (Q2, 3001, 256, 2, 128, "raw"),
 ]
 
 
@@ -80,7 +88,7 @@ def test_mfma_full_size(mfma_path, fmt, rows):
     """The small-batch workloads at their full sizes (qa 128, quantizer output)."""
     cols, qa = 4096, 128
     w = synth.blocks(fmt, rows, cols, 51, rows)
-    for ncols in (8, 16):
+    for ncols in (4, 8, 16):
         name = f"mfma full fmt={fmt} {rows}x{cols} N={ncols}"
         log(name)
         qs, ds = zip(*[oracle.quantize_q8(synth.activation(cols, 51, c), qa)[:2] for c in range(ncols)])
@@ -99,7 +107,8 @@ def test_mfma_q2_code3(mfma_path):
     assert_parity(matvec_gpu(Q2, w, rows, cols, q, d, qa), y_ref, "mfma Q2_0 code 3")
 
 
-@pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 20000, 16), (Q1, 70000, 8), (Q2, 20000, 12), (Q2, 70000, 16)])
+@pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 20000, 16), (Q1, 70000, 8), (Q1, 70000, 6), (Q1, 70000, 3),
+                                             (Q2, 20000, 12), (Q2, 70000, 16), (Q2, 70000, 4), (Q2, 70000, 5)])
 def test_batch_paths_agree(fmt, rows, ncols):
     """Both small-batch paths and the automatic choice give the same bits,
     and the same as the oracle."""
