@@ -126,3 +126,40 @@ def test_batch_paths_agree(fmt, rows, ncols):
     assert_parity(ys[0], y_ref, "tables")
     assert_parity(ys[1], y_ref, "mfma")
     assert_parity(ys[2], y_ref, "auto")
+
+
+@pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 70000, 8), (Q2, 70000, 4), (Q2, 12288, 16)])
+def test_mfma_graph_replay(mfma_path, fmt, rows, ncols):
+    """A matrix-core product captured in a graph: every replay, with eager
+    work and synchronisation between replays, gives the eager bits (and the
+    oracle's)."""
+    import torch as t
+    from gpu_util import stage_act
+    bq = bqmod()
+    cols, qa = 1024, 128
+    w, q, d = _inputs(fmt, rows, cols, ncols, qa, "quant", 71)
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    wd = bq.Weights.upload(fmt, w, rows, cols)
+    a = stage_act(q, d, qa)
+    y = t.full((ncols * rows,), float("nan"), dtype=t.float32, device="cuda")
+    f = bq.bq_q1_0_matvec if fmt == Q1 else bq.bq_q2_0_matvec
+    f(wd, a, y)
+    t.cuda.synchronize()
+    assert_parity(y.cpu().numpy().reshape(ncols, rows), y_ref, "mfma eager")
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        f(wd, a, y)  # warm-up on the capture stream
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        f(wd, a, y)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert_parity(y.cpu().numpy().reshape(ncols, rows), y_ref, f"mfma graph replay {rep}")
+        f(wd, a, y)  # eager work between replays
+        t.cuda.synchronize()
