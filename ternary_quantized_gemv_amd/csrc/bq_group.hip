@@ -303,7 +303,7 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
 template <int FMT, int QA, int RW, int TPW, bool Q8>
 __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
 {
-    static_assert(RW == 64 || TPW == 1, "several tiles per workgroup only with whole tiles");
+    static_assert(RW == 64 || RW == 32 || TPW == 1, "several units per workgroup: whole or half tiles");
     constexpr int kParts = kTileRows / RW;           // workgroups per tile
     constexpr int kChainWaves = 8 * RW / 64;
     constexpr int kBPW = RW == 64 ? 2 : 64 / RW;     // first block of wavefront w: kBPW * w
@@ -326,14 +326,17 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         g.y += (int64_t)c * g.rows;
     }
     const int tiles = (g.rows + kTileRows - 1) / kTileRows;
-    const int tile0 = (wg - wg0) / kParts * TPW, part = (wg - wg0) % kParts;
+    // the workgroup's units (RW rows each) in turn: unit t is part upart(t) of tile utile(t)
+    const int unit0 = (wg - wg0) * TPW;
+    auto utile = [&](int t) { return (unit0 + t) / kParts; };
+    auto upart = [&](int t) { return (unit0 + t) % kParts; };
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int h = lane / RW, r = lane % RW;  // half-wave and row of this lane (h = 0 when RW = 64)
-    const uint32_t lo = (uint32_t)(part * RW + r) * 16;
+    auto ulo = [&](int t) { return (uint32_t)(upart(t) * RW + r) * 16; };
     const int nb = g.nb, ng = g.ng;
     // a tile past the product's last one re-reads the last tile and stores nothing
-    auto wtile = [&](int t) { return rsrc_of(g.bits + (int64_t)min(tile0 + t, tiles - 1) * g.nb * kTileRows); };
-    auto stile = [&](int t) { return rsrc_of(g.scales + (int64_t)min(tile0 + t, tiles - 1) * g.ng * kTileRows); };
+    auto wtile = [&](int t) { return rsrc_of(g.bits + (int64_t)min(utile(t), tiles - 1) * g.nb * kTileRows); };
+    auto stile = [&](int t) { return rsrc_of(g.scales + (int64_t)min(utile(t), tiles - 1) * g.ng * kTileRows); };
 
     // Requests in the order of use (vector memory counts complete in order);
     // all unconditional, clamped to the row's last block / scale group.
@@ -357,16 +360,16 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         if (RW == 64) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                v[i] = bload(wp, lo, (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
+                v[i] = bload(wp, ulo(t), (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
         } else {
-            v[0] = bload(wp, lo + (uint32_t)min(cb + kBPW * wave + h, nb - 1) * kStep, 0);
+            v[0] = bload(wp, ulo(t) + (uint32_t)min(cb + kBPW * wave + h, nb - 1) * kStep, 0);
         }
     };
     auto request_scales = [&](int t, int cb) {
         const rsrc_t sp = stile(t);
 #pragma unroll
         for (int j = 0; j < kChunkBlocks / kScalesPerGroup; ++j)
-            sc[j] = bload(sp, lo, (uint32_t)min(cb / kScalesPerGroup + j, ng - 1) * kStep);
+            sc[j] = bload(sp, ulo(t), (uint32_t)min(cb / kScalesPerGroup + j, ng - 1) * kStep);
     };
     const int slot = threadIdx.x;
     load_a(0, min(kChunkBlocks, nb), slot);
@@ -432,8 +435,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         if (wave < kChainWaves)
             AB[0][L][r] = acc[t];
         __syncthreads();
-        if (wave == 0 && lane < RW && tile0 + t < tiles) {
-            const int row = (tile0 + t) * kTileRows + part * RW + lane;
+        if (wave == 0 && lane < RW && utile(t) < tiles) {
+            const int row = utile(t) * kTileRows + upart(t) * RW + lane;
             const float y = ((AB[0][0][lane] + AB[0][4][lane]) + (AB[0][2][lane] + AB[0][6][lane])) +
                             ((AB[0][1][lane] + AB[0][5][lane]) + (AB[0][3][lane] + AB[0][7][lane]));
             if (row < g.rows)
@@ -578,6 +581,7 @@ hipError_t launch_group(int fmt, int qa, GroupShape shape, const GroupArgs &a, h
     case kShapeQuarter: q1 ? wide_qa<BQ_Q1_0, 16, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 16, 1, false>(qa, a, 1, st); break;
     case kShapeHalf: q1 ? wide_qa<BQ_Q1_0, 32, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 32, 1, false>(qa, a, 1, st); break;
     case kShapeWide: q1 ? wide_qa<BQ_Q1_0, 64, 1, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 64, 1, false>(qa, a, 1, st); break;
+    case kShapeHalf3: q1 ? wide_qa<BQ_Q1_0, 32, 3, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 32, 3, false>(qa, a, 1, st); break;
     case kShapeWide2: q1 ? wide_qa<BQ_Q1_0, 64, 2, false>(qa, a, 1, st) : wide_qa<BQ_Q2_0, 64, 2, false>(qa, a, 1, st); break;
     default: q1 ? rows_qa<BQ_Q1_0>(qa, a, st) : rows_qa<BQ_Q2_0>(qa, a, st); break;
     }
@@ -593,6 +597,8 @@ hipError_t launch_wide_q8(int fmt, int qa, GroupShape shape, const GroupArgs &a,
         q1 ? wide_qa<BQ_Q1_0, 32, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 32, 1, true>(qa, a, ncols, st);
     else if (shape == kShapeWide)
         q1 ? wide_qa<BQ_Q1_0, 64, 1, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 64, 1, true>(qa, a, ncols, st);
+    else if (shape == kShapeHalf3)
+        q1 ? wide_qa<BQ_Q1_0, 32, 3, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 32, 3, true>(qa, a, ncols, st);
     else
         q1 ? wide_qa<BQ_Q1_0, 64, 2, true>(qa, a, ncols, st) : wide_qa<BQ_Q2_0, 64, 2, true>(qa, a, ncols, st);
     return hipGetLastError();

@@ -77,13 +77,14 @@ enum GroupShape {
     kShapeWide = 2,     // one tile per sixteen-wavefront workgroup
     kShapeWide2 = 3,    // two tiles per sixteen-wavefront workgroup, one after the other
     kShapeRows = 4,     // up to eight tiles per workgroup (GroupArgs::rows_tpw), one per wavefront, one row per lane
+    kShapeHalf3 = 5,    // three half tiles per sixteen-wavefront workgroup, one after the other
 };
 // The finest shape whose workgroups fit one round of the GPU's 256 compute
 // units (one sixteen-wavefront workgroup each), and its workgroup count.
 inline GroupShape group_shape(int64_t tiles)
 {
     return tiles <= 64 ? kShapeQuarter : tiles <= 128 ? kShapeHalf : tiles <= 256 ? kShapeWide
-           : tiles <= 512 ? kShapeWide2 : kShapeRows;
+           : tiles <= 384 ? kShapeHalf3 : tiles <= 512 ? kShapeWide2 : kShapeRows;
 }
 inline int64_t group_workgroups(GroupShape shape, int64_t tiles, int rows_tpw)
 {
@@ -92,6 +93,7 @@ inline int64_t group_workgroups(GroupShape shape, int64_t tiles, int rows_tpw)
     case kShapeHalf: return 2 * tiles;
     case kShapeWide: return tiles;
     case kShapeWide2: return (tiles + 1) / 2;
+    case kShapeHalf3: return (2 * tiles + 2) / 3;
     default: return (tiles + rows_tpw - 1) / rows_tpw;
     }
 }
