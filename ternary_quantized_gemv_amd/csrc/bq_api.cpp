@@ -42,16 +42,18 @@ constexpr int kColsMinCols = 4;
 // tiles (at most kSplitMaxTiles): the first of eight wavefronts per tile
 // with one tile per workgroup, then four per tile with two, three or four
 // tiles, whose workgroups (row blocks times groups of four columns) fit one
-// round of the 256 compute units; failing that three tiles per workgroup up
-// to two rounds, else four.  Measured on MI355X (us, event-timed replays of
-// ~1 GB of weight copies) against one grid row per column:
-//   Q1_0 12288x4096  N = 4 / 8 / 16   17.1 / 24.7 / 44.7 -> 15.0 / 18.0 / 20.7
-//   Q2_0 12288x4096  N = 8 / 16       42.3 / 78.1 -> 28.8 / 33.8
-//   Q1_0 44800x1024  N = 2 / 4 / 16   13.4 / 23.3 / 79.1 -> 7.7 / 7.8 / 21.4
-//   Q1_0 20000x4096  N = 2 / 4 / 16   17.8 / 25.4 / 77.1 -> 17.8 / 18.0 / 39.0
-//   Q1_0 65536x1024  N = 4 / 8        31.7 / 57.2 -> 8.7 / 15.5
-// and every choice this rule makes was the fastest shape measured or within
-// 0.4 us of it.
+// round of the 256 compute units; failing that four wavefronts per tile and
+// two tiles per workgroup.  Measured on MI355X (us, event-timed replays of
+// ~1 GB of weight copies; shapes 0 / 1 / 2 / 3, the rule's choice first):
+//   Q1_0 12288x4096  N = 4    10.9: 10.9 / 13.6 / 16.4 / 19.3
+//                    N = 8    13.6: 15.8 / 13.6 / 16.6 / 19.3
+//                    N = 16   16.7: 23.1 / 20.6 / 16.7 / 19.5
+//   Q2_0 12288x4096  N = 4 / 8 / 16     20.0 / 22.0 / 27.0 (shapes 0 / 1 / 2, each the fastest)
+//   Q1_0 44800x1024  N = 2 / 4 / 16     6.8 / 7.1 / 18.2 (2 / 2 / 1, each the fastest)
+//   Q1_0 20000x4096  N = 16   29.6: 35.7 / 29.6 / 31.6 / 36.7
+//   Q1_0 65536x1024  N = 4 / 8          8.2 / 13.7 (3 / 1, each the fastest)
+// Against one grid row per column the tables' single stream of the weights
+// per four columns gained 1.7-9x (Q1_0 65536x1024 N = 8: 57.2 -> 13.7).
 static int splitcols_shape(int tiles, int ncols)
 {
     const int64_t cgroups = (ncols + 3) / 4;
@@ -59,7 +61,7 @@ static int splitcols_shape(int tiles, int ncols)
     for (int s = 0; s < kSplitColsShapes; ++s)
         if (wgs(s) <= 256)
             return s;
-    return wgs(2) <= 512 ? 2 : 3;
+    return 1;
 }
 
 // The small batch on the matrix cores (launch_mfma) or on the table kernels
@@ -69,20 +71,21 @@ static int splitcols_shape(int tiles, int ncols)
 // wavefronts, for matrices of up to kSplitMaxTiles tiles); 2, four columns,
 // whole sub-blocks (two accumulating MFMAs each; no padded outputs below
 // five columns).  BQ_BATCH_AUTO takes the matrix cores where they measured
-// faster (MI355X, us, event-timed replays of ~1 GB of weight copies; tables
-// / four-column form / eight-column form):
-//   Q2_0 151936x4096  N = 2 / 4 / 6      88.0 / 110.8 / 177.3, 83.9 / 76.7 / 127.3, 98.3 / 88.7 / 91.0
-//                     N = 8 / 12 / 16    177.5 / 263.3 / 328.7, -, 93.1 / 161.4 / 165.8
-//   Q1_0 151936x4096  N = 2 / 4 / 6      46.2 / 68.8 / 107.9, 72.6 / 67.2 / 111.3, 98.1 / 93.6 / 92.4
-//                     N = 8 / 12 / 16    106.4 / 153.1 / 192.3, -, 92.5 / 165.9 / 168.4
-//   Q2_0 12288x4096   N = 8 / 16         28.9 / 34.1, -, 27.3 / 32.2 (shape 1)
-//   Q1_0 12288x4096   N = 8 / 16         17.9 / 20.7, -, 21.5 / 29.2 (shape 1; tables kept)
-// so: Q2_0 on more than kSplitMaxTiles tiles from 2 columns on (four-column
-// form up to 4), on fewer tiles from 8; Q1_0 on more than kSplitMaxTiles
-// tiles for 5-8 and 13-16 columns (the tables' cost grows by groups of
-// four columns, the matrix cores' by groups of eight).  Returns the shape,
-// or -1 for the tables.  BQ_BATCH_MFMA takes the matrix cores from 2
-// columns on, BQ_BATCH_TABLES never.
+// faster (MI355X, us, event-timed replays of ~1 GB of weight copies;
+// tables / matrix cores):
+//   Q1_0 151936x4096  N = 2 / 4 / 8 / 16   45.3 / 48.9 / 76.6 / 136.2, 69.3 / 65.4 / 92.3 / 167.4
+//   Q1_0 12288x4096   N = 2 / 4 / 8 / 16   9.1 / 10.9 / 14.2 / 17.4, 23.7 / 23.7 / 19.8 / 25.3
+//   Q1_0 44800x1024   N = 4 / 8 / 16       7.1 / 11.8 / 19.7, 10.5 / 10.4 / 18.5
+//   Q2_0 151936x4096  N = 2 / 4 / 8 / 16   87.4 / 87.5 / 145.0 / 267.9, 74.4 / 74.4 / 92.2 / 164.9
+//   Q2_0 65536x1024   N = 2 / 8 / 16       12.2 / 21.2 / 38.3, 11.9 / 15.1 / 26.6
+//   Q2_0 12288x4096   N = 2 / 4 / 8 / 16   15.1 / 20.1 / 22.3 / 28.6, 28.6 / 28.7 / 26.5 / 30.9
+//   Q2_0 20000x4096   N = 4 / 12 / 16      22.5 / 34.5 / 52.6, 29.0 / 39.1 / 37.9
+// so: Q1_0 always on the tables (the shapes with 4096 columns are faster
+// there at every N, the others within 13%); Q2_0 on the matrix cores from
+// kSplitMaxTiles tiles on, or where the tables' work items (tiles times
+// groups of four columns) exceed kSplitMaxTiles.  Returns the shape, or -1
+// for the tables.  BQ_BATCH_MFMA takes the matrix cores from 2 columns on,
+// BQ_BATCH_TABLES never.
 static std::atomic<int> g_batch_path{BQ_BATCH_AUTO};
 
 static int mfma_choice(int fmt, int tiles, int ncols)
@@ -94,9 +97,10 @@ static int mfma_choice(int fmt, int tiles, int ncols)
     const int path = g_batch_path.load(std::memory_order_relaxed);
     if (path != BQ_BATCH_AUTO)
         return path == BQ_BATCH_MFMA ? shape : -1;
-    if (fmt == BQ_Q2_0)
-        return tall || ncols >= 8 ? shape : -1;
-    return tall && ((ncols >= 5 && ncols <= 8) || ncols >= 13) ? shape : -1;
+    if (fmt == BQ_Q1_0)
+        return -1;
+    const int64_t items = (int64_t)tiles * ((ncols + 3) / 4);
+    return tiles >= kSplitMaxTiles || items > kSplitMaxTiles ? shape : -1;
 }
 
 // ------------------------------------------------------------ validation

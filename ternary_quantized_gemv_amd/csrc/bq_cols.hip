@@ -11,8 +11,8 @@
 // already hold d1*s (the same single rounding), then fma(d1, s, ab) per later
 // sub-block and fma(d0, ab, acc) per block; the final tree per column.
 //
-// Tables cover a chunk of 4 blocks: 4 x 32 slots x 16 entries x 16 bytes =
-// 32 KiB, rebuilt between barriers.  A workgroup is four wavefronts, one
+// Tables cover a chunk of 4 blocks: 4 x 32 slots x 16 entries x 16 bytes
+// (34 KiB with the slot padding below), rebuilt between barriers.  A workgroup is four wavefronts, one
 // 64-row tile each, so three workgroups share a CU (registers allow three
 // wavefronts per SIMD).
 #include "bq_device.h"
@@ -26,7 +26,14 @@ constexpr int kColsChunk = 4;  // blocks per table chunk
 // payload ring, so a full chunk must be a multiple of four blocks
 static_assert(kColsChunk % 4 == 0, "chunk of whole ring turns");
 constexpr int kColsWaves = 4;  // wavefronts (tiles) per workgroup
-constexpr int kColsSlotBytes = 16 * kColsNC * 4;
+// A slot's 16 entries take 256 bytes, padded to 272: the table builds store
+// single floats (entry n, column c) from lanes that differ in slot and
+// column, and a 256-byte slot stride would put sixteen of a wavefront's
+// stores in each LDS bank (a 272-byte one: two).  Lookups of one slot stay
+// within its 256 bytes.
+constexpr int kColsSlotBytes = 16 * kColsNC * 4 + 16;
+constexpr int kColsSlotVecs = kColsSlotBytes / 16;  // f32x4 per slot
+constexpr int kColsSlotFloats = kColsSlotBytes / 4;
 constexpr int kColsD1 = kColsChunk * 4 * kColsNC;  // activation scales per chunk [sub-block][column]
 
 // Byte m of x masked to bits 4..7: nibble * 16, the byte offset of a
@@ -48,29 +55,68 @@ __device__ __forceinline__ f32x4 tab4(const f32x4 *T, int slot, uint32_t idx16)
     return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(T) + slot * kColsSlotBytes + idx16);
 }
 
+// The 16 table entries of one slot and column from its packed quants
+// (Q1_0: four, Q2_0: two): Q1_0 entry n = sum_i (bit i of n ? q_i :
+// wrap8(-q_i)); Q2_0 entry 4h + e = (e-1) q_0 + (h-1) q_1.  Formed in f32
+// from converted quants: every partial sum is an integer of magnitude at
+// most 512, so each addition is exact, and negation is a subtraction from
+// +0 so that a zero entry is +0 as the integer sum's conversion would be.
+// Q1_0 shares its pair sums: entry 4h + e = lo[e] + hi[h].
+template <int FMT>
+__device__ __forceinline__ void slot_entries(uint32_t wq, float (&v)[16])
+{
+    if (FMT == BQ_Q1_0) {
+        float p[4], n[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int x = (int8_t)(wq >> (8 * i));
+            p[i] = (float)x;
+            n[i] = x == -128 ? -128.0f : 0.0f - p[i];
+        }
+        float lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo[e] = ((e & 1) ? p[0] : n[0]) + ((e & 2) ? p[1] : n[1]);
+            hi[e] = ((e & 1) ? p[2] : n[2]) + ((e & 2) ? p[3] : n[3]);
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[4 * h + e] = lo[e] + hi[h];
+    } else {
+        const float a = (float)(int8_t)(wq & 0xFF), b = (float)(int8_t)(wq >> 8);
+        const float A[4] = {0.0f - a, 0.0f, a, a + a}, B[4] = {0.0f - b, 0.0f, b, b + b};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[4 * h + e] = A[e] + B[h];
+    }
+}
+
 // Tables of one chunk for columns c0 .. c0+3 (zeros for columns >= ncols).
 // Q1_0 slot t covers chunk values 4t..4t+3 (block t/32, sub-block (t/8)%4,
-// lane group t%8); entry n: sum_i (bit i of n ? q_i : wrap8(-q_i)), times d1
-// on sub-block 0.  Q2_0 slot t covers values 2t, 2t+1; entry n = 4h + e:
-// (e-1)*q_2t + (h-1)*q_2t+1.
+// lane group t%8); entries as slot_entries, times d1 on sub-block 0.  Q2_0
+// slot t covers values 2t, 2t+1.
 template <int FMT, int QA, int CHUNK = kColsChunk, int THREADS = kColsWaves * 64>
 __device__ void build_cols(f32x4 *T, float *D1, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int c0, int ncols,
                            int k0, int nbc)
 {
     constexpr int S = FMT == BQ_Q1_0 ? 4 : 2;
     constexpr int kThreadsHere = THREADS;
-    constexpr int kIters = CHUNK * kSlotsPerBlock * 4 * kColsNC / kThreadsHere;
-    static_assert(kIters * kThreadsHere == CHUNK * kSlotsPerBlock * 4 * kColsNC, "whole table quarters per thread");
-    // unit u = (slot t, quarter h, column c): entries 4h..4h+3 of column c.
-    // All of a thread's loads are issued before any is used.
-    const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
+    constexpr int kIters = CHUNK * kSlotsPerBlock * kColsNC / kThreadsHere;
+    static_assert(kIters * kThreadsHere == CHUNK * kSlotsPerBlock * kColsNC, "whole slots per thread");
+    // unit u = (slot t, column c): the slot's 16 entries of column c.  All of
+    // a thread's loads are issued before any is used.
+    const int nunits = nbc * kSlotsPerBlock * kColsNC;
     float *Tf = reinterpret_cast<float *>(T);
     uint32_t wq[kIters];
     float d1[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
         const int u = threadIdx.x + it * kThreadsHere;
-        const int c = u % kColsNC, t = u / (4 * kColsNC);
+        const int c = u % kColsNC, t = u / kColsNC;
         const bool ok = u < nunits && c0 + c < ncols;
         const int cc = ok ? c0 + c : c0;
         const int8_t *q = g.q + (int64_t)cc * ld_q + k0;
@@ -87,35 +133,15 @@ __device__ void build_cols(f32x4 *T, float *D1, const GemvDesc &g, int64_t ld_q,
         const int u = threadIdx.x + it * kThreadsHere;
         if (u >= nunits)
             break;
-        const int c = u % kColsNC, h = (u / kColsNC) & 3, t = u / (4 * kColsNC);
-        float v[4];
-        if (FMT == BQ_Q1_0) {
-            int p1[4], p0[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int x = (int8_t)(wq[it] >> (8 * i));
-                p1[i] = x;
-                p0[i] = x == -128 ? -128 : -x;
-            }
-            const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
-            const bool first = ((t >> 3) & 3) == 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int lo = ((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]);
-                const float sf = (float)(lo + hi);
-                v[e] = first ? d1[it] * sf : sf;
-            }
-        } else {
-            const int qa0 = (int8_t)(wq[it] & 0xFF), qa1 = (int8_t)(wq[it] >> 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
-        }
+        const int c = u % kColsNC, t = u / kColsNC;
+        float v[16];
+        slot_entries<FMT>(wq[it], v);
         // a column past ncols loaded zeros: its entries are 0 (Q1_0 d1 = 0 on sub-block 0, and
         // the integer sums of zero quants are 0)
+        const bool first = FMT == BQ_Q1_0 && ((t >> 3) & 3) == 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Tf[(t * 16 + 4 * h + e) * kColsNC + c] = v[e];
+        for (int n = 0; n < 16; ++n)
+            Tf[t * kColsSlotFloats + n * kColsNC + c] = first ? d1[it] * v[n] : v[n];
     }
     for (int i = threadIdx.x; i < nbc * S * kColsNC; i += kThreadsHere) {
         const int sb = i / kColsNC, c = i % kColsNC;
@@ -192,7 +218,7 @@ template <int FMT, int QA>
 __global__ __launch_bounds__(kColsWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void cols_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int ncols, int tiles,
                                                         int cgroups)
 {
-    __shared__ f32x4 T[kColsChunk * kSlotsPerBlock * 16];
+    __shared__ f32x4 T[kColsChunk * kSlotsPerBlock * kColsSlotVecs];
     __shared__ float D1[kColsD1];
     const int id = blockIdx.x, slot = id & 7, rest = id >> 3;
     const int cg = rest % cgroups, rb = (rest / cgroups) * 8 + slot;
@@ -287,7 +313,7 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // The lane groups of a wavefront are ones the final tree joins first --
 // W = 4: a_k + a_(k+4); W = 2: (a_k + a_(k+4)) + (a_(k+2) + a_(k+6)) -- so a
 // wavefront adds them in the tree's order and the remaining additions of
-// the tree go through LDS.  Tables cover 8-block chunks (64 KiB); the
+// the tree go through LDS.  Tables cover 8-block chunks (68 KiB); the
 // wavefronts of a tile read the same payload (one HBM stream, the rest from
 // the caches), each rotating a word once so that its lane groups' nibbles
 // sit at bits 4..7 of bytes (nibble * 16: an entry of four floats).
@@ -308,12 +334,12 @@ __device__ __forceinline__ float sc_part(const float (&acc)[LG][kColsNC], int c)
 
 // The inputs of one chunk's interleaved tables, read a chunk ahead into
 // registers so that the build after the next barrier does not wait for
-// memory: unit u = (slot t, quarter h, column c) of the table.  Unlike
+// memory: unit u = (slot t, column c) of the table.  Unlike
 // build_cols, every entry holds the integer sum s (sub-block 0 too); the
 // walk forms d1 * s itself, the same single rounding.
 template <int FMT, int QA, int CHUNK, int THREADS>
 struct ColsInputs {
-    static constexpr int kIters = (CHUNK * kSlotsPerBlock * 4 * kColsNC + THREADS - 1) / THREADS;
+    static constexpr int kIters = (CHUNK * kSlotsPerBlock * kColsNC + THREADS - 1) / THREADS;
     static constexpr int S = FMT == BQ_Q1_0 ? 4 : 2;
     static constexpr int kD1 = (CHUNK * S * kColsNC + THREADS - 1) / THREADS;
     uint32_t wq[kIters];
@@ -322,11 +348,11 @@ struct ColsInputs {
     __device__ __forceinline__ void load(const GemvDesc &g, int64_t ld_q, int64_t ld_d, int c0, int ncols, int k0,
                                          int nbc)
     {
-        const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
+        const int nunits = nbc * kSlotsPerBlock * kColsNC;
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             const int u = threadIdx.x + it * THREADS;
-            const int c = u % kColsNC, t = u / (4 * kColsNC);
+            const int c = u % kColsNC, t = u / kColsNC;
             const bool ok = u < nunits && c0 + c < ncols;
             const int cc = ok ? c0 + c : c0;
             const int8_t *q = g.q + (int64_t)cc * ld_q + k0;
@@ -344,39 +370,23 @@ struct ColsInputs {
         }
     }
 
-    // the tables of the loaded chunk (entries as in build_cols)
+    // the tables of the loaded chunk: unit u = (slot t, column c), the
+    // slot's 16 entries of column c (slot_entries)
     __device__ __forceinline__ void store(f32x4 *T, float *D1, int nbc) const
     {
-        const int nunits = nbc * kSlotsPerBlock * 4 * kColsNC;
+        const int nunits = nbc * kSlotsPerBlock * kColsNC;
         float *Tf = reinterpret_cast<float *>(T);
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             const int u = threadIdx.x + it * THREADS;
             if (u >= nunits)
                 break;
-            const int c = u % kColsNC, h = (u / kColsNC) & 3, t = u / (4 * kColsNC);
-            float v[4];
-            if (FMT == BQ_Q1_0) {
-                int p1[4], p0[4];
+            const int c = u % kColsNC, t = u / kColsNC;
+            float v[16];
+            slot_entries<FMT>(wq[it], v);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int x = (int8_t)(wq[it] >> (8 * i));
-                    p1[i] = x;
-                    p0[i] = x == -128 ? -128 : -x;
-                }
-                const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = (float)(((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]) + hi);
-            } else {
-                const int qa0 = (int8_t)(wq[it] & 0xFF), qa1 = (int8_t)(wq[it] >> 8);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                Tf[(t * 16 + 4 * h + e) * kColsNC + c] = v[e];
+            for (int n = 0; n < 16; ++n)
+                Tf[t * kColsSlotFloats + n * kColsNC + c] = v[n];
         }
 #pragma unroll
         for (int r = 0; r < kD1; ++r) {
@@ -452,7 +462,7 @@ __global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int
 {
     constexpr int kThreadsHere = W * TPW * 64;
     constexpr int LG = 8 / W;
-    __shared__ f32x4 T[kScChunk * kSlotsPerBlock * 16];
+    __shared__ f32x4 T[kScChunk * kSlotsPerBlock * kColsSlotVecs];
     __shared__ float D1[kScChunk * 4 * kColsNC];
     __shared__ float P[TPW][W][kColsNC][64];
     const int id = blockIdx.x, slot = id & 7, rest = id >> 3;

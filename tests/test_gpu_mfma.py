@@ -128,6 +128,32 @@ def test_batch_paths_agree(fmt, rows, ncols):
     assert_parity(ys[2], y_ref, "auto")
 
 
+@pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 20000, 6), (Q1, 70000, 6), (Q2, 20000, 5), (Q2, 70000, 9)])
+def test_batch_zero_activations(fmt, rows, ncols):
+    """Zero quants: an all-zero column (scale 0) and columns with zero
+    blocks, on every small-batch path.  Zero table entries and zero lane-group
+    sums must come out as +0, as the oracle's integer sums do, so that every
+    output bit (the sign of a zero included) matches."""
+    bq = bqmod()
+    cols, qa = 1024, 64
+    w = synth.blocks(fmt, rows, cols, 73, rows, ncols)
+    xs = [synth.activation(cols, 73, c) for c in range(ncols)]
+    xs[1][:] = 0.0                      # the whole column
+    xs[2][: cols // 2] = 0.0            # the first half of the blocks
+    xs[-1][qa: 3 * qa] = 0.0            # two blocks inside
+    qs, ds = zip(*[oracle.quantize_q8(x, qa)[:2] for x in xs])
+    q, d = np.stack(qs), np.stack(ds)
+    assert not q[1].any() and not d[1].any()
+    y_ref = oracle.matvec(fmt, w, rows, cols, q, d, qa, ncols=ncols, threads=THREADS)
+    for path, name in ((bq.BQ_BATCH_TABLES, "tables"), (bq.BQ_BATCH_MFMA, "mfma"), (bq.BQ_BATCH_AUTO, "auto")):
+        prev = bq.bq_set_batch_path(path)
+        try:
+            y = matvec_gpu(fmt, w, rows, cols, q, d, qa)
+        finally:
+            bq.bq_set_batch_path(prev)
+        assert_parity(y, y_ref, f"zero activations {name} fmt={fmt} {rows}x{cols} N={ncols}")
+
+
 @pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 70000, 8), (Q2, 70000, 4), (Q2, 12288, 16)])
 def test_mfma_graph_replay(mfma_path, fmt, rows, ncols):
     """A matrix-core product captured in a graph: every replay, with eager

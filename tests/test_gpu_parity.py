@@ -204,7 +204,7 @@ def test_small_batch_tall(fmt, rows, cols, ncols, qa, regime):
 # the split-columns kernel, four columns per workgroup from interleaved
 # tables, eight wavefronts per tile (one tile per workgroup) or four (two,
 # three or four tiles), the shape chosen so the workgroups fit one round of
-# the GPU.  Cases: each shape and format, rows ragged, rows of 5 / 8 / 9 / 32
+# the GPU (else two tiles per workgroup).  Cases: each shape and format, rows ragged, rows of 5 / 8 / 9 / 32
 # / 34 / 96 blocks (partial and several 8-block chunks), a last group of one
 # to three columns, every qa, the -128 regimes, 1024 tiles.
 SPLITCOLS = [
@@ -215,7 +215,7 @@ SPLITCOLS = [
     (Q1, 44800, 1024, 2, 64, "mixed"),    # 700 tiles: four per tile, three tiles
     (Q1, 4096, 12288, 16, 128, "raw"),    # 64 tiles, sixteen columns: eight per tile; 96 blocks
     (Q2, 8192, 4096, 8, 64, "quant"),     # 128 tiles, eight columns: eight per tile
-    (Q1, 65536, 640, 6, 32, "quant"),     # 1024 tiles, six columns: four per tile, four tiles (two rounds)
+    (Q1, 65536, 640, 6, 32, "quant"),     # 1024 tiles, six columns: no shape fits one round, two tiles
     (Q2, 65536, 512, 3, 64, "raw"),       # 1024 tiles: four per tile, four tiles
     (Q2, 6400, 2048, 7, 32, "mixed"),     # 100 tiles, seven columns (a group of three)
 ]
