@@ -99,12 +99,22 @@ __device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restric
     }
 }
 
+// Thread t stores slot t's 16 entries as four 16-byte quarters, slots 64
+// bytes apart.  Stored in the same order by every lane, the quarters of
+// eight neighbouring lanes meet four to an LDS bank; with ROT, lane t stores
+// quarter (k + t/2) % 4 at step k instead, which spreads them over all
+// banks for a few more instructions and registers.  (Padding the slots
+// instead would push the far slots' table offsets past the 16-bit
+// immediate of the lookups.)
+template <bool ROT>
+__device__ __forceinline__ int slot_quarter(int k, int t) { return ROT ? (k + (t >> 1)) & 3 : k; }
+
 // The quantizer's per-block maximum (over the QA / V threads of an
 // activation block, group_max), its quants, and the slot's
 // 16-entry table.  Entries are sums of quants, exact in f32, formed from
 // converted quants; on a Q1_0 block's first sub-block they are multiplied by
 // d1 (one rounding, as the order prescribes).
-template <int FMT, int QA>
+template <int FMT, int QA, bool ROT>
 __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT> &xs, int nbc, int t)
 {
     constexpr int V = XSlot<FMT>::V, kLanes = QA / V;
@@ -121,20 +131,20 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
     if constexpr (FMT == BQ_Q1_0) {
         // entry 4h + e: +-q0 +-q1 by bits 0, 1 of e, +-q2 +-q3 by bits 0, 1 of h
-        float lo[4], hi[4];
+        float lo[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 4; ++e)
             lo[e] = ((e & 1) ? f[0] : -f[0]) + ((e & 2) ? f[1] : -f[1]);
-            hi[e] = ((e & 1) ? f[2] : -f[2]) + ((e & 2) ? f[3] : -f[3]);
-        }
         // times d1 on a block's first sub-block, times 1 (exact) elsewhere
         const float s1 = ((t >> 3) & 3) == 0 ? db : 1.0f;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int k = 0; k < 4; ++k) {
+            const int h = slot_quarter<ROT>(k, t);
+            const float hi = ((h & 1) ? f[2] : -f[2]) + ((h & 2) ? f[3] : -f[3]);
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = s1 * (lo[e] + hi[h]);
+                v[e] = s1 * (lo[e] + hi);
             dst[h] = v;
         }
         if ((t & 7) == 0)
@@ -142,7 +152,8 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     } else {
         // entry 4h + e: (e-1) q0 + (h-1) q1
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int k = 0; k < 4; ++k) {
+            const int h = slot_quarter<ROT>(k, t);
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -182,7 +193,7 @@ __device__ __forceinline__ void load_qslot(QSlot &qs, const int8_t *__restrict__
     qs.d = d[e / QA];
 }
 
-template <int FMT>
+template <int FMT, bool ROT>
 __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs, int nbc, int t)
 {
     if (t >= nbc * kSlotsPerBlock)
@@ -198,7 +209,8 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
         }
         const float s1 = ((t >> 3) & 3) == 0 ? qs.d : 1.0f;  // d1 on a block's first sub-block
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int k = 0; k < 4; ++k) {
+            const int h = slot_quarter<ROT>(k, t);
             const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
             f32x4 v;
 #pragma unroll
@@ -211,7 +223,8 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
     } else {
         const int q0 = (int8_t)(qs.w & 0xFF), q1 = (int8_t)(qs.w >> 8);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int k = 0; k < 4; ++k) {
+            const int h = slot_quarter<ROT>(k, t);
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -350,9 +363,9 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     };
     auto build_a = [&](int nbc, int t) {
         if constexpr (Q8)
-            build_qslot<FMT>(T, D1, qs, nbc, t);
+            build_qslot<FMT, true>(T, D1, qs, nbc, t);
         else
-            build_slot<FMT, QA>(T, D1, xs, nbc, t);
+            build_slot<FMT, QA, true>(T, D1, xs, nbc, t);
     };
     u32x4 v[2], sc[kChunkBlocks / kScalesPerGroup];
     auto request = [&](int t, int cb) {
@@ -525,8 +538,9 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
         const int nx = cb + kChunkBlocks < nb ? cb + kChunkBlocks : cb;  // the last chunk re-reads itself
         if (cb > 0)
             __syncthreads();  // every wavefront is done with the previous table
-        build_slot<FMT, QA>(T, D1, x0, nbc, s0);
-        build_slot<FMT, QA>(T, D1, x1, nbc, s1);
+        // (without the rotation: its registers would cost the second workgroup per CU)
+        build_slot<FMT, QA, false>(T, D1, x0, nbc, s0);
+        build_slot<FMT, QA, false>(T, D1, x1, nbc, s1);
         __syncthreads();
         load_slot<FMT>(x0, a.x, nx, min(kChunkBlocks, nb - nx), s0);
         load_slot<FMT>(x1, a.x, nx, min(kChunkBlocks, nb - nx), s1);
