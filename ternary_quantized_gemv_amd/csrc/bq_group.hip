@@ -276,12 +276,18 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, 
     }
 }
 
+// Rows of 8 lane groups per block in the wide kernel's AB array, padded to 9
+// for quarter tiles: there a wavefront's phase-B stores go to four blocks
+// (16 lanes each), and 128-float blocks would put the two blocks of each
+// half-wavefront in the same LDS banks; 144 floats put them 16 banks apart.
+constexpr int ab_rows(int rw) { return rw == 16 ? 9 : 8; }
+
 // Phase B for the wavefront whose first block is WB: with RW = 64 its lanes
 // (rows) take blocks WB and WB + 1 in turn; with RW = 32 or 16 the lanes
 // split into 64 / RW groups of RW rows, group h taking block WB + h.
 template <int FMT, int WB, int RW>
 __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float *__restrict__ D1,
-                                        float (*AB)[8][RW], const u32x4 (&v)[2], int nbc, int lane)
+                                        float (*AB)[ab_rows(RW)][RW], const u32x4 (&v)[2], int nbc, int lane)
 {
     if constexpr (WB >= kChunkBlocks) {
         return;  // RW = 16: wavefronts 8-15 have no block
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     constexpr int kChainWaves = 8 * RW / 64;
     constexpr int kBPW = RW == 64 ? 2 : 64 / RW;     // first block of wavefront w: kBPW * w
     __shared__ float T[kTableFloats];
-    __shared__ float AB[kChunkBlocks][8][RW];
+    __shared__ float AB[kChunkBlocks][ab_rows(RW)][RW];
     __shared__ float D1[kScaleFloats];
     const int wg = blockIdx.x;
     GemvDesc g = a.p[0];
