@@ -109,6 +109,14 @@ __device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restric
 template <bool ROT>
 __device__ __forceinline__ int slot_quarter(int k, int t) { return ROT ? (k + (t >> 1)) & 3 : k; }
 
+// Where slot t of a chunk is stored.  With SWZ the odd blocks' slots are
+// stored pairwise swapped (slot s of block b at b*32 + (s ^ (b & 1))), so
+// that the same slot of two neighbouring blocks falls in opposite halves of
+// the LDS banks: in the half- and quarter-tile shapes a half-wavefront reads
+// two blocks' tables at once (block_ab).
+template <bool SWZ>
+__device__ __forceinline__ int slot_pos(int t) { return SWZ ? t ^ ((t / kSlotsPerBlock) & 1) : t; }
+
 // The quantizer's per-block maximum (over the QA / V threads of an
 // activation block, group_max), its quants, and the slot's
 // 16-entry table.  Entries are sums of quants, exact in f32, formed from
@@ -128,7 +136,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     const float db = m / 127.0f;
     float f[V];
     quant_block<V>(xs.v, db, f);
-    f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(T + slot_pos<ROT>(t) * kSlotFloats);
     if constexpr (FMT == BQ_Q1_0) {
         // entry 4h + e: +-q0 +-q1 by bits 0, 1 of e, +-q2 +-q3 by bits 0, 1 of h
         float lo[4];
@@ -198,7 +206,7 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
 {
     if (t >= nbc * kSlotsPerBlock)
         return;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(T + t * kSlotFloats);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(T + slot_pos<ROT>(t) * kSlotFloats);
     if constexpr (FMT == BQ_Q1_0) {
         int p1[4], p0[4];
 #pragma unroll
@@ -242,12 +250,18 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
 
 // ab of the eight lane groups of chunk block B (payload v, activation scales
 // d1) for the calling lane's row.  B is a constant at every call (a template
-// argument or an unrolled loop index), so each table offset is an immediate.  hoff is a per-lane byte offset into the
-// table (a further block for the upper half-wave when RW = 32, else 0).
-template <int FMT>
-__device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, int B, uint32_t hoff,
-                                         float ab[8])
+// argument or an unrolled loop index), so each table offset is an immediate.
+// hoff_e / hoff_o are per-lane byte offsets into the table for even and odd
+// slots: a further block for lanes that read one (half and quarter tiles),
+// with the pairwise swap of an odd block's slots (SWZ, slot_pos) folded in;
+// B itself is even there, or the lanes share it.
+template <int FMT, bool SWZ>
+__device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, int B, uint32_t hoff_e,
+                                         uint32_t hoff_o, float ab[8])
 {
+    // position of local slot s of block B, and the lane's offset for it
+    auto pos = [&](int s) { return B * kSlotsPerBlock + (SWZ ? s ^ (B & 1) : s); };
+    auto hoff = [&](int s) { return (s & 1) ? hoff_o : hoff_e; };
     if (FMT == BQ_Q1_0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -255,7 +269,7 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, 
             const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
 #pragma unroll
             for (int L = 0; L < 8; ++L) {
-                const float t = tab(T, B * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1) + hoff);
+                const float t = tab(T, pos(j * 8 + L), nib4((L & 1) ? wb : wa, L >> 1) + hoff(j * 8 + L));
                 ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
             }
         }
@@ -268,8 +282,8 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, 
 #pragma unroll
             for (int beta = 0; beta < 4; ++beta) {
                 const int L = 4 * (m & 1) + beta;
-                const int slot = B * kSlotsPerBlock + m * 8 + 2 * beta;
-                const float sv = tab(T, slot, nib4(wa, beta) + hoff) + tab(T, slot + 1, nib4(wb, beta) + hoff);
+                const int s0 = m * 8 + 2 * beta;
+                const float sv = tab(T, pos(s0), nib4(wa, beta) + hoff(s0)) + tab(T, pos(s0 + 1), nib4(wb, beta) + hoff(s0 + 1));
                 ab[L] = j == 0 ? d1[0] * sv : __builtin_fmaf(d1[1], sv, ab[L]);
             }
         }
@@ -295,13 +309,13 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
         float ab[8];
         if (RW == 64) {
             if (WB < nbc) {
-                block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB), v[0], WB, 0u, ab);
+                block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB), v[0], WB, 0u, 0u, ab);
 #pragma unroll
                 for (int L = 0; L < 8; ++L)
                     AB[WB][L][lane] = ab[L];
             }
             if (WB + 1 < nbc) {
-                block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB + 4), v[1], WB + 1, 0u, ab);
+                block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB + 4), v[1], WB + 1, 0u, 0u, ab);
 #pragma unroll
                 for (int L = 0; L < 8; ++L)
                     AB[WB + 1][L][lane] = ab[L];
@@ -309,8 +323,12 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
         } else {
             const int h = lane / RW, r = lane % RW;
             if (WB + h < nbc) {
+                // block WB + h; WB is even, so the block is odd (its slots swapped) when h is
+                static_assert(WB % 2 == 0, "the wavefront's first block is even");
                 const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
-                block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB, hoff, ab);
+                const uint32_t swap = (h & 1) ? kSlotFloats * 4 : 0u;
+                block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB, hoff + swap,
+                                    hoff - swap, ab);
 #pragma unroll
                 for (int L = 0; L < 8; ++L)
                     AB[WB + h][L][r] = ab[L];
@@ -526,7 +544,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
     // block i of the chunk at cb: the chain step, then the request kRowsDepth ahead
     auto step = [&](int cb, int i) {
         float ab[8];
-        block_ab<FMT>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * i), p[i % kRowsDepth], i, 0u, ab);
+        block_ab<FMT, false>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * i), p[i % kRowsDepth], i, 0u, 0u, ab);
         float d0 = scale_of(sc[(i / kScalesPerGroup) % kScaleSlots], i);
         asm volatile("" : "+v"(d0));  // widen once, then full-rate fmas
 #pragma unroll
