@@ -255,7 +255,9 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
 // slots: a further block for lanes that read one (half and quarter tiles),
 // with the pairwise swap of an odd block's slots (SWZ, slot_pos) folded in;
 // B itself is even there, or the lanes share it.
-template <int FMT, bool SWZ>
+// LH >= 0 restricts the lane groups to half LH (0: lane groups 0-3, 1: 4-7);
+// only those entries of ab are written.
+template <int FMT, bool SWZ, int LH = -1>
 __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, int B, uint32_t hoff_e,
                                          uint32_t hoff_o, float ab[8])
 {
@@ -269,6 +271,8 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, 
             const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
 #pragma unroll
             for (int L = 0; L < 8; ++L) {
+                if (LH >= 0 && (L >> 2) != LH)
+                    continue;
                 const float t = tab(T, pos(j * 8 + L), nib4((L & 1) ? wb : wa, L >> 1) + hoff(j * 8 + L));
                 ab[L] = j == 0 ? t : __builtin_fmaf(d1[j], t, ab[L]);
             }
@@ -276,6 +280,8 @@ __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, 
     } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+            if (LH >= 0 && (m & 1) != LH)
+                continue;  // words 0, 2 hold lane groups 0-3, words 1, 3 lane groups 4-7
             const uint32_t wa = v[m];
             const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
             const int j = m >> 1;
@@ -298,14 +304,16 @@ constexpr int ab_rows(int rw) { return rw == 16 ? 9 : 8; }
 
 // Phase B for the wavefront whose first block is WB: with RW = 64 its lanes
 // (rows) take blocks WB and WB + 1 in turn; with RW = 32 or 16 the lanes
-// split into 64 / RW groups of RW rows, group h taking block WB + h.
-template <int FMT, int WB, int RW>
+// split into 64 / RW groups of RW rows, group h taking block WB + h; with
+// RW = 16 two wavefronts share those four blocks, LH = 0 taking lane groups
+// 0-3 and LH = 1 lane groups 4-7 (each ab depends on its own lane group
+// only), so that all sixteen wavefronts work.
+template <int FMT, int WB, int RW, int LH = -1>
 __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float *__restrict__ D1,
                                         float (*AB)[ab_rows(RW)][RW], const u32x4 (&v)[2], int nbc, int lane)
 {
-    if constexpr (WB >= kChunkBlocks) {
-        return;  // RW = 16: wavefronts 8-15 have no block
-    } else {
+    static_assert(WB < kChunkBlocks, "a block for every wavefront");
+    {
         float ab[8];
         if (RW == 64) {
             if (WB < nbc) {
@@ -327,11 +335,12 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
                 static_assert(WB % 2 == 0, "the wavefront's first block is even");
                 const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
                 const uint32_t swap = (h & 1) ? kSlotFloats * 4 : 0u;
-                block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB, hoff + swap,
-                                    hoff - swap, ab);
+                block_ab<FMT, true, LH>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB,
+                                        hoff + swap, hoff - swap, ab);
 #pragma unroll
                 for (int L = 0; L < 8; ++L)
-                    AB[WB + h][L][r] = ab[L];
+                    if (LH < 0 || (L >> 2) == LH)
+                        AB[WB + h][L][r] = ab[L];
             }
         }
     }
@@ -343,7 +352,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     static_assert(RW == 64 || RW == 32 || TPW == 1, "several units per workgroup: whole or half tiles");
     constexpr int kParts = kTileRows / RW;           // workgroups per tile
     constexpr int kChainWaves = 8 * RW / 64;
-    constexpr int kBPW = RW == 64 ? 2 : 64 / RW;     // first block of wavefront w: kBPW * w
+    constexpr int kBPW = RW == 64 ? 2 : 64 / RW;     // first block of wavefront w: kBPW * (w % kBWaves)
+    constexpr int kBWaves = kChunkBlocks / kBPW;     // wavefronts per set of the chunk's blocks (8 for RW = 16)
     __shared__ float T[kTableFloats];
     __shared__ float AB[kChunkBlocks][ab_rows(RW)][RW];
     __shared__ float D1[kScaleFloats];
@@ -399,7 +409,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             for (int i = 0; i < 2; ++i)
                 v[i] = bload(wp, ulo(t), (uint32_t)min(cb + 2 * wave + i, nb - 1) * kStep);
         } else {
-            v[0] = bload(wp, ulo(t) + (uint32_t)min(cb + kBPW * wave + h, nb - 1) * kStep, 0);
+            v[0] = bload(wp, ulo(t) + (uint32_t)min(cb + kBPW * (wave % kBWaves) + h, nb - 1) * kStep, 0);
         }
     };
     auto request_scales = [&](int t, int cb) {
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             // B (wavefront-uniform dispatch, so that every table offset is a constant)
             switch (wave) {
 #define BQ_PHASE_B(w) \
-    case w: phase_b<FMT, kBPW * (w), RW>(T, D1, AB, v, nbc, lane); break;
+    case w: phase_b<FMT, kBPW * ((w) % kBWaves), RW, (RW == 16 ? (w) / kBWaves : -1)>(T, D1, AB, v, nbc, lane); break;
                 BQ_PHASE_B(0) BQ_PHASE_B(1) BQ_PHASE_B(2) BQ_PHASE_B(3) BQ_PHASE_B(4) BQ_PHASE_B(5)
                 BQ_PHASE_B(6) BQ_PHASE_B(7) BQ_PHASE_B(8) BQ_PHASE_B(9) BQ_PHASE_B(10) BQ_PHASE_B(11)
                 BQ_PHASE_B(12) BQ_PHASE_B(13) BQ_PHASE_B(14) BQ_PHASE_B(15)
