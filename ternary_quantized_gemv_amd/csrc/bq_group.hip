@@ -99,30 +99,30 @@ __device__ __forceinline__ void load_slot(XSlot<FMT> &xs, const float *__restric
     }
 }
 
-// Thread t stores slot t's 16 entries as four 16-byte quarters, slots 64
-// bytes apart.  Stored in the same order by every lane, the quarters of
-// eight neighbouring lanes meet four to an LDS bank; with ROT, lane t stores
-// quarter (k + t/2) % 4 at step k instead, which spreads them over all
-// banks for a few more instructions and registers.  (Padding the slots
-// instead would push the far slots' table offsets past the 16-bit
-// immediate of the lookups.)
-template <bool ROT>
-__device__ __forceinline__ int slot_quarter(int k, int t) { return ROT ? (k + (t >> 1)) & 3 : k; }
+// The wide kernel's table layout (WIDE), against the plain one of the row
+// kernel, which keeps it for its registers (a second workgroup per CU):
+// - Thread t stores slot t's 16 entries as four 16-byte quarters, slots 64
+//   bytes apart.  Stored in the same order by every lane, the quarters of
+//   eight neighbouring lanes meet four to an LDS bank; lane t stores quarter
+//   (k + t/2) % 4 at step k instead, which spreads them over all banks.
+//   (Padding the slots instead would push the far slots' table offsets past
+//   the 16-bit immediate of the lookups.)
+// - The odd blocks' slots are stored pairwise swapped (slot s of block b at
+//   b*32 + (s ^ (b & 1))), so that the same slot of two neighbouring blocks
+//   falls in opposite halves of the LDS banks: in the half- and quarter-tile
+//   shapes a half-wavefront reads two blocks' tables at once (block_ab).
+template <bool WIDE>
+__device__ __forceinline__ int slot_quarter(int k, int t) { return WIDE ? (k + (t >> 1)) & 3 : k; }
 
-// Where slot t of a chunk is stored.  With SWZ the odd blocks' slots are
-// stored pairwise swapped (slot s of block b at b*32 + (s ^ (b & 1))), so
-// that the same slot of two neighbouring blocks falls in opposite halves of
-// the LDS banks: in the half- and quarter-tile shapes a half-wavefront reads
-// two blocks' tables at once (block_ab).
-template <bool SWZ>
-__device__ __forceinline__ int slot_pos(int t) { return SWZ ? t ^ ((t / kSlotsPerBlock) & 1) : t; }
+template <bool WIDE>
+__device__ __forceinline__ int slot_pos(int t) { return WIDE ? t ^ ((t / kSlotsPerBlock) & 1) : t; }
 
 // The quantizer's per-block maximum (over the QA / V threads of an
 // activation block, group_max), its quants, and the slot's
 // 16-entry table.  Entries are sums of quants, exact in f32, formed from
 // converted quants; on a Q1_0 block's first sub-block they are multiplied by
 // d1 (one rounding, as the order prescribes).
-template <int FMT, int QA, bool ROT>
+template <int FMT, int QA, bool WIDE>
 __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT> &xs, int nbc, int t)
 {
     constexpr int V = XSlot<FMT>::V, kLanes = QA / V;
@@ -136,7 +136,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
     const float db = m / 127.0f;
     float f[V];
     quant_block<V>(xs.v, db, f);
-    f32x4 *dst = reinterpret_cast<f32x4 *>(T + slot_pos<ROT>(t) * kSlotFloats);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(T + slot_pos<WIDE>(t) * kSlotFloats);
     if constexpr (FMT == BQ_Q1_0) {
         // entry 4h + e: +-q0 +-q1 by bits 0, 1 of e, +-q2 +-q3 by bits 0, 1 of h
         float lo[4];
@@ -147,7 +147,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
         const float s1 = ((t >> 3) & 3) == 0 ? db : 1.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int h = slot_quarter<ROT>(k, t);
+            const int h = slot_quarter<WIDE>(k, t);
             const float hi = ((h & 1) ? f[2] : -f[2]) + ((h & 2) ? f[3] : -f[3]);
             f32x4 v;
 #pragma unroll
@@ -161,7 +161,7 @@ __device__ __forceinline__ void build_slot(float *T, float *D1, const XSlot<FMT>
         // entry 4h + e: (e-1) q0 + (h-1) q1
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int h = slot_quarter<ROT>(k, t);
+            const int h = slot_quarter<WIDE>(k, t);
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -201,12 +201,12 @@ __device__ __forceinline__ void load_qslot(QSlot &qs, const int8_t *__restrict__
     qs.d = d[e / QA];
 }
 
-template <int FMT, bool ROT>
+template <int FMT, bool WIDE>
 __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs, int nbc, int t)
 {
     if (t >= nbc * kSlotsPerBlock)
         return;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(T + slot_pos<ROT>(t) * kSlotFloats);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(T + slot_pos<WIDE>(t) * kSlotFloats);
     if constexpr (FMT == BQ_Q1_0) {
         int p1[4], p0[4];
 #pragma unroll
@@ -218,7 +218,7 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
         const float s1 = ((t >> 3) & 3) == 0 ? qs.d : 1.0f;  // d1 on a block's first sub-block
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int h = slot_quarter<ROT>(k, t);
+            const int h = slot_quarter<WIDE>(k, t);
             const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
             f32x4 v;
 #pragma unroll
@@ -232,7 +232,7 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
         const int q0 = (int8_t)(qs.w & 0xFF), q1 = (int8_t)(qs.w >> 8);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int h = slot_quarter<ROT>(k, t);
+            const int h = slot_quarter<WIDE>(k, t);
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -251,18 +251,18 @@ __device__ __forceinline__ void build_qslot(float *T, float *D1, const QSlot &qs
 // ab of the eight lane groups of chunk block B (payload v, activation scales
 // d1) for the calling lane's row.  B is a constant at every call (a template
 // argument or an unrolled loop index), so each table offset is an immediate.
-// hoff_e / hoff_o are per-lane byte offsets into the table for even and odd
-// slots: a further block for lanes that read one (half and quarter tiles),
-// with the pairwise swap of an odd block's slots (SWZ, slot_pos) folded in;
-// B itself is even there, or the lanes share it.
+// WIDE: the wide kernel's layout (slot_pos).  hoff_e / hoff_o are per-lane
+// byte offsets into the table for even and odd slots: a further block for
+// lanes that read one (half and quarter tiles), with the pairwise swap of an
+// odd block's slots folded in; B itself is even there, or the lanes share it.
 // LH >= 0 restricts the lane groups to half LH (0: lane groups 0-3, 1: 4-7);
 // only those entries of ab are written.
-template <int FMT, bool SWZ, int LH = -1>
+template <int FMT, bool WIDE, int LH = -1>
 __device__ __forceinline__ void block_ab(const float *__restrict__ T, f32x4 d1, u32x4 v, int B, uint32_t hoff_e,
                                          uint32_t hoff_o, float ab[8])
 {
     // position of local slot s of block B, and the lane's offset for it
-    auto pos = [&](int s) { return B * kSlotsPerBlock + (SWZ ? s ^ (B & 1) : s); };
+    auto pos = [&](int s) { return B * kSlotsPerBlock + (WIDE ? s ^ (B & 1) : s); };
     auto hoff = [&](int s) { return (s & 1) ? hoff_o : hoff_e; };
     if (FMT == BQ_Q1_0) {
 #pragma unroll
@@ -313,35 +313,33 @@ __device__ __forceinline__ void phase_b(const float *__restrict__ T, const float
                                         float (*AB)[ab_rows(RW)][RW], const u32x4 (&v)[2], int nbc, int lane)
 {
     static_assert(WB < kChunkBlocks, "a block for every wavefront");
-    {
-        float ab[8];
-        if (RW == 64) {
-            if (WB < nbc) {
-                block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB), v[0], WB, 0u, 0u, ab);
+    float ab[8];
+    if (RW == 64) {
+        if (WB < nbc) {
+            block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB), v[0], WB, 0u, 0u, ab);
 #pragma unroll
-                for (int L = 0; L < 8; ++L)
-                    AB[WB][L][lane] = ab[L];
-            }
-            if (WB + 1 < nbc) {
-                block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB + 4), v[1], WB + 1, 0u, 0u, ab);
+            for (int L = 0; L < 8; ++L)
+                AB[WB][L][lane] = ab[L];
+        }
+        if (WB + 1 < nbc) {
+            block_ab<FMT, true>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * WB + 4), v[1], WB + 1, 0u, 0u, ab);
 #pragma unroll
-                for (int L = 0; L < 8; ++L)
-                    AB[WB + 1][L][lane] = ab[L];
-            }
-        } else {
-            const int h = lane / RW, r = lane % RW;
-            if (WB + h < nbc) {
-                // block WB + h; WB is even, so the block is odd (its slots swapped) when h is
-                static_assert(WB % 2 == 0, "the wavefront's first block is even");
-                const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
-                const uint32_t swap = (h & 1) ? kSlotFloats * 4 : 0u;
-                block_ab<FMT, true, LH>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB,
-                                        hoff + swap, hoff - swap, ab);
+            for (int L = 0; L < 8; ++L)
+                AB[WB + 1][L][lane] = ab[L];
+        }
+    } else {
+        const int h = lane / RW, r = lane % RW;
+        if (WB + h < nbc) {
+            // block WB + h; WB is even, so the block is odd (its slots swapped) when h is
+            static_assert(WB % 2 == 0, "the wavefront's first block is even");
+            const uint32_t hoff = (uint32_t)h * (kSlotsPerBlock * kSlotFloats * 4);
+            const uint32_t swap = (h & 1) ? kSlotFloats * 4 : 0u;
+            block_ab<FMT, true, LH>(T, *reinterpret_cast<const f32x4 *>(D1 + 4 * (WB + h)), v[0], WB, hoff + swap,
+                                    hoff - swap, ab);
 #pragma unroll
-                for (int L = 0; L < 8; ++L)
-                    if (LH < 0 || (L >> 2) == LH)
-                        AB[WB + h][L][r] = ab[L];
-            }
+            for (int L = 0; L < 8; ++L)
+                if (LH < 0 || (L >> 2) == LH)
+                    AB[WB + h][L][r] = ab[L];
         }
     }
 }
