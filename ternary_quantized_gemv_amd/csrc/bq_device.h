@@ -128,31 +128,64 @@ __device__ __forceinline__ void quantize_chunk(int8_t *Qs, float *Ds, const floa
 // Q1_0: slot t of a chunk covers chunk values 4t..4t+3 (block t/32, sub-block
 // (t/8)%4, lane t%8).  Entry n = 4h + e: s = sum_i (bit i of n ? q_i : -q_i),
 // where the negation of -128 stays -128; on sub-block 0 the entry is d1*s.
+// One quarter (entries 4h .. 4h+3) of Q1_0 slot t from its four quants w4
+// and, on sub-block 0, the activation scale d1.
+__device__ __forceinline__ void quarter_q1(float *T, int t, int h, uint32_t w4, float d1)
+{
+    int p1[4], p0[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int v = (int8_t)(w4 >> (8 * i));
+        p1[i] = v;
+        p0[i] = v == -128 ? -128 : -v;
+    }
+    const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
+    const bool first = ((t >> 3) & 3) == 0;
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int lo = ((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]);
+        const float sf = (float)(lo + hi);
+        v[e] = first ? d1 * sf : sf;
+    }
+    reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
+}
+
+// A full chunk built by a workgroup of kThreads takes kIt steps per thread,
+// in batches of kBatch: a batch's quants (and scales) are all requested
+// before the first is used, so the build waits for memory once per batch
+// rather than once per step.  (Larger batches hold more registers than two
+// workgroups per CU leave.)
+constexpr int kTableBatch = 4;
+
 template <int QA>
 __device__ void build_table_q1(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
 {
     const int nquarters = nbc * kSlotsPerBlock * 4;
-    for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
-        const int t = u >> 2, h = u & 3;
-        const uint32_t w4 = *reinterpret_cast<const uint32_t *>(q + k0 + 4 * t);
-        int p1[4], p0[4];
+    constexpr int kIt = kChunkBlocks * kSlotsPerBlock * 4 / kThreads;
+    if (nbc == kChunkBlocks && blockDim.x == kThreads) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int v = (int8_t)(w4 >> (8 * i));
-            p1[i] = v;
-            p0[i] = v == -128 ? -128 : -v;
-        }
-        const int hi = ((h & 1) ? p1[2] : p0[2]) + ((h & 2) ? p1[3] : p0[3]);
-        const bool first = ((t >> 3) & 3) == 0;
-        const float d1 = first ? d[(k0 + 4 * t) / QA] : 0.0f;
-        f32x4 v;
+        for (int i0 = 0; i0 < kIt; i0 += kTableBatch) {
+            uint32_t w4[kTableBatch];
+            float d1[kTableBatch];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int lo = ((e & 1) ? p1[0] : p0[0]) + ((e & 2) ? p1[1] : p0[1]);
-            const float sf = (float)(lo + hi);
-            v[e] = first ? d1 * sf : sf;
+            for (int i = 0; i < kTableBatch; ++i) {
+                const int t = (threadIdx.x + (i0 + i) * kThreads) >> 2;
+                w4[i] = *reinterpret_cast<const uint32_t *>(q + k0 + 4 * t);
+                d1[i] = ((t >> 3) & 3) == 0 ? d[(k0 + 4 * t) / QA] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < kTableBatch; ++i) {
+                const int u = threadIdx.x + (i0 + i) * kThreads;
+                quarter_q1(T, u >> 2, u & 3, w4[i], d1[i]);
+            }
         }
-        reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
+    } else {
+        for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
+            const int t = u >> 2;
+            const float d1 = ((t >> 3) & 3) == 0 ? d[(k0 + 4 * t) / QA] : 0.0f;
+            quarter_q1(T, t, u & 3, *reinterpret_cast<const uint32_t *>(q + k0 + 4 * t), d1);
+        }
     }
     for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x)
         D1[i] = d[(k0 + 32 * i) / QA];
@@ -161,19 +194,37 @@ __device__ void build_table_q1(float *T, float *D1, const int8_t *q, const float
 // Q2_0: slot t of a chunk covers chunk values 2t and 2t+1 (the low or high
 // nibble of payload byte t/2 of its block).  Entry n = 4h + e holds the codes
 // (e, h): (e-1)*q_2t + (h-1)*q_2t+1.
+__device__ __forceinline__ void quarter_q2(float *T, int t, int h, uint32_t w2)
+{
+    const int qa0 = (int8_t)(w2 & 0xFF), qa1 = (int8_t)(w2 >> 8);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
+    reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
+}
+
 template <int QA>
 __device__ void build_table_q2(float *T, float *D1, const int8_t *q, const float *d, int k0, int nbc)
 {
     const int nquarters = nbc * kSlotsPerBlock * 4;
-    for (int u = threadIdx.x; u < nquarters; u += blockDim.x) {
-        const int t = u >> 2, h = u & 3;
-        const uint32_t w2 = *reinterpret_cast<const uint16_t *>(q + k0 + 2 * t);
-        const int qa0 = (int8_t)(w2 & 0xFF), qa1 = (int8_t)(w2 >> 8);
-        f32x4 v;
+    constexpr int kIt = kChunkBlocks * kSlotsPerBlock * 4 / kThreads;
+    if (nbc == kChunkBlocks && blockDim.x == kThreads) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            v[e] = (float)((e - 1) * qa0 + (h - 1) * qa1);
-        reinterpret_cast<f32x4 *>(T + t * kSlotFloats)[h] = v;
+        for (int i0 = 0; i0 < kIt; i0 += kTableBatch) {
+            uint32_t w2[kTableBatch];
+#pragma unroll
+            for (int i = 0; i < kTableBatch; ++i)
+                w2[i] = *reinterpret_cast<const uint16_t *>(q + k0 + 2 * ((threadIdx.x + (i0 + i) * kThreads) >> 2));
+#pragma unroll
+            for (int i = 0; i < kTableBatch; ++i) {
+                const int u = threadIdx.x + (i0 + i) * kThreads;
+                quarter_q2(T, u >> 2, u & 3, w2[i]);
+            }
+        }
+    } else {
+        for (int u = threadIdx.x; u < nquarters; u += blockDim.x)
+            quarter_q2(T, u >> 2, u & 3, *reinterpret_cast<const uint16_t *>(q + k0 + 2 * (u >> 2)));
     }
     // d1 per (block, sub-block): D1[4b + j], j = 0, 1.
     for (int i = threadIdx.x; i < nbc * 4; i += blockDim.x) {

@@ -375,10 +375,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(GemvDesc g, int64_t ld_
 }
 
 // Tiles tpw * blockIdx.x .. + tpw - 1 (tpw <= kWaves) of activation column
-// blockIdx.y, one per wavefront.
+// blockIdx.y, one per wavefront.  (The second bound: see sweep_kernel.)
 template <int FMT, int QA>
-__global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d,
-                                                                          int tiles, int tpw)
+__global__ __launch_bounds__(kThreads, 4) void matvec_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int tiles,
+                                                             int tpw)
 {
     __shared__ float T[kTableFloats];
     __shared__ float D1[kScaleFloats];
@@ -390,17 +390,17 @@ __global__ __launch_bounds__(kThreads, QA < 128 ? 4 : 1) void matvec_kernel(Gemv
     run_item<FMT, QA, false>(g, tile0, min(tpw, tiles - tile0), T, D1, nullptr, nullptr);
 }
 
-// With activation blocks shorter than 128 values the chunk's activation
-// scales come from LDS, and the compiler would keep more of them in flight
-// than four wavefronts per SIMD (two workgroups per CU) leave room for; the
-// second bound holds those instantiations to 128 registers.  The qa-128
-// code is unaffected.
+// The second bound holds every instantiation to 128 registers, four
+// wavefronts per SIMD (two workgroups per CU): with activation blocks
+// shorter than 128 values the chunk's activation scales come from LDS and
+// the compiler would keep more of them in flight; with qa 128 the table
+// build's batched requests would take the 129th register (the bound moves
+// one value of the chunk loop's prologue to scratch instead).
 // X: the products' activations are f32 and every workgroup quantizes the
-// chunks it needs (the quantizer's bits) into LDS before building its table;
-// the bound keeps those instantiations at four wavefronts per SIMD too.
+// chunks it needs (the quantizer's bits) into LDS before building its table.
 template <int FMT, int QA, bool X>
-__global__ __launch_bounds__(kThreads, QA < 128 || X ? 4 : 1) void sweep_kernel(const GemvDesc *__restrict__ descs,
-                                                         const WorkItem *__restrict__ items)
+__global__ __launch_bounds__(kThreads, 4) void sweep_kernel(const GemvDesc *__restrict__ descs,
+                                                            const WorkItem *__restrict__ items)
 {
     constexpr int kChunkValues = kChunkBlocks * (FMT == BQ_Q1_0 ? 128 : 64);
     __shared__ float T[kTableFloats];
