@@ -70,7 +70,7 @@ hipError_t launch_splitcols(int fmt, int shape, int qa, const GemvDesc &g, int64
 hipError_t launch_mfma(int fmt, int shape, int qa, const GemvDesc &g, int64_t ld_q, int64_t ld_d, int ncols,
                        hipStream_t st);
 // launch_group: a group of products sharing one f32 activation, quantized
-// inside the kernel (bq_group.hip), in one of three workgroup shapes:
+// inside the kernel (bq_group.hip), in one of these workgroup shapes:
 enum GroupShape {
     kShapeQuarter = 0,  // a quarter tile (16 rows) per sixteen-wavefront workgroup
     kShapeHalf = 1,     // half a tile (32 rows) per sixteen-wavefront workgroup

@@ -64,6 +64,24 @@ def test_pack_layout():
     assert not sc[:, 1, :, 2:].any()  # padded blocks 10..15
 
 
+@pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
+def test_pack_layout_block_order(fmt):
+    """Both formats keep every block of a tile in row order, across tiles of
+    several eight-tile groups, full 32-block chunks and a partial one."""
+    rows, nb = 64 * 17 + 5, 70
+    cols = nb * bq.BLOCK_LEN[fmt]
+    w = synth.blocks(fmt, rows, cols, 5)
+    bits, scales = bq.bq_pack(fmt, w, rows, cols)
+    words = bits.view("<u4").reshape(18, nb, 64, 4)
+    for r in (0, 63, 64 * 8, 64 * 8 + 7, 64 * 16 + 3, rows - 1):
+        t, lane = divmod(r, 64)
+        for b in (0, 5, 24, 31, 32, 40, 63, 64, 69):
+            canon = w[r, b, 2:].copy().view("<u4").astype(np.uint64)
+            expect = (((canon << 2) | (canon >> 30)) & 0xFFFFFFFF).astype(np.uint32)
+            assert np.array_equal(words[t, b, lane], expect), (r, b)
+    assert np.array_equal(bq.bq_unpack(fmt, bits, scales, rows, cols), w)
+
+
 @pytest.mark.parametrize("call,args,code", [
     ("bq_packed_bytes", (3, 4, 128), bq.BQ_EARG),
     ("bq_packed_bytes", (1, 0, 128), bq.BQ_EARG),

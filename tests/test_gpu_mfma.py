@@ -107,13 +107,16 @@ def test_mfma_q2_code3(mfma_path):
     assert_parity(matvec_gpu(Q2, w, rows, cols, q, d, qa), y_ref, "mfma Q2_0 code 3")
 
 
-@pytest.mark.parametrize("fmt,rows,ncols", [(Q1, 20000, 16), (Q1, 70000, 8), (Q1, 70000, 6), (Q1, 70000, 3),
-                                             (Q2, 20000, 12), (Q2, 70000, 16), (Q2, 70000, 4), (Q2, 70000, 5)])
-def test_batch_paths_agree(fmt, rows, ncols):
+@pytest.mark.parametrize("fmt,rows,ncols,cols", [(Q1, 20000, 16, 1024), (Q1, 70000, 8, 1024), (Q1, 70000, 6, 1024),
+                                                  (Q1, 70000, 3, 1024), (Q2, 20000, 12, 1024), (Q2, 70000, 16, 1024),
+                                                  (Q2, 70000, 4, 1024), (Q2, 70000, 5, 1024),
+                                                  # Q2_0 rows of one full 32-block chunk
+                                                  (Q2, 70000, 6, 2048), (Q2, 20000, 5, 2048)])
+def test_batch_paths_agree(fmt, rows, ncols, cols):
     """Both small-batch paths and the automatic choice give the same bits,
     and the same as the oracle."""
     bq = bqmod()
-    cols, qa = 1024, 128
+    qa = 128
     w, q, d = _inputs(fmt, rows, cols, ncols, qa, "quant", 67)
     ys = []
     for path in (bq.BQ_BATCH_TABLES, bq.BQ_BATCH_MFMA, bq.BQ_BATCH_AUTO):

@@ -240,6 +240,9 @@ FULL = [
     # one row per lane with fewer than eight tiles per workgroup: 2374 tiles (five per workgroup),
     # 2051 ragged tiles (five, the last workgroup one), 2188 tiles of two table chunks each
     (Q2, 151936, 4096), (Q1, 131201, 1024), (Q2, 140001, 4096),
+    # Q2_0 rows of one full 32-block chunk: the four-wavefront split (700 tiles), two tiles per wide
+    # workgroup (438 tiles), one row per lane (1094 tiles)
+    (Q2, 44800, 2048), (Q2, 28000, 2048), (Q2, 70000, 2048),
 ]
 
 
@@ -375,6 +378,15 @@ def test_sweep_q2_0_decode_token():
 def test_sweep_ragged_mix():
     shapes = [("a", 1, 128), ("b", 100, 33 * 128), ("c", 65, 4096), ("d", 700, 12288), ("e", 64, 256)]
     _check_sweep(Q1, shapes, seed=63)
+
+
+def test_sweep_ragged_mix_q2():
+    """Q2_0 rows of one full 32-block chunk over 18 and 79 tiles (the
+    single-chunk walk, several tiles per wavefront), a full chunk and a
+    partial one, three full chunks and a partial one, and a row shorter than
+    a chunk."""
+    shapes = [("a", 1100, 2048), ("b", 700, 33 * 64), ("c", 1000, 100 * 64), ("d", 64, 64), ("e", 5000, 2048)]
+    _check_sweep(Q2, shapes, seed=64, qa=64)
 
 
 def test_gpu_errors_are_reported():
