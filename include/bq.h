@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 7
+#define BQ_ABI_VERSION 8
 
 /* Weight formats (one canonical block = 18 bytes: f16 scale, little-endian,
  * then 16 payload bytes).

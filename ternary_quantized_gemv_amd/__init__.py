@@ -22,7 +22,7 @@ BQ_Q1_0 = 1
 BQ_Q2_0 = 2
 BQ_OK, BQ_EARG, BQ_EALIGN, BQ_EHIP, BQ_ENOMEM = 0, 1, 2, 3, 4
 BQ_FLOOR_SINK_WORDS = 8192
-BQ_ABI_VERSION = 7  # include/bq.h
+BQ_ABI_VERSION = 8  # include/bq.h
 BQ_BATCH_AUTO, BQ_BATCH_TABLES, BQ_BATCH_MFMA = 0, 1, 2
 BLOCK_LEN = {BQ_Q1_0: 128, BQ_Q2_0: 64}
 BLOCK_BYTES = 18

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kColsWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int tile = rb * kColsWaves + wave;
     const bool live = tile < tiles;
     // a wavefront past the last tile reads the workgroup's first tile and stores nothing
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)(live ? tile : rb * kColsWaves) * g.nb * kTileRows);
+    const rsrc_t wp = rsrc_of(g.bits + tile_block0(FMT, live ? tile : rb * kColsWaves, g.nb) * kTileRows);
     const rsrc_t sp = rsrc_of(g.scales + (int64_t)(live ? tile : rb * kColsWaves) * g.ng * kTileRows);
     const uint32_t lo = (uint32_t)lane * 16;
     const int bl = FMT == BQ_Q1_0 ? 128 : 64;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int
     const bool live = tile < tiles;
     // a wavefront past the last tile reads the workgroup's first tile and stores nothing
     const int rt = live ? tile : rb * TPW;
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)rt * g.nb * kTileRows);
+    const rsrc_t wp = rsrc_of(g.bits + tile_block0(FMT, rt, g.nb) * kTileRows);
     const rsrc_t sp = rsrc_of(g.scales + (int64_t)rt * g.ng * kTileRows);
     const uint32_t lo = (uint32_t)lane * 16;
     const int bl = FMT == BQ_Q1_0 ? 128 : 64;

@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     auto ulo = [&](int t) { return (uint32_t)(upart(t) * RW + r) * 16; };
     const int nb = g.nb, ng = g.ng;
     // a tile past the product's last one re-reads the last tile and stores nothing
-    auto wtile = [&](int t) { return rsrc_of(g.bits + (int64_t)min(utile(t), tiles - 1) * g.nb * kTileRows); };
+    auto wtile = [&](int t) { return rsrc_of(g.bits + tile_block0(FMT, min(utile(t), tiles - 1), g.nb) * kTileRows); };
     auto stile = [&](int t) { return rsrc_of(g.scales + (int64_t)min(utile(t), tiles - 1) * g.ng * kTileRows); };
 
     // Requests in the order of use (vector memory counts complete in order);
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_kernel(GroupArgs a)
     const bool busy = wave < a.rows_tpw;
     const int tile = (wg - wg0) * a.rows_tpw + wave;
     const int tl = min(tile, tiles - 1);
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)tl * g.nb * kTileRows);
+    const rsrc_t wp = rsrc_of(g.bits + tile_block0(FMT, tl, g.nb) * kTileRows);
     const rsrc_t sp = rsrc_of(g.scales + (int64_t)tl * g.ng * kTileRows);
     const uint32_t lo = (uint32_t)lane * 16;
     const int nb = g.nb, ng = g.ng;

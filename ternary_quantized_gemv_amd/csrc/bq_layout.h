@@ -15,6 +15,13 @@
 //     right rotation by 4, so that masking a byte with 0x3C yields
 //     nibble * 4, a byte offset into a table of 16 floats.
 //     One wavefront reads one block of its 64 rows as 1 KiB contiguous.
+//     Q2_0 only: after every eight tiles the plane leaves a gap of
+//     kGroupGap blocks, so tile t starts at block t * nb + 7 * (t / 8)
+//     (tile_block0).  Wavefronts that walk neighbouring tiles' rows in step
+//     then request different low address bits in each group of eight tiles
+//     (measured: the Q2_0 token sweep 2.7% faster; the Q1_0 sweep, slower
+//     with every such shift tried, has no gaps).  The gaps are zero and
+//     never read.
 //
 //   scale plane, u16 (f16 bit patterns): [tile][block / 8][lane][block % 8]
 //     blocks padded to a multiple of 8 with zero scales; one 16-byte load per
@@ -41,6 +48,12 @@ inline bool tile_fits(int64_t nb) { return nb * kTileRows * kPayloadBytes <= kMa
 inline int block_len(int fmt) { return fmt == 1 ? 128 : fmt == 2 ? 64 : 0; }
 inline int64_t tiles_of(int64_t rows) { return (rows + kTileRows - 1) / kTileRows; }
 inline int64_t groups_of(int64_t nb) { return (nb + kScalesPerGroup - 1) / kScalesPerGroup; }
+
+// First block of tile t in the payload plane, and the plane's length in
+// blocks for `tiles` tiles.
+constexpr int64_t kGroupGap = 7;
+constexpr int64_t tile_block0(int fmt, int64_t t, int64_t nb) { return t * nb + (fmt == 2 ? kGroupGap * (t >> 3) : 0); }
+inline int64_t payload_blocks(int fmt, int64_t tiles, int64_t nb) { return tile_block0(fmt, tiles - 1, nb) + nb; }
 
 inline uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
 inline uint32_t rotr32(uint32_t x, int r) { return (x >> r) | (x << (32 - r)); }

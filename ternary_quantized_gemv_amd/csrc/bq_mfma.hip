@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kMfWaves * 64) __attribute__((amdgpu_waves_per_eu(3
     const bool live = nt < ntiles;
     const int ntc = live ? nt : rg * NTW;  // a wavefront past the last tile repeats the first and stores nothing
     const int kh = lane >> 5;
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)(ntc >> 1) * g.nb * kTileRows);
+    const rsrc_t wp = rsrc_of(g.bits + tile_block0(FMT, ntc >> 1, g.nb) * kTileRows);
     const rsrc_t sp = rsrc_of(g.scales + (int64_t)(ntc >> 1) * g.ng * kTileRows);
     const uint32_t lo = (uint32_t)((ntc & 1) * 32 + (lane & 31)) * 16;
     // Q1_0: rotate right by 8h - 1 (even lane groups) and 8h + 3 (odd); Q2_0: 16h and 16h + 4.

@@ -4,7 +4,8 @@
 // section "kernels.rs") repacks weights once and activations per call, with
 // the numbers unchanged; here the 18 bytes of every block are kept (the f16
 // scales are not widened) and only re-ordered so that a wavefront reads its
-// 64 rows' block as one contiguous 1 KiB.
+// 64 rows' block as one contiguous 1 KiB (Q2_0 tiles in groups of eight
+// with a gap after each group: tile_block0).
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -62,7 +63,7 @@ BQ_EXPORT int bq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols, size_t *b
         return set_error(BQ_EARG, "bq_packed_bytes: null output pointer");
     int64_t nb = cols / block_len(fmt);
     int64_t tiles = tiles_of(rows);
-    *bits_bytes = (size_t)(tiles * nb * kTileRows * kPayloadBytes);
+    *bits_bytes = (size_t)(payload_blocks(fmt, tiles, nb) * kTileRows * kPayloadBytes);
     *scale_bytes = (size_t)(tiles * groups_of(nb) * kTileRows * kScalesPerGroup * 2);
     return BQ_OK;
 }
@@ -79,7 +80,7 @@ BQ_EXPORT int bq_pack(int32_t fmt, const uint8_t *canon, int64_t rows, int64_t c
     const int64_t tiles = tiles_of(rows);
     const int64_t ng = groups_of(nb);
     uint32_t *words = static_cast<uint32_t *>(bits_out);
-    memset(words, 0, (size_t)(tiles * nb * kTileRows * kPayloadBytes));
+    memset(words, 0, (size_t)(payload_blocks(fmt, tiles, nb) * kTileRows * kPayloadBytes));
     memset(scales_out, 0, (size_t)(tiles * ng * kTileRows * kScalesPerGroup * 2));
     for (int64_t r = 0; r < rows; ++r) {
         const int64_t t = r / kTileRows, lane = r % kTileRows;
@@ -88,7 +89,7 @@ BQ_EXPORT int bq_pack(int32_t fmt, const uint8_t *canon, int64_t rows, int64_t c
             uint16_t sc = (uint16_t)(blk[0] | (blk[1] << 8));
             scales_out[((t * ng + b / kScalesPerGroup) * kTileRows + lane) * kScalesPerGroup +
                        b % kScalesPerGroup] = sc;
-            uint32_t *dst = words + ((t * nb + b) * kTileRows + lane) * 4;
+            uint32_t *dst = words + ((tile_block0(fmt, t, nb) + b) * kTileRows + lane) * 4;
             for (int j = 0; j < 4; ++j) {
                 const uint8_t *p = blk + 2 + 4 * j;
                 uint32_t w = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
@@ -119,7 +120,7 @@ BQ_EXPORT int bq_unpack(int32_t fmt, const void *bits, const uint16_t *scales, i
                                  b % kScalesPerGroup];
             blk[0] = (uint8_t)(sc & 0xFF);
             blk[1] = (uint8_t)(sc >> 8);
-            const uint32_t *src = words + ((t * nb + b) * kTileRows + lane) * 4;
+            const uint32_t *src = words + ((tile_block0(fmt, t, nb) + b) * kTileRows + lane) * 4;
             for (int j = 0; j < 4; ++j) {
                 uint32_t w = rotr32(src[j], 2);
                 for (int i = 0; i < 4; ++i)

@@ -65,7 +65,7 @@ __device__ __forceinline__ void run_split(const GemvDesc &g, int tile0, int ntil
     const int tile = tile0 + tl;
     const bool live = tl < ntiles;
     // a wavefront past the last tile reads the first tile and stores nothing
-    const rsrc_t wp = rsrc_of(g.bits + (int64_t)(live ? tile : tile0) * g.nb * kTileRows);
+    const rsrc_t wp = rsrc_of(g.bits + tile_block0(FMT, live ? tile : tile0, g.nb) * kTileRows);
     const rsrc_t sp = rsrc_of(g.scales + (int64_t)(live ? tile : tile0) * g.ng * kTileRows);
     const uint32_t lo = (uint32_t)lane * 16;
     const uint32_t sh = FMT == BQ_Q1_0 ? 8u * (k >> 1) + 4u * (k & 1) : 8u * k;

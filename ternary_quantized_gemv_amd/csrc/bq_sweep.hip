@@ -288,7 +288,7 @@ __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntile
     const int per_chunk = FMT == BQ_Q1_0 ? 128 * kChunkBlocks : 64 * kChunkBlocks;
     const int tend = tile0 + ntiles;
     const uint32_t lo = (uint32_t)lane * 16;
-    auto wtile = [&](int tile, int cb) { return rsrc_of(g.bits + ((int64_t)tile * g.nb + cb) * kTileRows); };
+    auto wtile = [&](int tile, int cb) { return rsrc_of(g.bits + (tile_block0(FMT, tile, g.nb) + cb) * kTileRows); };
     auto stile = [&](int tile, int cb) { return rsrc_of(g.scales + ((int64_t)tile * g.ng + cb / 8) * kTileRows); };
     float acc[8];
     Prefetch pf;

@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 7
+    assert bq.bq_abi_version() == bq.BQ_ABI_VERSION == 8
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
@@ -40,7 +40,8 @@ def test_pack_roundtrip(fmt, rows, nb):
     bits, scales = bq.bq_pack(fmt, w, rows, cols)
     nbits, nsc = bq.bq_packed_bytes(fmt, rows, cols)
     tiles = -(-rows // 64)
-    assert bits.nbytes == nbits == tiles * 64 * nb * 16
+    gaps = 7 * ((tiles - 1) // 8) if fmt == bq.BQ_Q2_0 else 0  # Q2_0: 7 blocks after every eight tiles
+    assert bits.nbytes == nbits == (tiles * nb + gaps) * 64 * 16
     assert scales.nbytes == nsc == tiles * 64 * (-(-nb // 8)) * 16
     assert np.array_equal(bq.bq_unpack(fmt, bits, scales, rows, cols), w)
 
@@ -65,20 +66,26 @@ def test_pack_layout():
 
 
 @pytest.mark.parametrize("fmt", [bq.BQ_Q1_0, bq.BQ_Q2_0])
-def test_pack_layout_block_order(fmt):
-    """Both formats keep every block of a tile in row order, across tiles of
-    several eight-tile groups, full 32-block chunks and a partial one."""
+def test_pack_layout_tile_groups(fmt):
+    """Tile t's block b starts at block t * nb + b of the payload plane, plus,
+    for Q2_0, a gap of 7 zero blocks after every eight tiles (t * nb + 7 *
+    (t // 8) + b); blocks stay in row order.  18 tiles (three groups), rows
+    of two full 32-block chunks and a partial one."""
     rows, nb = 64 * 17 + 5, 70
     cols = nb * bq.BLOCK_LEN[fmt]
     w = synth.blocks(fmt, rows, cols, 5)
     bits, scales = bq.bq_pack(fmt, w, rows, cols)
-    words = bits.view("<u4").reshape(18, nb, 64, 4)
+    gap = 7 if fmt == bq.BQ_Q2_0 else 0
+    blocks = bits.view("<u4").reshape(-1, 64, 4)
+    assert len(blocks) == 18 * nb + 2 * gap
     for r in (0, 63, 64 * 8, 64 * 8 + 7, 64 * 16 + 3, rows - 1):
         t, lane = divmod(r, 64)
         for b in (0, 5, 24, 31, 32, 40, 63, 64, 69):
             canon = w[r, b, 2:].copy().view("<u4").astype(np.uint64)
             expect = (((canon << 2) | (canon >> 30)) & 0xFFFFFFFF).astype(np.uint32)
-            assert np.array_equal(words[t, b, lane], expect), (r, b)
+            assert np.array_equal(blocks[t * nb + gap * (t // 8) + b, lane], expect), (r, b)
+    for g in (1, 2):  # the gaps are zero
+        assert not blocks[g * 8 * nb + (g - 1) * gap:g * 8 * nb + g * gap].any()
     assert np.array_equal(bq.bq_unpack(fmt, bits, scales, rows, cols), w)
 
 
