@@ -137,8 +137,11 @@ const char *bq_last_error(void);
  * (unknown fmt; rows or cols not in [1, 2^31); cols not a multiple of the
  * block length; a 64-row tile's payload above 2^31 - 16 bytes; a null output
  * pointer) with nothing written.  The sizes come back through pointers so
- * that the result is a return code like every other call.  Host only;
- * touches no GPU. */
+ * that the result is a return code like every other call.  The planes'
+ * layout belongs to the library and changes with BQ_ABI_VERSION (the
+ * payload plane may hold unused zero padding between groups of row tiles):
+ * size buffers with this call, not with a formula.  Host only; touches no
+ * GPU. */
 int bq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols, size_t *bits_bytes, size_t *scale_bytes);
 
 /* Repack canonical blocks into the device layout (bankML "gpu/", section
