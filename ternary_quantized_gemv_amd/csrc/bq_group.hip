@@ -353,7 +353,11 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
     constexpr int kBPW = RW == 64 ? 2 : 64 / RW;     // first block of wavefront w: kBPW * (w % kBWaves)
     constexpr int kBWaves = kChunkBlocks / kBPW;     // wavefronts per set of the chunk's blocks (8 for RW = 16)
     __shared__ float T[kTableFloats];
-    __shared__ float AB[kChunkBlocks][ab_rows(RW)][RW];
+    // half tiles in turn (RW = 32, TPW > 1): two ab buffers, so that unit
+    // t + 1's phase B (buffer (t + 1) & 1) needs no barrier after unit t's
+    // phase C (buffer t & 1); 128.5 KiB of LDS with the table
+    constexpr int kABBufs = RW == 32 && TPW > 1 ? 2 : 1;
+    __shared__ float AB[kABBufs * kChunkBlocks][ab_rows(RW)][RW];
     __shared__ float D1[kScaleFloats];
     const int wg = blockIdx.x;
     GemvDesc g = a.p[0];
@@ -441,10 +445,11 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
         for (int t = 0; t < TPW; ++t) {
             // the unit after (tile t, this chunk): the next tile, or the first tile of the next chunk
             const int tn = t + 1 < TPW ? t + 1 : 0, cn = t + 1 < TPW ? cb : nx;
+            float(*ABt)[ab_rows(RW)][RW] = AB + (kABBufs == 2 ? (t & 1) * kChunkBlocks : 0);
             // B (wavefront-uniform dispatch, so that every table offset is a constant)
             switch (wave) {
 #define BQ_PHASE_B(w) \
-    case w: phase_b<FMT, kBPW * ((w) % kBWaves), RW, (RW == 16 ? (w) / kBWaves : -1)>(T, D1, AB, v, nbc, lane); break;
+    case w: phase_b<FMT, kBPW * ((w) % kBWaves), RW, (RW == 16 ? (w) / kBWaves : -1)>(T, D1, ABt, v, nbc, lane); break;
                 BQ_PHASE_B(0) BQ_PHASE_B(1) BQ_PHASE_B(2) BQ_PHASE_B(3) BQ_PHASE_B(4) BQ_PHASE_B(5)
                 BQ_PHASE_B(6) BQ_PHASE_B(7) BQ_PHASE_B(8) BQ_PHASE_B(9) BQ_PHASE_B(10) BQ_PHASE_B(11)
                 BQ_PHASE_B(12) BQ_PHASE_B(13) BQ_PHASE_B(14) BQ_PHASE_B(15)
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
                 float abv[kChunkBlocks];
 #pragma unroll
                 for (int b = 0; b < kChunkBlocks; ++b)
-                    abv[b] = AB[b][L][r];
+                    abv[b] = ABt[b][L][r];
 #pragma unroll
                 for (int b = 0; b < kChunkBlocks; ++b) {
                     const float next = __builtin_fmaf(scale_of(sc[b / kScalesPerGroup], b), abv[b], acc[t]);
@@ -468,7 +473,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
                 }
             }
             request_scales(tn, cn);
-            if (t + 1 < TPW)
+            if (t + 1 < TPW && kABBufs == 1)
                 __syncthreads();  // this phase C reads AB before the next tile's phase B writes it
             // after the last tile: the next chunk's phase A writes only T and D1,
             // and its barrier orders this phase C before the next phase B
