@@ -479,19 +479,23 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(GroupArgs a)
             // and its barrier orders this phase C before the next phase B
         }
     }
+    // the units' eight lane accumulators through AB (slot t for unit t),
+    // then wavefront t forms unit t's tree
+    static_assert(TPW <= kChunkBlocks && TPW <= kWideWaves, "one AB slot and one wavefront per unit");
+    __syncthreads();  // every phase C has read AB
+    if (wave < kChainWaves) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        __syncthreads();
-        if (wave < kChainWaves)
-            AB[0][L][r] = acc[t];
-        __syncthreads();
-        if (wave == 0 && lane < RW && utile(t) < tiles) {
-            const int row = utile(t) * kTileRows + upart(t) * RW + lane;
-            const float y = ((AB[0][0][lane] + AB[0][4][lane]) + (AB[0][2][lane] + AB[0][6][lane])) +
-                            ((AB[0][1][lane] + AB[0][5][lane]) + (AB[0][3][lane] + AB[0][7][lane]));
-            if (row < g.rows)
-                g.y[row] = y;
-        }
+        for (int t = 0; t < TPW; ++t)
+            AB[t][L][r] = acc[t];
+    }
+    __syncthreads();
+    if (wave < TPW && lane < RW && utile(wave) < tiles) {
+        const int t = wave;
+        const int row = utile(t) * kTileRows + upart(t) * RW + lane;
+        const float y = ((AB[t][0][lane] + AB[t][4][lane]) + (AB[t][2][lane] + AB[t][6][lane])) +
+                        ((AB[t][1][lane] + AB[t][5][lane]) + (AB[t][3][lane] + AB[t][7][lane]));
+        if (row < g.rows)
+            g.y[row] = y;
     }
 }
 
