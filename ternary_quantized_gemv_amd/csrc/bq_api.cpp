@@ -54,6 +54,10 @@ constexpr int kColsMinCols = 4;
 //   Q1_0 65536x1024  N = 4 / 8          8.2 / 13.7 (3 / 1, each the fastest)
 // Against one grid row per column the tables' single stream of the weights
 // per four columns gained 1.7-9x (Q1_0 65536x1024 N = 8: 57.2 -> 13.7).
+// (Measured with 8-block table chunks; launches whose workgroups fit one
+// round now take 16-block chunks: Q1_0 12288x4096 N = 4 / 8 / 16 10.9 /
+// 13.7 / 17.1 -> 10.6 / 13.5 / 16.7, Q2_0 20.1 / 21.9 / 27.2 -> 19.2 /
+// 22.0 / 26.8.)
 static int splitcols_shape(int tiles, int ncols)
 {
     const int64_t cgroups = (ncols + 3) / 4;

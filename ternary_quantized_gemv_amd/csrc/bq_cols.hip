@@ -313,12 +313,14 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // The lane groups of a wavefront are ones the final tree joins first --
 // W = 4: a_k + a_(k+4); W = 2: (a_k + a_(k+4)) + (a_(k+2) + a_(k+6)) -- so a
 // wavefront adds them in the tree's order and the remaining additions of
-// the tree go through LDS.  Tables cover 8-block chunks (68 KiB); the
-// wavefronts of a tile read the same payload (one HBM stream, the rest from
-// the caches), each rotating a word once so that its lane groups' nibbles
-// sit at bits 4..7 of bytes (nibble * 16: an entry of four floats).
-constexpr int kScChunk = 8;  // blocks per table chunk (one scale group)
-constexpr int kScRing = 4;   // payload blocks loaded ahead
+// the tree go through LDS.  Tables cover chunks of CH blocks: 16 (136 KiB,
+// one workgroup per CU) when the launch's workgroups fit one round of the
+// GPU, halving the chunks' table builds and barriers, else 8 (68 KiB, two
+// workgroups per CU); the wavefronts of a tile read the same payload (one
+// HBM stream, the rest from the caches), each rotating a word once so that
+// its lane groups' nibbles sit at bits 4..7 of bytes (nibble * 16: an entry
+// of four floats).
+constexpr int kScRing = 4;  // payload blocks loaded ahead
 
 // The partial of a wavefront's lane groups, in the tree's order.
 template <int LG>
@@ -456,12 +458,15 @@ __device__ __forceinline__ void sc_block(const f32x4 *__restrict__ T, const floa
 
 // Workgroup id -> (row block of TPW tiles, column group); ids 8 apart share
 // an XCD, so the column groups of one row block read its weights from one L2.
-template <int FMT, int QA, int W, int TPW>
+template <int FMT, int QA, int W, int TPW, int CH>
 __global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int64_t ld_q, int64_t ld_d, int ncols,
                                                                  int tiles, int cgroups)
 {
     constexpr int kThreadsHere = W * TPW * 64;
     constexpr int LG = 8 / W;
+    constexpr int kScChunk = CH;                          // blocks per table chunk
+    constexpr int kScGroups = CH / kScalesPerGroup;      // scale groups per chunk
+    static_assert(CH % kScalesPerGroup == 0 && CH % kScRing == 0, "whole scale groups and ring turns");
     __shared__ f32x4 T[kScChunk * kSlotsPerBlock * kColsSlotVecs];
     __shared__ float D1[kScChunk * 4 * kColsNC];
     __shared__ float P[TPW][W][kColsNC][64];
@@ -487,12 +492,16 @@ __global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int
 #pragma unroll
         for (int c = 0; c < kColsNC; ++c)
             acc[i][c] = 0.0f;
-    // payload ring kScRing blocks ahead (continuing across chunks); one scale group per chunk
+    // payload ring kScRing blocks ahead (continuing across chunks); the
+    // chunk's scale groups, and the next chunk's requested during its walk
     u32x4 ring[kScRing];
 #pragma unroll
     for (int i = 0; i < kScRing; ++i)
         ring[i] = bload(wp, lo, (uint32_t)min(i, g.nb - 1) * kStep);
-    u32x4 sc = bload(sp, lo, 0);
+    u32x4 sc[kScGroups];
+#pragma unroll
+    for (int s = 0; s < kScGroups; ++s)
+        sc[s] = bload(sp, lo, (uint32_t)min(s, g.ng - 1) * kStep);
 
     ColsInputs<FMT, QA, kScChunk, kThreadsHere> in;
     in.load(g, ld_q, ld_d, c0, ncols, 0, min(kScChunk, g.nb));
@@ -504,7 +513,10 @@ __global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int
         __syncthreads();
         if (cb + kScChunk < g.nb)  // the next chunk's table inputs, read during this walk
             in.load(g, ld_q, ld_d, c0, ncols, (cb + kScChunk) * bl, min(kScChunk, g.nb - cb - kScChunk));
-        const u32x4 sc_next = bload(sp, lo, (uint32_t)min(cb / kScChunk + 1, g.ng - 1) * kStep);
+        u32x4 sc_next[kScGroups];
+#pragma unroll
+        for (int s = 0; s < kScGroups; ++s)
+            sc_next[s] = bload(sp, lo, (uint32_t)min(cb / kScalesPerGroup + kScGroups + s, g.ng - 1) * kStep);
 #pragma unroll
         for (int i0 = 0; i0 < kScChunk; i0 += kScRing) {
 #pragma unroll
@@ -512,13 +524,15 @@ __global__ __launch_bounds__(W * TPW * 64) void splitcols_kernel(GemvDesc g, int
                 const u32x4 w = ring[i];
                 ring[i] = bload(wp, lo, (uint32_t)min(cb + i0 + i + kScRing, g.nb - 1) * kStep);
                 if (i0 + i < nbc) {
-                    float d0 = scale_of(sc, i0 + i);
+                    float d0 = scale_of(sc[(i0 + i) / kScalesPerGroup], i0 + i);
                     asm volatile("" : "+v"(d0));
                     sc_block<FMT, W>(T, D1, i0 + i, w, d0, k, acc);
                 }
             }
         }
-        sc = sc_next;
+#pragma unroll
+        for (int s = 0; s < kScGroups; ++s)
+            sc[s] = sc_next[s];
     }
 #pragma unroll
     for (int c = 0; c < kColsNC; ++c)
@@ -550,11 +564,21 @@ static hipError_t splitcols_shape(int qa, const GemvDesc &g, int64_t ld_q, int64
     const int cgroups = (ncols + kColsNC - 1) / kColsNC;
     const int rblocks = (tiles + TPW - 1) / TPW;
     const dim3 grid((unsigned)(((rblocks + 7) / 8) * 8 * cgroups)), block(W * TPW * 64);
+    // 16-block chunks when the workgroups fit one per compute unit
+    const bool wide = (int64_t)rblocks * cgroups <= 256;
+#define BQ_SPLITCOLS(Q)                                                                                            \
+    if (wide)                                                                                                      \
+        hipLaunchKernelGGL((splitcols_kernel<FMT, Q, W, TPW, 16>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, \
+                           cgroups);                                                                               \
+    else                                                                                                           \
+        hipLaunchKernelGGL((splitcols_kernel<FMT, Q, W, TPW, 8>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles,  \
+                           cgroups)
     switch (qa) {
-    case 32: hipLaunchKernelGGL((splitcols_kernel<FMT, 32, W, TPW>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, cgroups); break;
-    case 64: hipLaunchKernelGGL((splitcols_kernel<FMT, 64, W, TPW>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, cgroups); break;
-    default: hipLaunchKernelGGL((splitcols_kernel<FMT, 128, W, TPW>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, cgroups); break;
+    case 32: BQ_SPLITCOLS(32); break;
+    case 64: BQ_SPLITCOLS(64); break;
+    default: BQ_SPLITCOLS(128); break;
     }
+#undef BQ_SPLITCOLS
     return hipGetLastError();
 }
 
