@@ -315,8 +315,8 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // wavefront adds them in the tree's order and the remaining additions of
 // the tree go through LDS.  Tables cover chunks of CH blocks: 16 (136 KiB,
 // one workgroup per CU) when the launch's workgroups fit one round of the
-// GPU, halving the chunks' table builds and barriers, else 8 (68 KiB, two
-// workgroups per CU); the wavefronts of a tile read the same payload (one
+// GPU and rows have more than 8 blocks, halving the chunks' table builds and
+// barriers, else 8 (68 KiB, two workgroups per CU); the wavefronts of a tile read the same payload (one
 // HBM stream, the rest from the caches), each rotating a word once so that
 // its lane groups' nibbles sit at bits 4..7 of bytes (nibble * 16: an entry
 // of four floats).
@@ -564,8 +564,9 @@ static hipError_t splitcols_shape(int qa, const GemvDesc &g, int64_t ld_q, int64
     const int cgroups = (ncols + kColsNC - 1) / kColsNC;
     const int rblocks = (tiles + TPW - 1) / TPW;
     const dim3 grid((unsigned)(((rblocks + 7) / 8) * 8 * cgroups)), block(W * TPW * 64);
-    // 16-block chunks when the workgroups fit one per compute unit
-    const bool wide = (int64_t)rblocks * cgroups <= 256;
+    // 16-block chunks when the workgroups fit one per compute unit and the
+    // rows are longer than one 8-block chunk
+    const bool wide = (int64_t)rblocks * cgroups <= 256 && g.nb > 8;
 #define BQ_SPLITCOLS(Q)                                                                                            \
     if (wide)                                                                                                      \
         hipLaunchKernelGGL((splitcols_kernel<FMT, Q, W, TPW, 16>), grid, block, 0, st, g, ld_q, ld_d, ncols, tiles, \
