@@ -55,7 +55,7 @@ constexpr int kColsMinCols = 4;
 // Against one grid row per column the tables' single stream of the weights
 // per four columns gained 1.7-9x (Q1_0 65536x1024 N = 8: 57.2 -> 13.7).
 // (Measured with 8-block table chunks; launches whose workgroups fit one
-// round now take 16-block chunks: Q1_0 12288x4096 N = 4 / 8 / 16 10.9 /
+// round, on rows of more than 8 blocks, now take 16-block chunks: Q1_0 12288x4096 N = 4 / 8 / 16 10.9 /
 // 13.7 / 17.1 -> 10.6 / 13.5 / 16.7, Q2_0 20.1 / 21.9 / 27.2 -> 19.2 /
 // 22.0 / 26.8.)
 static int splitcols_shape(int tiles, int ncols)
