@@ -315,11 +315,11 @@ hipError_t launch_cols(int fmt, int qa, const GemvDesc &g, int64_t ld_q, int64_t
 // wavefront adds them in the tree's order and the remaining additions of
 // the tree go through LDS.  Tables cover chunks of CH blocks: 16 (136 KiB,
 // one workgroup per CU) when the launch's workgroups fit one round of the
-// GPU and rows have more than 8 blocks, halving the chunks' table builds and
-// barriers, else 8 (68 KiB, two workgroups per CU); the wavefronts of a tile read the same payload (one
-// HBM stream, the rest from the caches), each rotating a word once so that
-// its lane groups' nibbles sit at bits 4..7 of bytes (nibble * 16: an entry
-// of four floats).
+// GPU and rows have more than 8 blocks, halving the chunks' table builds
+// and barriers, else 8 (68 KiB, two workgroups per CU).  The wavefronts of
+// a tile read the same payload (one HBM stream, the rest from the caches),
+// each rotating a word once so that its lane groups' nibbles sit at bits
+// 4..7 of bytes (nibble * 16: an entry of four floats).
 constexpr int kScRing = 4;  // payload blocks loaded ahead
 
 // The partial of a wavefront's lane groups, in the tree's order.
