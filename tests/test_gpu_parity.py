@@ -204,9 +204,12 @@ def test_small_batch_tall(fmt, rows, cols, ncols, qa, regime):
 # the split-columns kernel, four columns per workgroup from interleaved
 # tables, eight wavefronts per tile (one tile per workgroup) or four (two,
 # three or four tiles), the shape chosen so the workgroups fit one round of
-# the GPU (else two tiles per workgroup).  Cases: each shape and format, rows ragged, rows of 5 / 8 / 9 / 32
-# / 34 / 96 blocks (partial and several 8-block chunks), a last group of one
-# to three columns, every qa, the -128 regimes, 1024 tiles.
+# the GPU (else two tiles per workgroup), with 16-block table chunks where
+# the workgroups fit one round and rows are longer than 8 blocks, else
+# 8-block ones.  Cases: each shape and format, rows ragged, rows of 5 / 8 /
+# 9 / 10 / 24 / 32 / 34 / 96 blocks (partial and several chunks of either
+# length), a last group of one to three columns, every qa, the -128
+# regimes, 1024 tiles.
 SPLITCOLS = [
     (Q1, 12800, 1152, 3, 128, "quant"),   # 200 tiles: eight per tile; 9 blocks (8 + 1)
     (Q2, 12801, 576, 3, 64, "raw"),       # 201 ragged tiles, eight per tile
@@ -218,6 +221,10 @@ SPLITCOLS = [
     (Q1, 65536, 640, 6, 32, "quant"),     # 1024 tiles, six columns: no shape fits one round, two tiles
     (Q2, 65536, 512, 3, 64, "raw"),       # 1024 tiles: four per tile, four tiles
     (Q2, 6400, 2048, 7, 32, "mixed"),     # 100 tiles, seven columns (a group of three)
+    # chunk lengths: 1024 tiles x 2 column groups fit no round (two tiles per workgroup, 8-block
+    # chunks: 8 + 2 blocks); 192 workgroups with 16-block chunks, 24 blocks (16 + 8)
+    (Q1, 65536, 1280, 6, 64, "raw"),
+    (Q2, 12288, 1536, 4, 128, "quant"),
 ]
 
 
