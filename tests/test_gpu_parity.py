@@ -250,6 +250,9 @@ FULL = [
     # Q2_0 rows of one full 32-block chunk: the four-wavefront split (700 tiles), two tiles per wide
     # workgroup (438 tiles), one row per lane (1094 tiles)
     (Q2, 44800, 2048), (Q2, 28000, 2048), (Q2, 70000, 2048),
+    # three half tiles per workgroup in turn over two table chunks (the units' two ab buffers
+    # across a chunk boundary)
+    (Q1, 20000, 8192),
 ]
 
 
