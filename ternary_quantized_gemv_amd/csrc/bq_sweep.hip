@@ -276,10 +276,14 @@ __device__ __forceinline__ void chunk_table(const GemvDesc &g, int k0, int nbc, 
 
 // Rows [64*tile0, 64*(tile0+ntiles)) of one product; wavefront w takes tiles
 // tile0 + w, tile0 + w + kWaves, ...  Rows of at most one chunk share one
-// table for every tile of the item; longer rows (ntiles <= kWaves) walk the
-// chunks with a table rebuild between barriers.  X: the activation is f32
-// and quantized chunk by chunk into Qs, Ds (chunk_table).
-template <int FMT, int QA, bool X>
+// table for every tile of the item; longer rows walk the chunks with a table
+// rebuild between barriers, one tile per wavefront (ntiles <= kWaves) or,
+// with PAIR, two (ntiles <= 2 * kWaves): each chunk's table then serves both
+// of a wavefront's tiles, which halves the rebuilds per tile.  PAIR costs a
+// second set of accumulators, which Q2_0's walk has room for under the
+// 128-register bound and Q1_0's has not.  X: the activation is f32 and
+// quantized chunk by chunk into Qs, Ds (chunk_table).
+template <int FMT, int QA, bool X, bool PAIR>
 __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1, int8_t *Qs,
                                          float *Ds)
 {
@@ -322,11 +326,14 @@ __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntile
         return;
     }
 
-    const int tile = tile0 + wave;
-    const bool active = tile < tend;
+    const int tile = tile0 + wave, tile2 = tile + kWaves;
+    const bool active = tile < tend, active2 = PAIR && tile2 < tend;
+    float acc2[8];
 #pragma unroll
-    for (int L = 0; L < 8; ++L)
+    for (int L = 0; L < 8; ++L) {
         acc[L] = 0.0f;
+        acc2[L] = 0.0f;
+    }
     if (active)
         prefetch_chunk(pf, wtile(tile, 0), stile(tile, 0), lo);
     for (int cb = 0; cb < g.nb; cb += kChunkBlocks) {
@@ -344,15 +351,38 @@ __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntile
                 else
                     cs.load(g.d + k0 / QA);
                 const bool has_next = cb + 2 * kChunkBlocks <= g.nb;
-                run_full_chunk<FMT, QA>(T, D1, cs, wtile(tile, cb), stile(tile, cb), wtile(tile, cb + kChunkBlocks),
-                                        stile(tile, cb + kChunkBlocks), has_next, lo, pf, acc);
+                // The wavefront's tiles in turn, through one instance of the
+                // walk (two would not fit the register bound): the first
+                // tile's walk prefetches the second's chunk, the last one the
+                // first tile's next chunk; acc holds the walked tile's sums,
+                // acc2 the other's.
+#pragma unroll 1
+                for (int r = 0; r < (active2 ? 2 : 1); ++r) {
+                    const bool last = r == (active2 ? 1 : 0);
+                    const int t = r ? tile2 : tile, tn = last ? tile : tile2;
+                    const int cn = last ? cb + kChunkBlocks : cb;
+                    run_full_chunk<FMT, QA>(T, D1, cs, wtile(t, cb), stile(t, cb), wtile(tn, cn), stile(tn, cn),
+                                            last ? has_next : true, lo, pf, acc);
+                    if (active2) {
+#pragma unroll
+                        for (int L = 0; L < 8; ++L) {
+                            const float x = acc[L];
+                            acc[L] = acc2[L];
+                            acc2[L] = x;
+                        }
+                    }
+                }
             } else {
                 run_tail_chunk<FMT>(T, D1, wtile(tile, cb), stile(tile, cb), lo, nbc, acc);
+                if (active2)
+                    run_tail_chunk<FMT>(T, D1, wtile(tile2, cb), stile(tile2, cb), lo, nbc, acc2);
             }
         }
     }
     if (active)
         store_row(g, tile, lane, acc);
+    if (active2)
+        store_row(g, tile2, lane, acc2);
 }
 
 template <int FMT, int QA>
@@ -387,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 4) void matvec_kernel(GemvDesc g, int64_t
     g.d += c * ld_d;
     g.y += (int64_t)c * g.rows;
     const int tile0 = blockIdx.x * tpw;
-    run_item<FMT, QA, false>(g, tile0, min(tpw, tiles - tile0), T, D1, nullptr, nullptr);
+    run_item<FMT, QA, false, false>(g, tile0, min(tpw, tiles - tile0), T, D1, nullptr, nullptr);
 }
 
 // The second bound holds every instantiation to 128 registers, four
@@ -409,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 4) void sweep_kernel(const GemvDesc *__re
     __shared__ float Ds[X ? kChunkValues / QA : 1];
     const WorkItem it = items[blockIdx.x];
     const GemvDesc g = descs[it.gemv];
-    run_item<FMT, QA, X>(g, it.tile0, it.ntiles, T, D1, Qs, Ds);
+    run_item<FMT, QA, X, FMT == BQ_Q2_0>(g, it.tile0, it.ntiles, T, D1, Qs, Ds);
 }
 
 template <int FMT>

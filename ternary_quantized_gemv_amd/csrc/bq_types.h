@@ -32,9 +32,10 @@ constexpr int kWaves = 8;                                            // wavefron
 constexpr int kThreads = kWaves * 64;
 constexpr int kPrefetch = 4;                                         // blocks loaded ahead
 // Sweep work items of single-chunk products hold up to kMaxRounds tiles per
-// wavefront, all served by one table; the last kTailItems items of the
-// dispatch order are cut back to one tile per wavefront so the end of the
-// launch drains in small pieces.
+// wavefront, all served by one table; those of longer Q2_0 rows two, each
+// chunk's table serving both; the last kTailItems items of the dispatch order
+// are cut back to one tile per wavefront so the end of the launch drains in
+// small pieces.
 constexpr int kMaxRounds = 3;
 constexpr int kTailItems = 1024;
 

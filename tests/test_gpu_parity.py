@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import SweepWorkload, assert_parity, log, matvec_gpu, quantize_gpu, torch
+from gpu_util import SweepWorkload, assert_parity, log, matvec_gpu, paired_walk_shapes, quantize_gpu, torch
 from pins import load_witnesses, same_bits
 
 pytestmark = pytest.mark.gpu
@@ -388,6 +388,13 @@ def test_sweep_q2_0_decode_token():
 def test_sweep_ragged_mix():
     shapes = [("a", 1, 128), ("b", 100, 33 * 128), ("c", 65, 4096), ("d", 700, 12288), ("e", 64, 256)]
     _check_sweep(Q1, shapes, seed=63)
+
+
+@pytest.mark.parametrize("qa", [128, 32])
+def test_sweep_q2_paired_walk(qa):
+    """Q2_0 work items of two tiles per wavefront over several chunks
+    (gpu_util.paired_walk_shapes), every output against the oracle."""
+    _check_sweep(Q2, paired_walk_shapes(), seed=65, qa=qa)
 
 
 def test_sweep_ragged_mix_q2():

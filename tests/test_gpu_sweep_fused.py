@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import log, torch
+from gpu_util import log, paired_walk_shapes, torch
 from pins import same_bits
 
 pytestmark = pytest.mark.gpu
@@ -36,12 +36,10 @@ def _staged(fmt, shapes, seed, qa, special):
     return StagedSweep(fmt, canon, shapes, x, qa), canon
 
 
-@pytest.mark.parametrize("fmt", [Q1, Q2])
-@pytest.mark.parametrize("qa,special", [(128, True), (64, False), (32, True)])
-def test_fused_sweep_against_oracle(fmt, qa, special):
+def _check_fused(fmt, shapes, seed, qa, special):
     t = torch()
-    log(f"fused sweep fmt={fmt} qa={qa} special={special}")
-    sw, canon = _staged(fmt, MIX, 70 + fmt + qa, qa, special)
+    log(f"fused sweep fmt={fmt} qa={qa} special={special}: {len(shapes)} products")
+    sw, canon = _staged(fmt, shapes, seed, qa, special)
     try:
         sw.sweep_fused()
         t.cuda.synchronize()
@@ -64,6 +62,19 @@ def test_fused_sweep_against_oracle(fmt, qa, special):
         assert same_bits(sw.y.cpu().numpy(), y)
     finally:
         sw.close()
+
+
+@pytest.mark.parametrize("fmt", [Q1, Q2])
+@pytest.mark.parametrize("qa,special", [(128, True), (64, False), (32, True)])
+def test_fused_sweep_against_oracle(fmt, qa, special):
+    _check_fused(fmt, MIX, 70 + fmt + qa, qa, special)
+
+
+@pytest.mark.parametrize("qa", [128, 64])
+def test_fused_sweep_q2_paired_walk(qa):
+    """Q2_0 work items of two tiles per wavefront over several chunks
+    (gpu_util.paired_walk_shapes), quantizing in the launch."""
+    _check_fused(Q2, paired_walk_shapes(), 90 + qa, qa, True)
 
 
 @pytest.mark.parametrize("fmt", [Q1, Q2])
