@@ -64,6 +64,13 @@ def test_noalloc_decode_token_then_smaller():
     _check(Q1, shapes, 101, 128, [0, 1, 2, 3, 4, 5, 6, 100, 252])
 
 
+def test_noalloc_q2_decode_token_then_smaller():
+    """The full Q2_0 decode token, whose products of several table chunks make
+    work items of two tiles per wavefront, then 5 of them."""
+    shapes = synth.decode_sweep_shapes()
+    _check(Q2, shapes, 103, 128, [0, 3, 6, 100, 252])
+
+
 def test_noalloc_mix_then_smaller():
     """A ragged Q2_0 mix (one block, partial and several table chunks, ragged
     rows) at qa 64, then two of its products."""
