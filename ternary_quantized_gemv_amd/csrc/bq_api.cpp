@@ -352,14 +352,12 @@ BQ_EXPORT int bq_group_matvec(const bq_weights *w, int32_t count, const float *x
 // order, so the short items fill the tail; the last kTailItems are cut to
 // one tile per wavefront.  Ties keep the order items were made in (the
 // sequence number rides in WorkItem::pad while sorting).
-static int plan_items(const GemvDesc *descs, int n, int fmt, WorkItem *out, WorkItem *tmp, int cap)
+static int plan_items(const GemvDesc *descs, int n, WorkItem *out, WorkItem *tmp, int cap)
 {
-    // tiles per wavefront of an item, as the sweep kernel walks them
-    const int long_rounds = fmt == BQ_Q2_0 ? 2 : 1;
     int m = 0;
     for (int i = 0; i < n; ++i) {
         const int tiles = (int)tiles_of(descs[i].rows);
-        const int per_item = kWaves * (descs[i].nb <= kChunkBlocks ? kMaxRounds : long_rounds);
+        const int per_item = kWaves * (descs[i].nb <= kChunkBlocks ? kMaxRounds : kLongRounds);
         for (int t = 0; t < tiles; t += per_item) {
             if (m >= cap)
                 return -1;
@@ -410,7 +408,7 @@ static int make_plan(const char *fn, const std::vector<GemvDesc> &descs, int fmt
     for (const GemvDesc &g : descs)
         cap += (size_t)((tiles_of(g.rows) + kWaves - 1) / kWaves);
     std::vector<WorkItem> items(cap + 1), tmp(cap + 1);
-    const int nitems = plan_items(descs.data(), (int)descs.size(), fmt, items.data(), tmp.data(), (int)cap + 1);
+    const int nitems = plan_items(descs.data(), (int)descs.size(), items.data(), tmp.data(), (int)cap + 1);
     if (nitems < 0)
         return set_error(BQ_EARG, "%s: too many work items", fn);
     const size_t dbytes = descs.size() * sizeof(GemvDesc);
@@ -548,7 +546,7 @@ BQ_EXPORT int bq_token_sweep_noalloc(const bq_gemv *list, int32_t count, bq_stre
         if (rc)
             return rc;
     }
-    const int nitems = plan_items(descs, count, fmt, items, g_tmp, kScratchItems);
+    const int nitems = plan_items(descs, count, items, g_tmp, kScratchItems);
     if (nitems < 0)
         return set_error(BQ_EARG, "%s: the products need more than the fixed scratch's %d work items", fn,
                          kScratchItems);

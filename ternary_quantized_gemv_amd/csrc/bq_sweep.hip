@@ -165,20 +165,20 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch &pf, rsrc_t w, rsrc_t sc
 // iterations already load the first blocks and scale groups of the next full
 // chunk this wavefront will run (wn, sn), if has_next.  Every index is a
 // compile-time constant, so each table read carries its slot as an immediate
-// LDS offset.  For Q1_0 the table reads of block b+1 are issued, sub-block by
-// sub-block, between the fma steps of block b.
+// LDS offset.  For Q1_0 the table reads run one sub-block ahead: those of the
+// next sub-block (the next block's first, after a block's last) are issued
+// before the fma steps of the current one.  (A whole block ahead measured no
+// faster and holds 48 more registers, which the second tile's sums of
+// run_item need.)
 template <int FMT, int QA>
 __device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, const float *__restrict__ D1,
                                                const ChunkScales<FMT, QA> &cs, rsrc_t wp, rsrc_t sp, rsrc_t wn,
                                                rsrc_t sn, bool has_next, uint32_t lo, Prefetch &pf, float acc[8])
 {
     u32x4 sc = pf.sc0, sc_next = pf.sc1;
-    float tc[32], tn[32];
-    if (FMT == BQ_Q1_0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            lookups_q1(T, 0, j, pf.buf[0][j], tc + 8 * j);
-    }
+    float tc[8], tn[8];
+    if (FMT == BQ_Q1_0)
+        lookups_q1(T, 0, 0, pf.buf[0][0], tc);
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         if ((b & 7) == 0 && b > 0) {
@@ -199,26 +199,27 @@ __device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, cons
         // (the compiler's choice for an f16 operand) runs at half rate
         asm volatile("" : "+v"(d0));
         if (FMT == BQ_Q1_0) {
-            const u32x4 vn = pf.buf[(b + 1) % kPrefetch];
             float ab[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (b + 1 < kChunkBlocks)
-                    lookups_q1(T, b + 1, j, vn[j], tn + 8 * j);
+                if (j < 3)
+                    lookups_q1(T, b, j + 1, v[j + 1], tn);
+                else if (b + 1 < kChunkBlocks)
+                    lookups_q1(T, b + 1, 0, pf.buf[(b + 1) % kPrefetch][0], tn);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int L = 0; L < 8; ++L)
-                    ab[L] = j == 0 ? tc[L] : __builtin_fmaf(d1[j], tc[8 * j + L], ab[L]);
+                    ab[L] = j == 0 ? tc[L] : __builtin_fmaf(d1[j], tc[L], ab[L]);
                 __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int L = 0; L < 8; ++L)
+                    tc[L] = tn[L];
             }
 #pragma unroll
             for (int L = 0; L < 8; ++L) {
                 acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
                 asm volatile("" : "+v"(acc[L]));
             }
-#pragma unroll
-            for (int i = 0; i < 32; ++i)
-                tc[i] = tn[i];
         } else {
             block_math<FMT>(T, d1, b, v, d0, acc);
         }
@@ -279,10 +280,9 @@ __device__ __forceinline__ void chunk_table(const GemvDesc &g, int k0, int nbc, 
 // table for every tile of the item; longer rows walk the chunks with a table
 // rebuild between barriers, one tile per wavefront (ntiles <= kWaves) or,
 // with PAIR, two (ntiles <= 2 * kWaves): each chunk's table then serves both
-// of a wavefront's tiles, which halves the rebuilds per tile.  PAIR costs a
-// second set of accumulators, which Q2_0's walk has room for under the
-// 128-register bound and Q1_0's has not.  X: the activation is f32 and
-// quantized chunk by chunk into Qs, Ds (chunk_table).
+// of a wavefront's tiles, which halves the rebuilds per tile, for a second
+// set of accumulators.  X: the activation is f32 and quantized chunk by chunk
+// into Qs, Ds (chunk_table).
 template <int FMT, int QA, bool X, bool PAIR>
 __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntiles, float *T, float *D1, int8_t *Qs,
                                          float *Ds)
@@ -326,6 +326,7 @@ __device__ __forceinline__ void run_item(const GemvDesc &g, int tile0, int ntile
         return;
     }
 
+    static_assert(kLongRounds == 2, "the plan's items of longer rows hold two tiles per wavefront");
     const int tile = tile0 + wave, tile2 = tile + kWaves;
     const bool active = tile < tend, active2 = PAIR && tile2 < tend;
     float acc2[8];
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 4) void sweep_kernel(const GemvDesc *__re
     __shared__ float Ds[X ? kChunkValues / QA : 1];
     const WorkItem it = items[blockIdx.x];
     const GemvDesc g = descs[it.gemv];
-    run_item<FMT, QA, X, FMT == BQ_Q2_0>(g, it.tile0, it.ntiles, T, D1, Qs, Ds);
+    run_item<FMT, QA, X, true>(g, it.tile0, it.ntiles, T, D1, Qs, Ds);
 }
 
 template <int FMT>

@@ -32,11 +32,12 @@ constexpr int kWaves = 8;                                            // wavefron
 constexpr int kThreads = kWaves * 64;
 constexpr int kPrefetch = 4;                                         // blocks loaded ahead
 // Sweep work items of single-chunk products hold up to kMaxRounds tiles per
-// wavefront, all served by one table; those of longer Q2_0 rows two, each
+// wavefront, all served by one table; those of longer rows kLongRounds, each
 // chunk's table serving both; the last kTailItems items of the dispatch order
 // are cut back to one tile per wavefront so the end of the launch drains in
 // small pieces.
 constexpr int kMaxRounds = 3;
+constexpr int kLongRounds = 2;
 constexpr int kTailItems = 1024;
 
 constexpr uint32_t kStep = kTileRows * 16;  // bytes of one block (or scale group) of a tile

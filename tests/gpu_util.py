@@ -33,19 +33,21 @@ def torch():
     return t
 
 
-def paired_walk_shapes():
-    """Q2_0 products whose rows span several table chunks, ahead of 1024
-    one-tile products.  A sweep dispatches its heaviest work items first and
-    cuts only the last 1024 back to one tile per wavefront, so the one-tile
-    products take that cut and the items of the products in front keep two
-    tiles per wavefront, each chunk's table serving both:
+def paired_walk_shapes(fmt: int):
+    """Products whose rows span several table chunks (32 blocks: 4096 columns
+    of Q1_0, 2048 of Q2_0), ahead of 1024 one-tile products.  A sweep
+    dispatches its heaviest work items first and cuts only the last 1024
+    back to one tile per wavefront, so the one-tile products take that cut
+    and the items of the products in front keep two tiles per wavefront,
+    each chunk's table serving both:
       a: 16 tiles (the last one 40 rows), 3 full chunks and a partial one --
          every wavefront two tiles;
       b: 11 tiles, a full chunk and 2 blocks -- three wavefronts two tiles,
          five one;
       c: 40 tiles, two full chunks -- items of 16, 16 and 8 tiles;
       d: 15 tiles of one chunk (the single-chunk walk beside them)."""
-    heavy = [("a", 1000, 100 * 64), ("b", 700, 34 * 64), ("c", 2560, 64 * 64), ("d", 900, 2048)]
+    qk = 128 if fmt == 1 else 64
+    heavy = [("a", 1000, 100 * qk), ("b", 700, 34 * qk), ("c", 2560, 64 * qk), ("d", 900, 32 * qk)]
     return heavy + [(f"t{i}", 1 + i % 64, 128) for i in range(1024)]
 
 

@@ -390,11 +390,11 @@ def test_sweep_ragged_mix():
     _check_sweep(Q1, shapes, seed=63)
 
 
-@pytest.mark.parametrize("qa", [128, 32])
-def test_sweep_q2_paired_walk(qa):
-    """Q2_0 work items of two tiles per wavefront over several chunks
+@pytest.mark.parametrize("fmt,qa", [(Q1, 128), (Q1, 32), (Q2, 128), (Q2, 32)])
+def test_sweep_paired_walk(fmt, qa):
+    """Work items of two tiles per wavefront over several chunks
     (gpu_util.paired_walk_shapes), every output against the oracle."""
-    _check_sweep(Q2, paired_walk_shapes(), seed=65, qa=qa)
+    _check_sweep(fmt, paired_walk_shapes(fmt), seed=65 + fmt, qa=qa)
 
 
 def test_sweep_ragged_mix_q2():

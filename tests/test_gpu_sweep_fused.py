@@ -70,11 +70,11 @@ def test_fused_sweep_against_oracle(fmt, qa, special):
     _check_fused(fmt, MIX, 70 + fmt + qa, qa, special)
 
 
-@pytest.mark.parametrize("qa", [128, 64])
-def test_fused_sweep_q2_paired_walk(qa):
-    """Q2_0 work items of two tiles per wavefront over several chunks
+@pytest.mark.parametrize("fmt,qa", [(Q1, 128), (Q1, 32), (Q2, 128), (Q2, 64)])
+def test_fused_sweep_paired_walk(fmt, qa):
+    """Work items of two tiles per wavefront over several chunks
     (gpu_util.paired_walk_shapes), quantizing in the launch."""
-    _check_fused(Q2, paired_walk_shapes(), 90 + qa, qa, True)
+    _check_fused(fmt, paired_walk_shapes(fmt), 90 + fmt + qa, qa, True)
 
 
 @pytest.mark.parametrize("fmt", [Q1, Q2])
