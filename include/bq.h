@@ -274,7 +274,8 @@ int bq_token_sweep(const bq_sweep *plan, bq_stream s);
  * and planned on fixed host storage, and the plan (descriptors and work
  * items) is copied on s into a fixed device array of the library: 320 KiB
  * per GPU, held until the process ends, room for up to 1024 products and
- * 16384 work items (the 253 products of a decode token need about 1,900).
+ * 16384 work items (the 253 products of a decode token need 1,743 in Q1_0,
+ * 2,029 in Q2_0).
  * Larger lists are refused with BQ_EARG, as is every invalid entry, before
  * anything is copied or launched.  The copy is from pageable memory, so the
  * call returns once the table is staged; it may wait for earlier work on s.
