@@ -424,9 +424,11 @@ __global__ __launch_bounds__(kThreads, 4) void matvec_kernel(GemvDesc g, int64_t
 // The second bound holds every instantiation to 128 registers, four
 // wavefronts per SIMD (two workgroups per CU): with activation blocks
 // shorter than 128 values the chunk's activation scales come from LDS and
-// the compiler would keep more of them in flight; with qa 128 the table
-// build's batched requests would take the 129th register (the bound moves
-// one value of the chunk loop's prologue to scratch instead).
+// the compiler would keep more of them in flight; elsewhere the table
+// build's batched requests and the second tile's sums would take more than
+// 128.  Under the bound some instantiations keep up to four values of the
+// chunk loop in scratch (none in the block walk, and none at all in the
+// qa-128 sweeps of quantized activations).
 // X: the products' activations are f32 and every workgroup quantizes the
 // chunks it needs (the quantizer's bits) into LDS before building its table.
 template <int FMT, int QA, bool X>
