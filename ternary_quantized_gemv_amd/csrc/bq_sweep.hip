@@ -145,6 +145,20 @@ __device__ __forceinline__ void lookups_q1(const float *__restrict__ T, int b, i
         t[L] = tab(T, b * kSlotsPerBlock + j * 8 + L, nib4((L & 1) ? wb : wa, L >> 1));
 }
 
+// The eight table reads of word m of a Q2_0 block: for lane groups beta of
+// that word, the entries of its low and its high nibble, in t[2 beta] and
+// t[2 beta + 1].
+__device__ __forceinline__ void lookups_q2(const float *__restrict__ T, int b, int m, uint32_t wa, float t[8])
+{
+    const uint32_t wb = __builtin_amdgcn_alignbit(wa, wa, 4);
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta) {
+        const int slot = b * kSlotsPerBlock + m * 8 + 2 * beta;
+        t[2 * beta] = tab(T, slot, nib4(wa, beta));
+        t[2 * beta + 1] = tab(T, slot + 1, nib4(wb, beta));
+    }
+}
+
 // Payload words of the first kPrefetch blocks of a full chunk, plus its first
 // two scale groups.
 struct Prefetch {
@@ -165,11 +179,13 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch &pf, rsrc_t w, rsrc_t sc
 // iterations already load the first blocks and scale groups of the next full
 // chunk this wavefront will run (wn, sn), if has_next.  Every index is a
 // compile-time constant, so each table read carries its slot as an immediate
-// LDS offset.  For Q1_0 the table reads run one sub-block ahead: those of the
-// next sub-block (the next block's first, after a block's last) are issued
-// before the fma steps of the current one.  (A whole block ahead measured no
-// faster and holds 48 more registers, which the second tile's sums of
-// run_item need.)
+// LDS offset.  The table reads run one payload word ahead: those of the next
+// word (the next block's first, after a block's last) are issued before the
+// arithmetic of the current one -- for Q1_0 a sub-block's eight entries, for
+// Q2_0 the two nibble entries of each of four lane groups (0.6% off the Q2_0
+// token sweep against reading each block's entries at its start).  (Q1_0's
+// reads a whole block ahead measured no faster and hold 48 more registers,
+// which the second tile's sums of run_item need.)
 template <int FMT, int QA>
 __device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, const float *__restrict__ D1,
                                                const ChunkScales<FMT, QA> &cs, rsrc_t wp, rsrc_t sp, rsrc_t wn,
@@ -179,6 +195,8 @@ __device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, cons
     float tc[8], tn[8];
     if (FMT == BQ_Q1_0)
         lookups_q1(T, 0, 0, pf.buf[0][0], tc);
+    else
+        lookups_q2(T, 0, 0, pf.buf[0][0], tc);
 #pragma unroll
     for (int b = 0; b < kChunkBlocks; ++b) {
         if ((b & 7) == 0 && b > 0) {
@@ -221,7 +239,31 @@ __device__ __forceinline__ void run_full_chunk(const float *__restrict__ T, cons
                 asm volatile("" : "+v"(acc[L]));
             }
         } else {
-            block_math<FMT>(T, d1, b, v, d0, acc);
+            float ab[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m < 3)
+                    lookups_q2(T, b, m + 1, v[m + 1], tn);
+                else if (b + 1 < kChunkBlocks)
+                    lookups_q2(T, b + 1, 0, pf.buf[(b + 1) % kPrefetch][0], tn);
+                __builtin_amdgcn_sched_barrier(0);
+                const int j = m >> 1;
+#pragma unroll
+                for (int beta = 0; beta < 4; ++beta) {
+                    const int L = 4 * (m & 1) + beta;
+                    const float s = tc[2 * beta] + tc[2 * beta + 1];
+                    ab[L] = j == 0 ? d1[0] * s : __builtin_fmaf(d1[1], s, ab[L]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int L = 0; L < 8; ++L)
+                    tc[L] = tn[L];
+            }
+#pragma unroll
+            for (int L = 0; L < 8; ++L) {
+                acc[L] = __builtin_fmaf(d0, ab[L], acc[L]);
+                asm volatile("" : "+v"(acc[L]));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
