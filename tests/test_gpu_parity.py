@@ -390,11 +390,13 @@ def test_sweep_ragged_mix():
     _check_sweep(Q1, shapes, seed=63)
 
 
-@pytest.mark.parametrize("fmt,qa", [(Q1, 128), (Q1, 32), (Q2, 128), (Q2, 32)])
-def test_sweep_paired_walk(fmt, qa):
+@pytest.mark.parametrize("fmt,qa,f16", [(Q1, 128, False), (Q1, 32, False), (Q2, 128, False), (Q2, 32, False),
+                                         (Q1, 32, True), (Q2, 32, True)])
+def test_sweep_paired_walk(fmt, qa, f16):
     """Work items of two tiles per wavefront over several chunks
-    (gpu_util.paired_walk_shapes), every output against the oracle."""
-    _check_sweep(fmt, paired_walk_shapes(fmt), seed=65 + fmt, qa=qa)
+    (gpu_util.paired_walk_shapes), every output against the oracle; also
+    with the q8_0 activation flavour (qa 32, f16-valued scales)."""
+    _check_sweep(fmt, paired_walk_shapes(fmt), seed=65 + fmt + int(f16), qa=qa, f16_scale=f16)
 
 
 def test_sweep_ragged_mix_q2():
